@@ -1,0 +1,261 @@
+"""Plain fp64 reference of one quantized MoE FFN layer (test infrastructure).
+
+Sources (pages as titled; sections as numbered on each page):
+  [Routing]   Baidu Cloud article on quantized MoE LLM inference, section
+              "expert routing": router logits from a linear layer, keep the
+              top-k experts, softmax over the selected logits, output is the
+              weight-sum of the selected experts applied to the token.
+  [TopK]      "Sparse activation in large models: the MoE engineering behind
+              GPT-4's 2% activation", section 2.2: the router emits one logit
+              per expert and the K highest are kept.
+  [Gate]      MoE mixed-precision field notes, section 2.1: gating, softmax,
+              top-k, expert compute, weighted sum; the gate stays unquantised
+              and the expert inputs are quantised per token dynamically to
+              int8 (W8A8).
+  [PerExpert] "AlphaQ" blog, section 4.2: per-expert, per-layer
+              {bit_width, group_size}; expert-aware quantisation digest:
+              hot experts at 4-bit, cold experts at 2-bit.
+  [FFN]       "AlphaQ" blog, section 2.2 and the mixed-precision notes,
+              section 3.3: each expert is a three-matrix FFN (gate, up/middle,
+              down/output); its gated form is SwiGLU.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes): ties and near-ties go to the lower expert index; the bias adds
+to the logits before selection; segments are ordered by ascending token;
+asymmetric blocks decode as w = s*q + m with one fp32 rounding; e2m1 uses the
+OCP MX value set; int8 activations are symmetric absmax/127, round half to
+even, clamped to +-127; the router sees the unquantised hidden states.
+
+Parity pins: see tests/test_oracle.py (brute-force dense MoE, invariants,
+closed forms, textbook special cases, hand-written golden blobs).
+"""
+import numpy as np
+
+# Adjacent top-(k+1) logit gaps below this (absolute, fp64) are near-ties: the
+# token is flagged and excluded from id / output comparisons.
+NEAR_TIE = 1e-6
+
+# e2m1 magnitudes by 3-bit code (OCP microscaling spec): exponent bias 1, one
+# mantissa bit, code 1 is the subnormal 0.5.
+E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Weight blocks [PerExpert]
+# --------------------------------------------------------------------------
+def _unpack_codes(codes: np.ndarray, bits: int, cols: int) -> np.ndarray:
+    """uint8 [rows, row_bytes] -> int64 [rows, cols]. 4-bit: element 2i is the
+    low nibble of byte i. 2-bit: element 4i+j is bits [2j, 2j+1] of byte i."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    per_byte = 8 // bits
+    nbytes = cols // per_byte
+    b = codes[:, :nbytes].astype(np.int64)
+    mask = (1 << bits) - 1
+    parts = [(b >> (bits * j)) & mask for j in range(per_byte)]
+    out = np.empty((codes.shape[0], cols), dtype=np.int64)
+    for j in range(per_byte):
+        out[:, j::per_byte] = parts[j]
+    return out
+
+
+def decode_qmat(qm) -> np.ndarray:
+    """Decode one canonical block matrix to fp32 [rows, cols].
+
+    Asymmetric (fmt 1): w = round_fp32(s*q + m) with fp16 s, m and unsigned
+    b-bit q. The exact value s*q + m is formed in fp64 (both terms are exact
+    there) and rounded once to fp32.
+    e2m1 (fmt 2): w = round_fp32(v(q) * s), v from the 3 magnitude bits, bit 3
+    the sign, fp16 s per group.
+    """
+    q = _unpack_codes(qm.codes, qm.bits, qm.cols)
+    G = qm.cols // qm.group
+    p = np.asarray(qm.params, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if qm.fmt == 1:
+        s = np.repeat(p[:, 0::2][:, :G], qm.group, axis=1)
+        m = np.repeat(p[:, 1::2][:, :G], qm.group, axis=1)
+        return (s * q.astype(np.float64) + m).astype(np.float32)
+    if qm.fmt == 2:
+        s = np.repeat(p[:, :G], qm.group, axis=1)
+        v = E2M1_TABLE[q & 7] * np.where((q & 8) != 0, -1.0, 1.0)
+        return (v * s).astype(np.float32)
+    raise ValueError(f"unknown weight format {qm.fmt}")
+
+
+# --------------------------------------------------------------------------
+# Router [Routing], [TopK], [Gate]
+# --------------------------------------------------------------------------
+def x_to_f64(x: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Hidden states to fp64 (exact): bf16 bit patterns or fp32."""
+    if x_dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def router_logits(X: np.ndarray, Wr: np.ndarray, b) -> np.ndarray:
+    """L = X Wr^T + b in fp64 (the router linear, with its bias)."""
+    L = X @ np.asarray(Wr, dtype=np.float64).T
+    if b is not None:
+        L = L + np.asarray(b, dtype=np.float64)[None, :]
+    return L
+
+
+def topk_softmax(L: np.ndarray, k: int):
+    """Per token: the k largest logits, descending, ties to the lower expert
+    index (a stable sort of -L); weights = softmax over those k logits.
+
+    Returns ids [T,k] int32, w [T,k] fp64, gap [T] fp64 (smallest adjacent gap
+    among the sorted top min(k+1, E)), flagged [T] bool (gap < NEAR_TIE).
+    """
+    T, E = L.shape
+    ids = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    gap = np.full(T, np.inf)
+    for t in range(T):
+        order = np.argsort(-L[t], kind="stable")
+        sel = order[:k]
+        ids[t] = sel
+        top = L[t, order[:min(k + 1, E)]]
+        if top.size > 1:
+            gap[t] = np.min(top[:-1] - top[1:])
+        z = L[t, sel] - L[t, sel].max()
+        e = np.exp(z)
+        w[t] = e / e.sum()
+    return ids, w, gap, gap < NEAR_TIE
+
+
+# --------------------------------------------------------------------------
+# Permutation by expert (contiguous per-expert segments)
+# --------------------------------------------------------------------------
+def canonical_permute(ids: np.ndarray, E: int):
+    """Stable counting sort of the T*k assignments a = t*k + j by expert.
+
+    counts[e]; offsets = exclusive prefix sum (length E+1);
+    perm_token[r] = token of the r-th sorted assignment (ascending token
+    inside a segment); inv[a] = r.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:E].copy()
+    perm_token = np.zeros(T * k, dtype=np.int64)
+    inv = np.zeros(T * k, dtype=np.int64)
+    for a in range(T * k):
+        e = flat[a]
+        r = cursor[e]
+        cursor[e] += 1
+        perm_token[r] = a // k
+        inv[a] = r
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm_token.astype(np.int32), inv.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# Per-token dynamic int8 activations [Gate]
+# --------------------------------------------------------------------------
+def act_quant_i8(v: np.ndarray):
+    """Per row of fp32 v: s = fp32(absmax)/127 in fp32; q = clamp(rint(v/s),
+    -127, 127) with fp32 division and round half to even; zero row -> s = 0,
+    q = 0. Returns q int8 [rows, cols], s fp32 [rows]."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    s = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    r = (v / safe[:, None]).astype(np.float32)
+    q = np.clip(np.rint(r), -127, 127)
+    q = np.where(s[:, None] == 0, 0, q).astype(np.int8)
+    return q, s
+
+
+def dq8(v32: np.ndarray) -> np.ndarray:
+    """fp64 value of the int8 quantisation of fp32 rows: q * s (exact)."""
+    q, s = act_quant_i8(v32)
+    return q.astype(np.float64) * s.astype(np.float64)[:, None]
+
+
+# --------------------------------------------------------------------------
+# Expert FFN [FFN]
+# --------------------------------------------------------------------------
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """silu(g) * u with silu(z) = z / (1 + exp(-z))."""
+    return g * u / (1.0 + np.exp(-g))
+
+
+def expert_ffn(A: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
+               act: int) -> np.ndarray:
+    """One expert on its rows A (fp64): h = silu(A Wg^T) * (A Wu^T); when both
+    expert inputs are int8 (act == 2) h is replaced by dq8(fp32(h));
+    Y = h Wd^T."""
+    G = A @ Wg.astype(np.float64).T
+    U = A @ Wu.astype(np.float64).T
+    Hh = swiglu(G, U)
+    if act == 2:
+        Hh = dq8(Hh.astype(np.float32))
+    return Hh @ Wd.astype(np.float64).T
+
+
+# --------------------------------------------------------------------------
+# Weighted combine [Routing]
+# --------------------------------------------------------------------------
+def combine(Y: np.ndarray, w: np.ndarray, inv: np.ndarray, T: int, k: int) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * Y[inv[t*k + j]] in fp64."""
+    out = np.zeros((T, Y.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            out[t] += w[t, j] * Y[inv[t * k + j]]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def moe_layer(x, x_dtype: str, Wr, b, get_expert, E: int, k: int, act: int = 0,
+              tokens=None, ids_override=None):
+    """Forward pass of the layer.
+
+    get_expert(e) returns {"gate", "up", "down"} canonical block matrices; it
+    is called once per expert with assignments, one expert at a time.
+    tokens: optional subset of token indices whose outputs are computed (the
+    routing and permutation always cover every token).
+    ids_override: route with these ids instead of the oracle's own top-k
+    (the weights are still the softmax over L[t, ids]).
+    act: 0 none; 1 int8 x before gate/up; 2 int8 x and int8 h before down.
+    """
+    X = x_to_f64(x, x_dtype)
+    T = X.shape[0]
+    L = router_logits(X, Wr, b)
+    ids, w, gap, flagged = topk_softmax(L, k)
+    if ids_override is not None:
+        ids = np.asarray(ids_override, dtype=np.int32)
+        for t in range(T):
+            z = L[t, ids[t]] - L[t, ids[t]].max()
+            e_ = np.exp(z)
+            w[t] = e_ / e_.sum()
+    counts, offsets, perm_token, inv = canonical_permute(ids, E)
+    A_all = dq8(X.astype(np.float32)) if act in (1, 2) else X
+
+    want = np.ones(T, dtype=bool) if tokens is None else np.isin(np.arange(T), tokens)
+    H = X.shape[1]
+    Y = np.zeros((T * k, H), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        rows = np.arange(r0, r1)
+        rows = rows[want[perm_token[rows]]]
+        if rows.size == 0:
+            continue
+        ex = get_expert(e)
+        Wg, Wu, Wd = (decode_qmat(ex["gate"]), decode_qmat(ex["up"]),
+                      decode_qmat(ex["down"]))
+        Y[rows] = expert_ffn(A_all[perm_token[rows]], Wg, Wu, Wd, act)
+        del Wg, Wu, Wd
+    out = combine(Y, w, inv, T, k)
+    return dict(logits=L, ids=ids, w=w, gap=gap, flagged=flagged, counts=counts,
+                offsets=offsets, perm_token=perm_token, inv=inv, Y=Y, out=out)

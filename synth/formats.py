@@ -1,0 +1,157 @@
+"""Canonical block format of one quantized weight matrix, and the quantisers
+that write it (input preparation, not part of the layer's forward pass).
+
+A matrix W[rows, cols] is quantised in groups of `group` consecutive elements
+along `cols` (the input / K dimension of the GEMM that uses it).
+
+Codes plane: uint8 [rows, row_bytes(cols, bits)], row-major, each row padded
+with zero bytes to a multiple of 16 bytes.
+  * 4-bit: element 2i in the low nibble of byte i, element 2i+1 in the high
+    nibble.
+  * 2-bit: element 4i+j in bits [2j, 2j+1] of byte i.
+Params plane: uint16 (IEEE fp16 bit patterns) [rows, n_params], row-major.
+  * FMT_ASYM (w = s*q + m, q unsigned b-bit): n_params = 2*cols/group, stored
+    as (s, m) pairs per group.
+  * FMT_E2M1 (w = e2m1(q) * s): n_params = cols/group, one s per group.
+
+The per-expert bit-width / group-size descriptor follows the per-expert
+`{bit_width, group_size}` configuration of the AlphaQ blog (section 4.2); the
+4-bit floating-point element follows the OCP microscaling e2m1 encoding
+(sign bit 3, two exponent bits with bias 1, one mantissa bit).
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+FMT_ASYM = 1
+FMT_E2M1 = 2
+
+# e2m1 magnitudes by 3-bit code (OCP MX e2m1).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+_E2M1_MID = (E2M1_VALUES[1:] + E2M1_VALUES[:-1]) / 2.0
+
+
+def row_bytes(cols: int, bits: int) -> int:
+    """Bytes per code row, padded to 16."""
+    raw = (cols * bits + 7) // 8
+    return (raw + 15) // 16 * 16
+
+
+@dataclass
+class QMat:
+    fmt: int
+    bits: int
+    group: int
+    rows: int
+    cols: int
+    codes: np.ndarray   # uint8 [rows, row_bytes]
+    params: np.ndarray  # uint16 [rows, n_params] (fp16 bits)
+
+    @property
+    def n_groups(self) -> int:
+        return self.cols // self.group
+
+    def nbytes(self) -> int:
+        return int(self.codes.nbytes + self.params.nbytes)
+
+    def payload_bytes(self) -> int:
+        """Codes + params without row padding (the bytes a kernel must read)."""
+        return self.rows * (self.cols * self.bits // 8) + self.params.nbytes
+
+
+def _pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    rows, cols = q.shape
+    q = q.astype(np.uint8)
+    out = np.zeros((rows, row_bytes(cols, bits)), dtype=np.uint8)
+    if bits == 4:
+        packed = q[:, 0::2] | (q[:, 1::2] << 4)
+    elif bits == 2:
+        packed = q[:, 0::4] | (q[:, 1::4] << 2) | (q[:, 2::4] << 4) | (q[:, 3::4] << 6)
+    else:
+        raise ValueError("bits must be 2 or 4")
+    out[:, : packed.shape[1]] = packed
+    return out
+
+
+def quantize_asym(W: np.ndarray, bits: int, group: int) -> QMat:
+    """Asymmetric b-bit group quantisation: m = fp16(min), s = fp16(range/(2^b-1)),
+    q = clip(rint((w - m)/s), 0, 2^b - 1) (round half to even); s == 0 gives q = 0."""
+    rows, cols = W.shape
+    assert cols % group == 0
+    qmax = (1 << bits) - 1
+    Wg = W.astype(np.float64).reshape(rows, cols // group, group)
+    mn = Wg.min(axis=-1)
+    mx = Wg.max(axis=-1)
+    m16 = mn.astype(np.float16)
+    s16 = ((mx - mn) / qmax).astype(np.float16)
+    s64 = s16.astype(np.float64)[..., None]
+    m64 = m16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((Wg - m64) / np.where(s64 == 0, 1.0, s64))
+    q = np.where(s64 == 0, 0.0, q)
+    q = np.clip(q, 0, qmax).astype(np.uint8).reshape(rows, cols)
+    params = np.empty((rows, 2 * (cols // group)), dtype=np.uint16)
+    params[:, 0::2] = s16.view(np.uint16)
+    params[:, 1::2] = m16.view(np.uint16)
+    return QMat(FMT_ASYM, bits, group, rows, cols, _pack_codes(q, bits), params)
+
+
+def quantize_e2m1(W: np.ndarray, group: int) -> QMat:
+    """e2m1 group quantisation with one fp16 scale per group: s = fp16(absmax/6);
+    each element goes to the nearest e2m1 value of w/s (ties to the even
+    mantissa, saturating at 6); the sign goes to bit 3 (zero magnitude -> +0)."""
+    rows, cols = W.shape
+    assert cols % group == 0
+    Wg = W.astype(np.float64).reshape(rows, cols // group, group)
+    amax = np.abs(Wg).max(axis=-1)
+    s16 = (amax / 6.0).astype(np.float16)
+    s64 = s16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        a = np.abs(Wg) / np.where(s64 == 0, 1.0, s64)
+    a = np.where(s64 == 0, 0.0, a)
+    code = np.searchsorted(_E2M1_MID, a, side="left")
+    at_mid = (code < 7) & (a == _E2M1_MID[np.minimum(code, 6)])
+    code = np.where(at_mid & (code % 2 == 1), code + 1, code)
+    code = np.minimum(code, 7)
+    sign = (Wg < 0) & (code > 0)
+    q = (code | (sign.astype(np.int64) << 3)).astype(np.uint8).reshape(rows, cols)
+    params = s16.view(np.uint16).reshape(rows, cols // group).copy()
+    return QMat(FMT_E2M1, 4, group, rows, cols, _pack_codes(q, 4), params)
+
+
+def random_qmat(rng: np.random.Generator, rows: int, cols: int, fmt: int,
+                bits: int, group: int, sigma: float = 0.02) -> QMat:
+    """Codes drawn uniformly, per-group parameters drawn so that the decoded
+    values span the range a quantisation of N(0, sigma) groups would give."""
+    assert cols % group == 0
+    rb = row_bytes(cols, bits)
+    used = cols * bits // 8
+    codes = np.zeros((rows, rb), dtype=np.uint8)
+    codes[:, :used] = rng.integers(0, 256, size=(rows, used), dtype=np.uint8)
+    G = cols // group
+    if fmt == FMT_ASYM:
+        qmax = (1 << bits) - 1
+        r = rng.uniform(3.5, 4.5, size=(rows, G))
+        s = (sigma * r / qmax).astype(np.float16)
+        m = (-sigma * r / 2.0 + 0.1 * sigma * rng.standard_normal((rows, G))).astype(np.float16)
+        params = np.empty((rows, 2 * G), dtype=np.uint16)
+        params[:, 0::2] = s.view(np.uint16)
+        params[:, 1::2] = m.view(np.uint16)
+    elif fmt == FMT_E2M1:
+        assert bits == 4
+        s = (sigma * rng.uniform(2.5, 3.5, size=(rows, G)) / 6.0).astype(np.float16)
+        params = s.view(np.uint16).copy()
+    else:
+        raise ValueError(fmt)
+    return QMat(fmt, bits, group, rows, cols, codes, params)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounding = 0x7FFF + ((u >> 16) & 1)
+    return ((u + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
