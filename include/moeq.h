@@ -1,0 +1,221 @@
+/*
+ * moeq.h: C ABI of a quantized Mixture-of-Experts FFN layer (forward pass)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (Baidu Cloud article on quantized MoE LLM
+ * inference, "expert routing" section; MoE mixed-precision field notes,
+ * section 2.1): for every token t of the hidden states x[T,H]
+ *     L[t,:]   = x[t,:] Wr^T + b                       (router, fp32 in, fp64 accumulate)
+ *     ids[t,:] = the k experts with the largest L[t,e], descending, ties to the
+ *                lower expert index ("Sparse activation ... GPT-4's 2%
+ *                activation", section 2.2: keep the K highest of E logits)
+ *     w[t,:]   = softmax of L[t, ids[t,:]]
+ *     out[t,:] = sum_j w[t,j] * FFN_{ids[t,j]}(x[t,:])
+ *     FFN_e(a) = (silu(a Wg_e^T) * (a Wu_e^T)) Wd_e^T     (SwiGLU expert)
+ * Expert weights are block-quantised with a per-expert bit width and group
+ * size ("AlphaQ" blog, section 4.2; expert-aware quantisation digest: hot
+ * experts 4-bit, cold experts 2-bit) and are decoded on the fly. Optionally
+ * the expert inputs are quantised per token to int8 (mixed-precision notes,
+ * sections 2.1-2.2); the router always sees the unquantised x.
+ *
+ * Conventions for every entry point
+ *  - Pointers named *_dev or documented "device" are device (HBM) pointers;
+ *    everything else is host memory. The caller owns every buffer. The library
+ *    keeps no state between calls and never allocates.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Compute entry points
+ *    only enqueue kernels on it and return; they never synchronise.
+ *  - Arguments are checked before anything is enqueued. A failing check
+ *    returns a negative moe_status and enqueues nothing. A failed launch
+ *    returns MOE_ERR_HIP.
+ *  - Data-dependent trouble found on the device (an expert id out of range,
+ *    NaN router logits) sets bits of the flag word at the start of the
+ *    workspace (MOE_FLAG_*), readable after the stream synchronises. The
+ *    flag word is cleared by every call that takes a workspace.
+ *  - Matrices are row-major; int32 indices; fp32 weights of the router.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k outside [1,E], ... */
+  MOE_ERR_UNSUPPORTED = -2, /* format / bit width / group size not provided */
+  MOE_ERR_ALIGNMENT = -3,   /* pointer not aligned as documented */
+  MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -5          /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Element formats of a weight block.
+ * MOE_W_ASYM: w = s*q + m, q unsigned b-bit (b in {2,4}), fp16 s and m per
+ *             group; decoded value rounded once to fp32.
+ * MOE_W_E2M1: w = e2m1(q) * s, 4-bit OCP-MX e2m1 element (bit 3 sign, two
+ *             exponent bits with bias 1, one mantissa bit: magnitudes
+ *             0, .5, 1, 1.5, 2, 3, 4, 6), fp16 s per group (the 4-bit
+ *             floating-point weights of the quantized-MoE article). */
+typedef enum { MOE_W_ASYM = 1, MOE_W_E2M1 = 2 } moe_wfmt;
+
+/* Per-token dynamic int8 expert inputs (mixed-precision notes, section 2.1):
+ * per row, s = fp32(absmax)/127 (fp32 division, correctly rounded),
+ * q = clamp(rint(v/s), -127, 127) (round half to even), a zero row gives
+ * s = 0, q = 0.
+ * MOE_ACT_I8_X: x before gate/up; MOE_ACT_I8_XH: x, and h before down. */
+typedef enum { MOE_ACT_NONE = 0, MOE_ACT_I8_X = 1, MOE_ACT_I8_XH = 2 } moe_actq;
+
+enum {
+  MOE_FLAG_BAD_EXPERT_ID = 1u << 0, /* an id outside [0,E) reached moe_permute */
+  MOE_FLAG_NAN_LOGIT = 1u << 1      /* a router logit was NaN (routing undefined) */
+};
+
+/* One weight matrix W[rows, cols] in the canonical block format.
+ * Groups of `group` consecutive elements along cols (the GEMM's K).
+ * codes (device): uint8 [rows, row_bytes], row_bytes = cols*bits/8 rounded
+ *   up to a multiple of 16 (padding bytes are ignored). 4-bit: element 2i in
+ *   the low nibble of byte i, 2i+1 in the high nibble. 2-bit: element 4i+j in
+ *   bits [2j, 2j+1] of byte i.
+ * params (device): fp16 [rows, cols/group] scales for MOE_W_E2M1, or
+ *   [rows, cols/group] (scale, min) pairs for MOE_W_ASYM, row-major.
+ * Supported: ASYM with bits 2 or 4 and group 16/32/64/128; E2M1 with bits 4
+ * and group 16/32/64/128. rows % 32 == 0; cols % 128 == 0; codes 16-byte
+ * aligned, params 4-byte aligned. */
+typedef struct {
+  uint8_t fmt;    /* moe_wfmt */
+  uint8_t bits;   /* 2 or 4 */
+  uint16_t group; /* 16, 32, 64 or 128 */
+  uint32_t rows;
+  uint32_t cols;
+  const void* codes;
+  const void* params;
+} moe_qmat;
+
+/* One expert: gate [I,H], up [I,H] (same format), down [H,I]. */
+typedef struct {
+  moe_qmat gate, up, down;
+} moe_expert_canon;
+
+/* Device-layout descriptor of one packed expert, filled by moe_pack_expert.
+ * The pointed-to layout is private to the library (32-row by 64- or 128-
+ * column tiles in matrix-core fragment order, gate and up tiles interleaved).
+ * An array of E of these, copied to device memory by the caller, is what the
+ * FFN entry points take. 64 bytes. */
+typedef struct {
+  uint8_t gu_fmt, gu_bits;
+  uint16_t gu_group;
+  uint8_t dn_fmt, dn_bits;
+  uint16_t dn_group;
+  uint32_t H, I;
+  uint32_t reserved0, reserved1, reserved2, reserved3;
+  const void* gu_codes;
+  const void* gu_params;
+  const void* dn_codes;
+  const void* dn_params;
+} moe_packed_expert;
+
+/* Bytes of device memory moe_pack_expert needs for this expert (0 if the
+ * descriptor is invalid or unsupported). Host only. */
+size_t moe_packed_expert_bytes(const moe_expert_canon* src);
+
+/* Repack one expert from the canonical format (device planes named in *src)
+ * into the device layout at dst_dev (256-byte aligned, dst_bytes >=
+ * moe_packed_expert_bytes(src)). Fills *out_desc (host). Enqueues the repack
+ * on `stream`; the canonical planes must stay valid until it has run. */
+moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t dst_bytes,
+                           moe_packed_expert* out_desc, void* stream);
+
+/* Workspace bytes the layer entry points need for these sizes. Host only. */
+size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
+
+/* Router + top-k + softmax (steps 1-2 above).
+ * x (device): [T,H] fp32 or bf16 (xdt). Wr (device): fp32 [E,H]. b (device):
+ * fp32 [E] or NULL (no bias). Logits are accumulated in fp64 so that the
+ * selection matches an exact evaluation except on near-ties.
+ * Outputs (device): topk_ids int32 [T,k] (descending logit), topk_w fp32
+ * [T,k] (softmax over the k selected logits, computed in fp64), logits fp32
+ * [T,E] (optional, NULL to skip). Constraints: 1 <= k <= min(E, 32),
+ * E <= 512, H % 8 == 0, x/Wr 16-byte aligned. T == 0 is a no-op. */
+moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                     int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
+                     float* logits, void* stream);
+
+/* Stable counting sort of the T*k assignments a = t*k + j by expert.
+ * topk_ids (device) int32 [T,k]. Outputs (device, int32): counts [E],
+ * offsets [E+1] (exclusive prefix sum, offsets[E] = T*k), perm_token [T*k]
+ * (token of the r-th sorted assignment; ascending token inside each
+ * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: workspace of at
+ * least moe_workspace_size(T, 1, 1, E, k, MOE_ACT_NONE) bytes (flag word).
+ * Ids outside [0,E) are dropped and flag MOE_FLAG_BAD_EXPERT_ID. */
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Grouped expert FFN over the permuted assignments (steps 3-5):
+ * for every sorted row r of expert e (offsets[e] <= r < offsets[e+1]):
+ *   Y[r,:] = FFN_e(x[perm_token[r], :]).
+ * experts (device): moe_packed_expert [E]. Y (device): fp32 [T*k, H].
+ * Decoded weights and the SwiGLU output h run through fp16 matrix-core
+ * operations with fp32 accumulation; with int8 activations the int8 codes
+ * enter the matrix cores exactly and the per-row scales are applied in fp32.
+ * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes, 256-aligned.
+ * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I. */
+moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
+                             const int32_t* offsets, const int32_t* perm_token, int T, int H,
+                             int I, int E, int k, moe_actq aq, float* Y, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* The two halves of moe_grouped_ffn_q, for callers that time or overlap them.
+ * moe_ffn_gate_up: gathers (and optionally quantises) the expert inputs and
+ * runs the fused gate/up + SwiGLU, leaving h in the workspace.
+ * moe_ffn_down: (optionally quantises h and) runs the down projection into
+ * Y (fp32 [T*k, H]). Same arguments and workspace as moe_grouped_ffn_q; call
+ * gate_up then down on the same stream with the same workspace. */
+moe_status moe_ffn_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
+                           const int32_t* offsets, const int32_t* perm_token, int T, int H,
+                           int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
+                           void* stream);
+moe_status moe_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T,
+                        int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Weighted combine (step 5's sum): out[t,:] = sum_j topk_w[t,j] * Y[inv[t*k+j], :],
+ * accumulated in fp32 in slot order j = 0..k-1. out (device): [T,H] fp32 or
+ * bf16 (round to nearest even). H % 4 == 0. */
+moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, int T, int H,
+                       int k, void* out, moe_dtype out_dt, void* stream);
+
+/* The whole layer in one call: route, permute, grouped FFN, combine.
+ * topk_ids / topk_w (device, optional): receive the routing when non-NULL.
+ * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes. */
+moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                             const moe_packed_expert* experts, int T, int H, int I, int E,
+                             int k, moe_actq aq, void* out, moe_dtype out_dt,
+                             int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Per-token dynamic int8 quantisation of rows (mixed-precision notes,
+ * sections 2.1-2.2), the arithmetic the layer applies to its expert inputs
+ * under MOE_ACT_I8_*: per row s = fp32(absmax)/127, q = clamp(rint(v/s),
+ * -127, 127) with IEEE fp32 division and round half to even; a zero row gives
+ * s = 0 and q = 0. v (device): [rows, cols] fp32 or bf16. q (device): int8
+ * [rows, cols]. s (device): fp32 [rows]. */
+moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,
+                            void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

@@ -1,0 +1,299 @@
+"""ctypes binding of libmoeq.so: argument marshalling only.
+
+Torch tensors provide device memory and the current HIP stream; every step of
+the layer runs in the library's HIP kernels. If the shared library is missing
+the import of this module fails loudly (there is no fallback path).
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+
+MOE_OK = 0
+MOE_F32, MOE_BF16 = 0, 1
+MOE_W_ASYM, MOE_W_E2M1 = 1, 2
+ACT_NONE, ACT_I8_X, ACT_I8_XH = 0, 1, 2
+FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT = 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status)} ({status})")
+
+
+class QMatC(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_uint8), ("bits", ctypes.c_uint8), ("group", ctypes.c_uint16),
+                ("rows", ctypes.c_uint32), ("cols", ctypes.c_uint32),
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
+
+
+class ExpertCanonC(ctypes.Structure):
+    _fields_ = [("gate", QMatC), ("up", QMatC), ("down", QMatC)]
+
+
+class PackedExpertC(ctypes.Structure):
+    _fields_ = [("gu_fmt", ctypes.c_uint8), ("gu_bits", ctypes.c_uint8), ("gu_group", ctypes.c_uint16),
+                ("dn_fmt", ctypes.c_uint8), ("dn_bits", ctypes.c_uint8), ("dn_group", ctypes.c_uint16),
+                ("H", ctypes.c_uint32), ("I", ctypes.c_uint32),
+                ("reserved0", ctypes.c_uint32), ("reserved1", ctypes.c_uint32),
+                ("reserved2", ctypes.c_uint32), ("reserved3", ctypes.c_uint32),
+                ("gu_codes", ctypes.c_void_p), ("gu_params", ctypes.c_void_p),
+                ("dn_codes", ctypes.c_void_p), ("dn_params", ctypes.c_void_p)]
+
+
+assert ctypes.sizeof(PackedExpertC) == 64
+
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "moe_version": ([], _i),
+    "moe_status_string": ([_i], ctypes.c_char_p),
+    "moe_packed_expert_bytes": ([ctypes.POINTER(ExpertCanonC)], _sz),
+    "moe_pack_expert": ([ctypes.POINTER(ExpertCanonC), _vp, _sz, ctypes.POINTER(PackedExpertC), _vp], _i),
+    "moe_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
+    "moe_route": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_permute": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_grouped_ffn_q": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "moe_ffn_gate_up": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "moe_ffn_down": ([_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "moe_combine": ([_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
+    "moe_layer_forward": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_mixture_experts_router_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in _SIGS.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+LIB = _load()
+EXPORTED = tuple(_SIGS)
+
+
+def _status_string(s):
+    return LIB.moe_status_string(int(s)).decode()
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def version():
+    return LIB.moe_version()
+
+
+def workspace_size(T, H, I, E, k, act=ACT_NONE):
+    return int(LIB.moe_workspace_size(T, H, I, E, k, act))
+
+
+def workspace(T, H, I, E, k, act=ACT_NONE, device="cuda"):
+    n = workspace_size(T, H, I, E, k, act)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def read_flags(ws):
+    return int(ws[:4].view(torch.int32).item())
+
+
+# ---------------------------------------------------------------- weights
+class DeviceQMat:
+    """A canonical block matrix whose planes live in device memory."""
+
+    def __init__(self, fmt, bits, group, rows, cols, codes, params):
+        self.fmt, self.bits, self.group, self.rows, self.cols = fmt, bits, group, rows, cols
+        self.codes, self.params = codes, params
+
+    @classmethod
+    def from_host(cls, q, device="cuda"):
+        codes = torch.from_numpy(np.ascontiguousarray(q.codes)).to(device)
+        params = torch.from_numpy(np.ascontiguousarray(q.params).view(np.int16)).to(device)
+        return cls(q.fmt, q.bits, q.group, q.rows, q.cols, codes, params)
+
+    def c(self):
+        return QMatC(self.fmt, self.bits, self.group, self.rows, self.cols,
+                     self.codes.data_ptr(), self.params.data_ptr())
+
+
+class PackedExperts:
+    """E experts in the device layout plus the device array of descriptors."""
+
+    def __init__(self, buffers, descs, H, I, device="cuda"):
+        self.buffers = buffers
+        self.descs = descs
+        self.H, self.I = H, I
+        raw = bytearray(ctypes.sizeof(PackedExpertC) * len(descs))
+        for i, d in enumerate(descs):
+            ctypes.memmove(ctypes.addressof(ctypes.c_char.from_buffer(raw, i * 64)), ctypes.addressof(d), 64)
+        self.dev = torch.frombuffer(raw, dtype=torch.uint8).to(device)
+
+    @property
+    def E(self):
+        return len(self.descs)
+
+    def nbytes(self):
+        return sum(int(b.numel()) for b in self.buffers if b is not None)
+
+
+def packed_expert_bytes(gate, up, down):
+    ec = ExpertCanonC(gate.c(), up.c(), down.c())
+    return int(LIB.moe_packed_expert_bytes(ctypes.byref(ec)))
+
+
+def pack_expert(gate, up, down, device="cuda"):
+    """Pack one expert (DeviceQMat gate/up/down) -> (buffer tensor, descriptor)."""
+    ec = ExpertCanonC(gate.c(), up.c(), down.c())
+    n = int(LIB.moe_packed_expert_bytes(ctypes.byref(ec)))
+    if n == 0:
+        raise MoeError(-2, "moe_packed_expert_bytes")
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    view = buf[off:off + n]
+    d = PackedExpertC()
+    _check(LIB.moe_pack_expert(ctypes.byref(ec), _ptr(view), n, ctypes.byref(d), _stream()),
+           "moe_pack_expert")
+    return buf, d
+
+
+def pack_experts(get_expert, E, device="cuda"):
+    """get_expert(e) -> {"gate","up","down"} host QMats (canonical). Uploads,
+    packs and frees the canonical copies one expert at a time."""
+    bufs, descs = [], []
+    H = I = None
+    for e in range(E):
+        ex = get_expert(e)
+        g = DeviceQMat.from_host(ex["gate"], device)
+        u = DeviceQMat.from_host(ex["up"], device)
+        dn = DeviceQMat.from_host(ex["down"], device)
+        buf, d = pack_expert(g, u, dn, device)
+        torch.cuda.current_stream().synchronize()  # canonical planes may be freed now
+        del g, u, dn
+        bufs.append(buf)
+        descs.append(d)
+        I, H = ex["gate"].rows, ex["gate"].cols
+    return PackedExperts(bufs, descs, H, I, device)
+
+
+# ---------------------------------------------------------------- layer steps
+def route(x, Wr, b, k, want_logits=False):
+    x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
+    T, H = x.shape
+    E = Wr.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    _check(LIB.moe_route(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), T, H, E, k, _ptr(ids), _ptr(w),
+                         _ptr(logits), _stream()), "moe_route")
+    return (ids, w, logits) if want_logits else (ids, w)
+
+
+def permute(ids, E, ws=None):
+    ids = _dev(ids, "ids")
+    T, k = ids.shape
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    _check(LIB.moe_permute(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
+                           _ptr(ws), ws.numel(), _stream()), "moe_permute")
+    return counts, offsets, perm[:T * k], inv[:T * k], ws
+
+
+def grouped_ffn(x, packed, offsets, perm, k, act=ACT_NONE, ws=None):
+    x = _dev(x, "x")
+    T, H = x.shape
+    Y = torch.empty((T * k, H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(T, H, packed.I, packed.E, k, act, x.device)
+    _check(LIB.moe_grouped_ffn_q(_ptr(x), _dt(x), _ptr(packed.dev), _ptr(offsets), _ptr(perm), T, H,
+                                 packed.I, packed.E, k, act, _ptr(Y), _ptr(ws), ws.numel(), _stream()),
+           "moe_grouped_ffn_q")
+    return Y
+
+
+def ffn_gate_up(x, packed, offsets, perm, k, act, ws):
+    T, H = x.shape
+    _check(LIB.moe_ffn_gate_up(_ptr(x), _dt(x), _ptr(packed.dev), _ptr(offsets), _ptr(perm), T, H,
+                               packed.I, packed.E, k, act, _ptr(ws), ws.numel(), _stream()),
+           "moe_ffn_gate_up")
+
+
+def ffn_down(T, packed, offsets, k, act, Y, ws):
+    _check(LIB.moe_ffn_down(_ptr(packed.dev), _ptr(offsets), T, packed.H, packed.I, packed.E, k, act,
+                            _ptr(Y), _ptr(ws), ws.numel(), _stream()), "moe_ffn_down")
+
+
+def combine(Y, w, inv, T, k, out_dtype=torch.float32):
+    H = Y.shape[1]
+    out = torch.empty((T, H), dtype=out_dtype, device=Y.device)
+    _check(LIB.moe_combine(_ptr(Y), _ptr(w), _ptr(inv), T, H, k, _ptr(out), _dt(out), _stream()),
+           "moe_combine")
+    return out
+
+
+def layer_forward(x, Wr, b, packed, k, act=ACT_NONE, out_dtype=torch.float32, ws=None,
+                  out=None, ids=None, w=None):
+    x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
+    T, H = x.shape
+    E = Wr.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(T, H, packed.I, E, k, act, x.device)
+    _check(LIB.moe_layer_forward(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), _ptr(packed.dev), T, H, packed.I,
+                                 E, k, act, _ptr(out), _dt(out), _ptr(ids), _ptr(w), _ptr(ws),
+                                 ws.numel(), _stream()), "moe_layer_forward")
+    return out, ids, w
+
+
+def act_quant_i8(v):
+    v = _dev(v, "v")
+    rows, cols = v.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=v.device)
+    s = torch.empty(rows, dtype=torch.float32, device=v.device)
+    _check(LIB.moe_act_quant_i8(_ptr(v), _dt(v), rows, cols, _ptr(q), _ptr(s), _stream()),
+           "moe_act_quant_i8")
+    return q, s

@@ -1,0 +1,298 @@
+// Host side of the C ABI: argument checks, workspace carving and dispatch.
+// Every check runs before anything is enqueued; nothing here synchronises.
+#include "common.h"
+
+using namespace moeq;
+
+namespace {
+
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 32;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_qmat(const moe_qmat& q, uint32_t rows, uint32_t cols) {
+  if (q.rows != rows || q.cols != cols) return MOE_ERR_INVALID_ARG;
+  if (!q.codes || !q.params) return MOE_ERR_INVALID_ARG;
+  if (fmt_id(q.fmt, q.bits, q.group) < 0) return MOE_ERR_UNSUPPORTED;
+  if (rows % 32 != 0 || cols % 128 != 0 || cols % q.group != 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(q.codes, 16) || !aligned(q.params, 4)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+moe_status check_canon(const moe_expert_canon* src) {
+  if (!src) return MOE_ERR_INVALID_ARG;
+  const uint32_t I = src->gate.rows, H = src->gate.cols;
+  if (I == 0 || H == 0) return MOE_ERR_INVALID_ARG;
+  moe_status s;
+  if ((s = check_qmat(src->gate, I, H)) != MOE_OK) return s;
+  if ((s = check_qmat(src->up, I, H)) != MOE_OK) return s;
+  if ((s = check_qmat(src->down, H, I)) != MOE_OK) return s;
+  if (src->up.fmt != src->gate.fmt || src->up.bits != src->gate.bits ||
+      src->up.group != src->gate.group)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct PackedSizes {
+  size_t gu_codes, gu_params, dn_codes, dn_params, total;
+};
+
+PackedSizes packed_sizes(const moe_expert_canon* src) {
+  PackedSizes p;
+  const int I = (int)src->gate.rows, H = (int)src->gate.cols;
+  p.gu_codes = align256(packed_codes_bytes(2 * I, H, src->gate.bits));
+  p.gu_params = align256(packed_params_bytes(2 * I, H, src->gate.fmt, src->gate.bits, src->gate.group));
+  p.dn_codes = align256(packed_codes_bytes(H, I, src->down.bits));
+  p.dn_params = align256(packed_params_bytes(H, I, src->down.fmt, src->down.bits, src->down.group));
+  p.total = p.gu_codes + p.gu_params + p.dn_codes + p.dn_params;
+  return p;
+}
+
+moe_status check_sizes(int T, int H, int I, int E, int k) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || E > kMaxE) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if ((long)T * k > (1L << 30)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return MOE_ERR_HIP;  \
+  } while (0)
+
+inline char* ws_at(void* ws, size_t off) { return (char*)ws + off; }
+
+// gate/up half of the grouped FFN (workspace already validated)
+moe_status run_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
+                       const int32_t* offsets, const int32_t* perm, int T, int H, int I, int E,
+                       int k, moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
+  const int R = T * k;
+  f16* a16 = (f16*)ws_at(ws, L.a16);
+  float* ascale = (float*)ws_at(ws, L.ascale);
+  MOE_TRY(launch_gather_a(x, xdt, perm, R, H, aq != MOE_ACT_NONE, a16, ascale, s));
+  MOE_TRY(launch_ffn_gate_up(experts, offsets, T, H, I, E, k, a16,
+                             aq != MOE_ACT_NONE ? ascale : nullptr, ws_at(ws, L.h),
+                             aq == MOE_ACT_I8_XH, L.decode, s));
+  return MOE_OK;
+}
+
+moe_status run_down(const moe_packed_expert* experts, const int32_t* offsets, int T, int H,
+                    int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws, float* yp,
+                    hipStream_t s) {
+  const int R = T * k;
+  const f16* ain = (const f16*)ws_at(ws, L.h);
+  const float* sc = nullptr;
+  if (aq == MOE_ACT_I8_XH) {
+    f16* h16 = (f16*)ws_at(ws, L.h16);
+    float* hs = (float*)ws_at(ws, L.hscale);
+    MOE_TRY(launch_quant_rows_f32((const float*)ws_at(ws, L.h), R, I, h16, hs, s));
+    ain = h16;
+    sc = hs;
+  }
+  MOE_TRY(launch_ffn_down(experts, offsets, T, H, I, E, k, ain, sc, yp, L.splits, L.decode, s));
+  return MOE_OK;
+}
+
+moe_status check_ffn_args(const void* experts, const int32_t* offsets, bool need_offsets, int T,
+                          int H, int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
+                          WsLayout& L) {
+  moe_status st = check_sizes(T, H, I, E, k);
+  if (st != MOE_OK) return st;
+  if (aq < MOE_ACT_NONE || aq > MOE_ACT_I8_XH) return MOE_ERR_INVALID_ARG;
+  if (!experts || !ws || (need_offsets && !offsets)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, 256) || !aligned(experts, 16)) return MOE_ERR_ALIGNMENT;
+  L = ws_layout(T, H, I, E, k, aq);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported format";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_packed_expert_bytes(const moe_expert_canon* src) {
+  if (check_canon(src) != MOE_OK) return 0;
+  return packed_sizes(src).total;
+}
+
+moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t dst_bytes,
+                           moe_packed_expert* out_desc, void* stream) {
+  moe_status st = check_canon(src);
+  if (st != MOE_OK) return st;
+  if (!dst_dev || !out_desc) return MOE_ERR_INVALID_ARG;
+  if (!aligned(dst_dev, 256)) return MOE_ERR_ALIGNMENT;
+  PackedSizes p = packed_sizes(src);
+  if (dst_bytes < p.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)dst_dev;
+  void* guc = base;
+  void* gup = base + p.gu_codes;
+  void* dnc = base + p.gu_codes + p.gu_params;
+  void* dnp = base + p.gu_codes + p.gu_params + p.dn_codes;
+  MOE_TRY(launch_pack_matrix(&src->gate, &src->up, guc, gup, s));
+  MOE_TRY(launch_pack_matrix(&src->down, nullptr, dnc, dnp, s));
+  moe_packed_expert d;
+  d.gu_fmt = src->gate.fmt;
+  d.gu_bits = src->gate.bits;
+  d.gu_group = src->gate.group;
+  d.dn_fmt = src->down.fmt;
+  d.dn_bits = src->down.bits;
+  d.dn_group = src->down.group;
+  d.H = src->gate.cols;
+  d.I = src->gate.rows;
+  d.reserved0 = d.reserved1 = d.reserved2 = d.reserved3 = 0;
+  d.gu_codes = guc;
+  d.gu_params = gup;
+  d.dn_codes = dnc;
+  d.dn_params = dnp;
+  *out_desc = d;
+  return MOE_OK;
+}
+
+size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+  return ws_layout(T, H, I, E, k, aq).total;
+}
+
+moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b, int T, int H,
+                     int E, int k, int32_t* topk_ids, float* topk_w, float* logits,
+                     void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || E > kMaxE || k < 1 || k > E || k > kMaxK)
+    return MOE_ERR_INVALID_ARG;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (H % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(Wr, 16)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_route(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, logits, nullptr,
+                                 (hipStream_t)stream));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm_token || !inv)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < 256) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flags = (uint32_t*)ws;
+  MOE_TRY(launch_zero_u32(flags, 64, s));
+  MOE_TRY(launch_permute(topk_ids, T, k, E, counts, offsets, perm_token, inv, flags, s));
+  return MOE_OK;
+}
+
+moe_status moe_ffn_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
+                           const int32_t* offsets, const int32_t* perm_token, int T, int H, int I,
+                           int E, int k, moe_actq aq, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout L;
+  moe_status st = check_ffn_args(experts, offsets, true, T, H, I, E, k, aq, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !perm_token)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return run_gate_up(x, xdt, experts, offsets, perm_token, T, H, I, E, k, aq, L, ws,
+                     (hipStream_t)stream);
+}
+
+moe_status moe_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T, int H,
+                        int I, int E, int k, moe_actq aq, float* Y, void* ws, size_t ws_bytes,
+                        void* stream) {
+  WsLayout L;
+  moe_status st = check_ffn_args(experts, offsets, true, T, H, I, E, k, aq, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  if (T > 0 && !Y) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t n = (size_t)T * k * H;
+  if (L.decode && L.splits > 1) {
+    float* yp = (float*)ws_at(ws, L.yp);
+    st = run_down(experts, offsets, T, H, I, E, k, aq, L, ws, yp, s);
+    if (st != MOE_OK) return st;
+    return hip_status(launch_reduce_splits(yp, L.splits, n, Y, s));
+  }
+  return run_down(experts, offsets, T, H, I, E, k, aq, L, ws, Y, s);
+}
+
+moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
+                             const int32_t* offsets, const int32_t* perm_token, int T, int H,
+                             int I, int E, int k, moe_actq aq, float* Y, void* ws,
+                             size_t ws_bytes, void* stream) {
+  moe_status st = moe_ffn_gate_up(x, xdt, experts, offsets, perm_token, T, H, I, E, k, aq, ws,
+                                  ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down(experts, offsets, T, H, I, E, k, aq, Y, ws, ws_bytes, stream);
+}
+
+moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, int T, int H,
+                       int k, void* out, moe_dtype out_dt, void* stream) {
+  if (T < 0 || H <= 0 || k < 1 || H % 4 != 0) return MOE_ERR_INVALID_ARG;
+  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!Y || !topk_w || !inv || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(Y, 16) || !aligned(out, out_dt == MOE_F32 ? 16 : 8)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_combine(Y, 1, topk_w, inv, T, H, k, out, out_dt, (hipStream_t)stream));
+}
+
+moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                             const moe_packed_expert* experts, int T, int H, int I, int E, int k,
+                             moe_actq aq, void* out, moe_dtype out_dt, int32_t* topk_ids,
+                             float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout L;
+  moe_status st = check_ffn_args(experts, nullptr, false, T, H, I, E, k, aq, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, out_dt == MOE_F32 ? 16 : 8))
+    return MOE_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flags = (uint32_t*)ws_at(ws, L.flags);
+  int32_t* ids = topk_ids ? topk_ids : (int32_t*)ws_at(ws, L.ids);
+  float* w = topk_w ? topk_w : (float*)ws_at(ws, L.w);
+  int32_t* counts = (int32_t*)ws_at(ws, L.counts);
+  int32_t* offsets = (int32_t*)ws_at(ws, L.offsets);
+  int32_t* perm = (int32_t*)ws_at(ws, L.perm);
+  int32_t* inv = (int32_t*)ws_at(ws, L.inv);
+  float* yp = (float*)ws_at(ws, L.yp);
+  MOE_TRY(launch_zero_u32(flags, 64, s));
+  MOE_TRY(launch_route(x, xdt, Wr, b, T, H, E, k, ids, w, nullptr, flags, s));
+  MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
+  st = run_gate_up(x, xdt, experts, offsets, perm, T, H, I, E, k, aq, L, ws, s);
+  if (st != MOE_OK) return st;
+  st = run_down(experts, offsets, T, H, I, E, k, aq, L, ws, yp, s);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(yp, L.decode ? L.splits : 1, w, inv, T, H, k, out, out_dt, s));
+}
+
+moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,
+                            void* stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!v || !q || !s) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_act_quant_i8(v, dt, rows, cols, q, s, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moeq.h"
+
+namespace moeq {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Weight formats handled by the kernels: (element format, bits, group size).
+// ---------------------------------------------------------------------------
+enum FmtId : int {
+  F_A4G16 = 0, F_A4G32, F_A4G64, F_A4G128,
+  F_A2G16, F_A2G32, F_A2G64, F_A2G128,
+  F_E4G16, F_E4G32, F_E4G64, F_E4G128,
+  F_COUNT
+};
+
+__host__ __device__ inline int fmt_id(int fmt, int bits, int group) {
+  int g = group == 16 ? 0 : group == 32 ? 1 : group == 64 ? 2 : group == 128 ? 3 : -1;
+  if (g < 0) return -1;
+  if (fmt == MOE_W_ASYM && bits == 4) return F_A4G16 + g;
+  if (fmt == MOE_W_ASYM && bits == 2) return F_A2G16 + g;
+  if (fmt == MOE_W_E2M1 && bits == 4) return F_E4G16 + g;
+  return -1;
+}
+
+// Device layout of one packed matrix W[N, K] (N rows = GEMM output columns).
+//  - 32-row tiles; one tile spans KT = 2*SPAN columns; one tile is 1 KiB of
+//    codes: lane l = (n = l % 32, kh = l / 32) holds 16 bytes = SPAN codes of
+//    row n, columns [kt*KT + kh*SPAN, +SPAN).
+//  - Inside each 32-bit word the codes are ordered so that (word >> b*i) &
+//    mask yields the pair (code 2i, code 2i+1) in the two 16-bit halves.
+//  - Tiles are stored row-tile major, then K-tile; gate/up are interleaved
+//    as row tiles (2j = gate rows 32j.., 2j+1 = up rows 32j..).
+//  - Params: one "entry" per (row, GE columns) with GE = max(group, SPAN),
+//    holding max(1, SPAN/group) params (ASYM: fp16 (s, m) = 4 B each; E2M1:
+//    fp16 s = 2 B each). Stored [row tile][entry][32 rows][EB bytes].
+template <int FMT, int BITS, int GROUP>
+struct Fmt {
+  static constexpr int kFmt = FMT;
+  static constexpr int kBits = BITS;
+  static constexpr int kGroup = GROUP;
+  static constexpr int SPAN = 128 / BITS;                  // codes per lane per tile
+  static constexpr int KT = 2 * SPAN;                      // K columns per tile
+  static constexpr int STEPS = SPAN / 8;                   // 32x32x16 MFMA steps per tile
+  static constexpr int GE = GROUP > SPAN ? GROUP : SPAN;   // K columns per param entry
+  static constexpr int NP = GROUP < SPAN ? SPAN / GROUP : 1;
+  static constexpr int PSZ = FMT == MOE_W_ASYM ? 4 : 2;
+  static constexpr int EB = NP * PSZ;                      // entry bytes
+};
+
+__host__ __device__ inline int fmt_span(int bits) { return 128 / bits; }
+__host__ __device__ inline int fmt_kt(int bits) { return 256 / bits; }
+
+inline size_t packed_codes_bytes(int N, int K, int bits) {
+  return (size_t)(N / 32) * (size_t)(K / fmt_kt(bits)) * 1024;
+}
+inline size_t packed_params_bytes(int N, int K, int fmt, int bits, int group) {
+  int span = fmt_span(bits);
+  int ge = group > span ? group : span;
+  int np = group < span ? span / group : 1;
+  int eb = np * (fmt == MOE_W_ASYM ? 4 : 2);
+  return (size_t)(N / 32) * (size_t)(K / ge) * 32 * eb;
+}
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout (byte offsets from the workspace base).
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t flags;    // uint32 flag word (+ pad to 256)
+  size_t ids;      // int32 [T*k]
+  size_t w;        // f32 [T*k]
+  size_t counts;   // int32 [E]
+  size_t offsets;  // int32 [E+1]
+  size_t perm;     // int32 [T*k]
+  size_t inv;      // int32 [T*k]
+  size_t a16;      // f16 [T*k, H] expert inputs in sorted-row order
+  size_t ascale;   // f32 [T*k] per-row int8 scale of a16 (int8 modes)
+  size_t h;        // f16 [T*k, I]  or f32 [T*k, I] under MOE_ACT_I8_XH
+  size_t h16;      // f16 [T*k, I] int8 codes of h (MOE_ACT_I8_XH)
+  size_t hscale;   // f32 [T*k]
+  size_t yp;       // f32 [splits, T*k, H] down-projection (partial) sums
+  size_t total;
+  int splits;
+  bool decode;
+};
+
+// Choice of kernel family and split-K factor from host-known sizes only.
+inline bool use_decode_path(int T, int k, int E) { return (long)T * k < 48L * E; }
+inline int down_splits(int T, int H, int I, int E, int k) {
+  if (!use_decode_path(T, k, E)) return 1;
+  long rows = (long)T * k;
+  long mtiles = rows < E ? rows : E;  // at most one 32-row tile per touched expert
+  long blocks = mtiles * (H / 64);    // one block = 2 row tiles of 32
+  int kt_total = I / 64;              // upper bound on K tiles (4-bit)
+  int s = 1;
+  while (blocks * s < 2048 && s * 2 * 8 <= kt_total) s *= 2;
+  return s;
+}
+
+inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
+  WsLayout L;
+  size_t R = (size_t)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t p = o; o = align256(o + bytes); return p; };
+  L.flags = take(256);
+  L.ids = take(R * 4);
+  L.w = take(R * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.a16 = take(R * H * 2);
+  L.ascale = take(R * 4);
+  L.h = take(R * I * (aq == MOE_ACT_I8_XH ? 4 : 2));
+  L.h16 = take(aq == MOE_ACT_I8_XH ? R * I * 2 : 0);
+  L.hscale = take(R * 4);
+  L.splits = down_splits(T, H, I, E, k);
+  L.decode = use_decode_path(T, k, E);
+  L.yp = take((size_t)L.splits * R * H * 4);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the kernel translation units). All return a hip
+// error code from the launch.
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
+                        int E, int k, int32_t* ids, float* w, float* logits, uint32_t* flags,
+                        hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
+                          hipStream_t s);
+hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int R, int H, int quant,
+                           f16* a16, float* ascale, hipStream_t s);
+hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
+                                 hipStream_t s);
+hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
+                               hipStream_t s);
+hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets, int T,
+                              int H, int I, int E, int k, const f16* a16, const float* ascale,
+                              void* h, int h_f32, bool decode, hipStream_t s);
+hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T,
+                           int H, int I, int E, int k, const f16* a, const float* ascale,
+                           float* yp, int splits, bool decode, hipStream_t s);
+hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
+hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
+                          int H, int k, void* out, int out_dt, hipStream_t s);
+hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,
+                              void* params, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
+}  // namespace moeq

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point the header declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_mixture_experts_router_amd as moeq
+from quantized_mixture_experts_router_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "moeq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(moeq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_status_strings():
+    L = _lib.LIB
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(-4) == b"workspace too small"
+
+
+def test_workspace_size_monotone():
+    a = moeq.workspace_size(16, 4096, 14336, 8, 2)
+    b = moeq.workspace_size(2048, 4096, 14336, 8, 2)
+    c = moeq.workspace_size(2048, 4096, 14336, 8, 2, moeq.ACT_I8_XH)
+    assert 0 < a < b < c
+
+
+def _route(**kw):
+    a = dict(x=16, xdt=1, Wr=16, b=None, T=4, H=64, E=8, k=2, ids=16, w=16, logits=None)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return _lib.LIB.moe_route(p(a["x"]), a["xdt"], p(a["Wr"]), p(a["b"]), a["T"], a["H"], a["E"],
+                              a["k"], p(a["ids"]), p(a["w"]), p(a["logits"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), -1), (dict(k=9), -1), (dict(E=0), -1), (dict(E=513, k=2), -1),
+    (dict(H=60), -1), (dict(xdt=7), -1), (dict(x=None), -1), (dict(ids=None), -1),
+    (dict(x=17), -3), (dict(T=-1), -1), (dict(k=33, E=64), -1),
+])
+def test_route_rejects(kw, status):
+    assert _route(**kw) == status
+
+
+def test_route_empty_is_noop():
+    assert _route(T=0, x=None, ids=None, w=None) == 0
+
+
+def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bits=None):
+    q = lambda r, c, b: _lib.QMatC(fmt, b, group, r, c, codes, params)
+    return _lib.ExpertCanonC(q(I, H, bits), q(I, H, bits), q(H, I, down_bits or bits))
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True), (dict(bits=3), False), (dict(group=48), False), (dict(fmt=3), False),
+    (dict(fmt=2, bits=2), False), (dict(I=100), False), (dict(codes=8), False),
+    (dict(params=2), False), (dict(codes=0), False), (dict(fmt=2, group=16), True),
+    (dict(bits=2, group=16), True), (dict(down_bits=2), True),
+])
+def test_packed_bytes_validation(kw, ok):
+    ec = _canon(**kw)
+    n = _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec))
+    assert (n > 0) == ok
+
+
+def test_packed_bytes_value():
+    # asym 4-bit g32: codes 0.5 B/weight; params (s, m) 4 B per 32 weights
+    ec = _canon(I=512, H=256)
+    n = _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec))
+    w = 3 * 512 * 256
+    assert n == w // 2 + w // 32 * 4
+
+
+def test_ffn_rejects_small_workspace():
+    L = _lib.LIB
+    need = L.moe_workspace_size(8, 256, 256, 4, 2, 0)
+    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                           ctypes.c_void_p(256), 8, 256, 256, 4, 2, 0, ctypes.c_void_p(256),
+                           need - 1, None)
+    assert st == -4
+    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                           ctypes.c_void_p(256), 8, 256, 256, 4, 2, 0, ctypes.c_void_p(260),
+                           need, None)
+    assert st == -3
+    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                           ctypes.c_void_p(256), 8, 200, 256, 4, 2, 0, ctypes.c_void_p(256),
+                           need, None)
+    assert st == -1
+
+
+def test_layer_forward_rejects():
+    L = _lib.LIB
+    p = ctypes.c_void_p(256)
+    ws = L.moe_workspace_size(4, 256, 256, 8, 2, 0)
+    # k > E
+    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 9, 0, p, 0, None, None, p, ws, None) == -1
+    # bad activation mode
+    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 2, 5, p, 0, None, None, p, ws, None) == -1
+    # bad output dtype
+    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 2, 0, p, 9, None, None, p, ws, None) == -1
+    # T = 0 is a no-op
+    assert L.moe_layer_forward(p, 1, p, None, p, 0, 256, 256, 8, 2, 0, p, 0, None, None, p, ws, None) == 0

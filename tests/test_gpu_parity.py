@@ -1,0 +1,218 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: routing ids bit-exact except near-tie tokens (logit gap < 1e-6,
+flagged by the oracle); permutation bit-exact; int8 codes and scales
+bit-exact; layer outputs within max per-row relative L2 2e-3 (bf16/fp32
+activations) or 1e-2 (int8 activations)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from layer_cases import Workload, rel_l2_rows, tolerance, x_to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moeq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_mixture_experts_router_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- routing
+ROUTE_CASES = [
+    ("tiny", None, None),
+    ("mixtral", 96, None),
+    ("fine_e2m1", 300, None),
+    ("hotcold", 700, None),
+    ("w4a8", 64, None),
+]
+
+
+@pytest.mark.parametrize("name,T,_", ROUTE_CASES)
+def test_route_parity(moeq, name, T, _):
+    cfg = synth.get_config(name)
+    T = cfg.T if T is None else T
+    _say(f"[route] {name} T={T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    x_np = synth.gen_x(cfg, T)
+    Wr, b = synth.gen_router(cfg)
+    x = x_to_torch(x_np, cfg.x_dtype)
+    bt = torch.from_numpy(b).cuda() if cfg.zipf_alpha > 0 else None
+    ids, w, logits = moeq.route(x, torch.from_numpy(Wr).cuda(), bt, cfg.k, want_logits=True)
+    torch.cuda.synchronize()
+    L = oracle.router_logits(oracle.x_to_f64(x_np, cfg.x_dtype), Wr, b if cfg.zipf_alpha > 0 else None)
+    rids, rw, gap, flagged = oracle.topk_softmax(L, cfg.k)
+    ids, w, logits = ids.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy()
+    ok = ~flagged
+    np.testing.assert_array_equal(ids[ok], rids[ok])
+    assert np.max(np.abs(w[ok] - rw[ok])) <= 1e-6
+    assert np.max(np.abs(w.sum(1) - 1.0)) <= 1e-6
+    assert np.all(np.abs(logits - L) <= 1e-6 * np.maximum(1.0, np.abs(L)))
+
+
+def test_route_ties_and_bias_closed_form(moeq):
+    """Zero router weights: all logits tie -> ids 0..k-1, w = 1/k; a ramp bias
+    -> ids E-1, E-2, ... with the closed-form softmax."""
+    T, H, E, k = 37, 256, 64, 4
+    x = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    Wr = torch.zeros(E, H, device="cuda")
+    ids, w = moeq.route(x, Wr, None, k)
+    assert (ids.cpu().numpy() == np.arange(k)).all()
+    assert np.allclose(w.cpu().numpy(), 1.0 / k, atol=1e-7)
+    b = torch.arange(E, dtype=torch.float32, device="cuda")
+    ids, w = moeq.route(x, Wr, b, k)
+    assert (ids.cpu().numpy() == np.arange(E - 1, E - 1 - k, -1)).all()
+    z = np.exp(-np.arange(k, dtype=np.float64))
+    assert np.allclose(w.cpu().numpy(), z / z.sum(), atol=1e-7)
+
+
+# --------------------------------------------------------------------------- permutation
+PERM_CASES = [
+    (1, 2, 8, "random"), (0, 2, 8, "random"), (33, 2, 8, "random"), (1000, 6, 256, "random"),
+    (4096, 8, 256, "random"), (2048, 2, 8, "one_expert"), (5000, 8, 64, "skewed"),
+    (16384, 2, 64, "random"), (300, 1, 1, "random"), (777, 32, 512, "random"),
+]
+
+
+@pytest.mark.parametrize("T,k,E,kind", PERM_CASES)
+def test_permute_parity(moeq, T, k, E, kind):
+    _say(f"[permute] T={T} k={k} E={E} {kind}")
+    rng = np.random.default_rng(T * 31 + k)
+    if kind == "random":
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k))
+    elif kind == "one_expert":
+        ids = np.tile(np.arange(k), (T, 1))
+    else:
+        p = 1.0 / np.arange(1, E + 1)
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    ids = ids.astype(np.int32).reshape(T, k)
+    counts, offsets, perm, inv, ws = moeq.permute(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = oracle.canonical_permute(ids, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+    np.testing.assert_array_equal(perm.cpu().numpy(), rp)
+    np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+    assert moeq.read_flags(ws) == 0
+
+
+def test_permute_flags_bad_ids(moeq):
+    ids = torch.tensor([[0, 1], [2, 9], [-1, 3]], dtype=torch.int32, device="cuda")
+    counts, offsets, perm, inv, ws = moeq.permute(ids, 4)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) & moeq.FLAG_BAD_EXPERT_ID
+    assert counts.sum().item() == 4
+
+
+# --------------------------------------------------------------------------- int8
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_quant_bit_exact(moeq, dtype):
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((67, 1000)).astype(np.float32)
+    v[3] = 0.0
+    v[5, 7] = 37.0
+    v[6] *= 1e-30
+    v[8] = np.round(v[8] * 40) / 2  # many exact halves
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(v)
+        v = synth.bf16_bits_to_f32(bits)
+        vt = x_to_torch(bits, "bf16")
+    else:
+        vt = torch.from_numpy(v).cuda()
+    q, s = moeq.act_quant_i8(vt)
+    torch.cuda.synchronize()
+    rq, rs = oracle.act_quant_i8(v)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+# --------------------------------------------------------------------------- whole layer
+LAYER_CASES = [
+    # name, T, H, I, E, k   (decode family when T*k < 48*E, else prefill)
+    ("tiny", 64, 256, 512, 8, 2),
+    ("tiny", 700, 256, 512, 8, 2),
+    ("mixtral", 40, 512, 1024, 8, 2),
+    ("mixtral", 600, 512, 1024, 8, 2),
+    ("fine_e2m1", 70, 256, 256, 256, 6),
+    ("fine_e2m1", 2100, 256, 128, 256, 6),
+    ("hotcold", 300, 256, 128, 256, 8),
+    ("hotcold", 2048, 256, 128, 256, 8),
+    ("w4a8", 16, 512, 512, 8, 2),
+    ("w4a8", 300, 512, 512, 8, 2),
+]
+
+
+def _run_layer_case(moeq, name, T, H, I, E, k, weight_mode="quantize"):
+    cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode=weight_mode,
+                              n_hot=min(64, E // 4) if name == "hotcold" else None)
+    _say(f"[layer] {name} T={T} H={H} I={I} E={E} k={k} act={cfg.act}")
+    wl = Workload(cfg)
+    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, wl.b_np if cfg.zipf_alpha > 0 else None,
+                           wl.expert, cfg.E, cfg.k, act=cfg.act)
+    return cfg, wl, out.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k", LAYER_CASES)
+def test_layer_parity(moeq, name, T, H, I, E, k):
+    cfg, wl, out, ids, w, ref = _run_layer_case(moeq, name, T, H, I, E, k)
+    ok = ~ref["flagged"]
+    np.testing.assert_array_equal(ids[ok], ref["ids"][ok])
+    err = rel_l2_rows(out[ok], ref["out"][ok])
+    _say(f"    max row rel-L2 {err.max():.3e}  mean {err.mean():.3e}  flagged {int((~ok).sum())}")
+    assert err.max() <= tolerance(cfg), err.max()
+
+
+def test_split_api_matches_layer_forward(moeq):
+    cfg = synth.scaled_config("hotcold", T=300, H=256, I=128, E=64, k=8, weight_mode="quantize", n_hot=16)
+    wl = Workload(cfg)
+    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)
+    ids2, w2 = moeq.route(wl.x, wl.Wr, wl.b, cfg.k)
+    counts, offsets, perm, inv, _ = moeq.permute(ids2, cfg.E)
+    Y = moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k)
+    out2 = moeq.combine(Y, w2, inv, cfg.T, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    assert torch.equal(out, out2)
+    # the permutation the layer used is the canonical one of its own ids
+    rc, ro, rp, ri = oracle.canonical_permute(ids.cpu().numpy(), cfg.E)
+    np.testing.assert_array_equal(perm.cpu().numpy(), rp)
+    np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+
+
+def test_layer_deterministic(moeq):
+    cfg = synth.scaled_config("fine_e2m1", T=500, H=256, I=128, E=256, k=6, weight_mode="quantize")
+    wl = Workload(cfg)
+    a = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)[0]
+    b = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_empty_batch(moeq):
+    cfg = synth.scaled_config("tiny", T=4, H=256, I=512, E=8, k=2, weight_mode="quantize")
+    wl = Workload(cfg)
+    x = wl.x[:0]
+    out, ids, w = moeq.layer_forward(x, wl.Wr, wl.b, wl.packed, cfg.k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.H)
+
+
+def test_bf16_output(moeq):
+    cfg = synth.scaled_config("mixtral", T=40, H=512, I=1024, E=8, k=2, weight_mode="quantize")
+    wl = Workload(cfg)
+    o32 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)[0]
+    o16 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, out_dtype=torch.bfloat16)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16), o16)
