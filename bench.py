@@ -1,0 +1,278 @@
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+One step = one pass of the whole layer (router + top-k/softmax, permutation,
+expert-input gather, gate/up + SwiGLU, down projection, weighted combine) over
+one batch of synthetic tokens already resident in HBM. Default workload: the
+Mixtral-8x7B-shaped layer (hidden 4096, 8 experts, top-2, intermediate 14336,
+4-bit group-32 asymmetric weights with fp16 scale+min, bf16 activations) at
+prefill, 2048 tokens. Decode batches of 1/8/32 tokens of the same layer are
+measured alongside (weight GB/s against HBM peak), each repetition preceded by
+a 1 GiB buffer write so the 256 MB last-level cache holds no weights.
+
+Prints one JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "MoE-layer tokens/s; decode weight GB/s and prefill TFLOP/s vs MI355X peak"
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["quantized_mixture_experts_router_amd/csrc/gemm.hip",
+                  "quantized_mixture_experts_router_amd/csrc/deq.h",
+                  "quantized_mixture_experts_router_amd/csrc/common.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def packed_payload_bytes(cfg, e):
+    """Algorithmic weight bytes of expert e: codes + scales (+ mins)."""
+    import synth
+    fmt, bits, group = synth.expert_format(cfg, e)
+    psz = 4 if fmt == synth.FMT_ASYM else 2
+    w = 3 * cfg.H * cfg.I
+    return w * bits // 8 + (w // group) * psz, (2 * cfg.H * cfg.I * bits // 8 + (2 * cfg.H * cfg.I // group) * psz)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="profiling aid: run only the decode repetitions")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import quantized_mixture_experts_router_amd as moeq
+    from layer_cases import Workload, rel_l2_rows
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calib:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 5}))
+        return
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------ prefill
+    cfg = synth.get_config("mixtral")
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    log(f"[bench] building workload {cfg.name} T={T} H={H} I={I} E={E} k={k}")
+    t0 = time.time()
+    wl = Workload(cfg, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] packed {wl.packed.nbytes() / 1e6:.1f} MB of experts in {time.time() - t0:.1f}s")
+
+    ws = moeq.workspace(T, H, I, E, k, 0, dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    Y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+
+    def step(evs=None):
+        ids_, w_ = moeq.route(wl.x, wl.Wr, wl.b, k)
+        counts, offsets, perm, inv, _ = moeq.permute(ids_, E, ws)
+        moeq.ffn_gather(wl.x, perm, k, wl.packed, 0, ws)
+        if evs is not None:
+            evs[0].record()
+        moeq.ffn_gate_up(T, wl.packed, offsets, k, 0, ws)
+        if evs is not None:
+            evs[1].record()
+        moeq.ffn_down(T, wl.packed, offsets, k, 0, Y, ws)
+        if evs is not None:
+            evs[2].record()
+        o = moeq.combine(Y, w_, inv, T, k)
+        return o, ids_, counts
+
+    if args.decode_only:
+        args.steps, args.warmup = 1, 0
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        o, ids_, counts = step(evs[i])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flop_gu = 2.0 * T * k * H * 2 * I
+    flop_dn = 2.0 * T * k * I * H
+    flop_layer = flop_gu + flop_dn + 2.0 * T * H * E
+    gu_tflops = flop_gu / (gu_ms * 1e-3) / 1e12
+    dn_tflops = flop_dn / (dn_ms * 1e-3) / 1e12
+    log(f"[bench] prefill: {ms_step:.3f} ms/step, gate_up {gu_ms:.3f} ms ({gu_tflops:.0f} TFLOP/s), "
+        f"down {dn_ms:.3f} ms ({dn_tflops:.0f} TFLOP/s)")
+
+    # the same layer through the one-shot entry point (must agree bit for bit)
+    out1, ids1, w1 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, k, ws=ws)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out1, o))
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "Mixtral-8x7B-shaped quantized MoE layer, prefill",
+                   "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+                   "weights": "asym 4-bit, group 32, fp16 scale+min", "activations": "bf16",
+                   "router": "fp32 weights, fp64 accumulation", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "ffn_prefill_kernel<true> (gate/up + SwiGLU)",
+                     "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_FP16_TFLOPS,
+                     "traffic": read_traffic("ffn_prefill_gate_up_mixtral_T2048_traffic.txt"),
+                     "avg_launch_ms": gu_ms, "flop_per_launch": flop_gu},
+        "phases": {"gate_up_ms": gu_ms, "down_ms": dn_ms, "down_tflops": dn_tflops,
+                   "layer_tflops": flop_layer / (ms_step * 1e-3) / 1e12},
+        "split_api_equals_layer_forward": same,
+    }
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dec = []
+        for Td in cfg.decode_T:
+            x_d = wl.x[:Td].contiguous()
+            ws_d = moeq.workspace(Td, H, I, E, k, 0, dev)
+            Yd = torch.empty((Td * k, H), dtype=torch.float32, device=dev)
+            reps = args.decode_reps
+            lay, gu = [], []
+            for r in range(reps + 3):
+                flush.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                moeq.layer_forward(x_d, wl.Wr, wl.b, wl.packed, k, ws=ws_d)
+                e1.record()
+                flush.zero_()
+                ids_d, w_d = moeq.route(x_d, wl.Wr, wl.b, k)
+                counts_d, off_d, perm_d, inv_d, _ = moeq.permute(ids_d, E, ws_d)
+                moeq.ffn_gather(x_d, perm_d, k, wl.packed, 0, ws_d)
+                g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                g0.record()
+                moeq.ffn_gate_up(Td, wl.packed, off_d, k, 0, ws_d)
+                g1.record()
+                moeq.ffn_down(Td, wl.packed, off_d, k, 0, Yd, ws_d)
+                torch.cuda.synchronize()
+                if r >= 3:
+                    lay.append(e0.elapsed_time(e1))
+                    gu.append(g0.elapsed_time(g1))
+            touched = np.nonzero(counts_d.cpu().numpy())[0]
+            tot_b = sum(packed_payload_bytes(cfg, int(e))[0] for e in touched)
+            gu_b = sum(packed_payload_bytes(cfg, int(e))[1] for e in touched)
+            lay_ms, gu_ms_d = float(np.median(lay)), float(np.median(gu))
+            d = {"tokens": Td, "experts_touched": int(len(touched)),
+                 "layer_ms": lay_ms, "layer_tokens_per_s": Td / (lay_ms * 1e-3),
+                 "layer_weight_GBps": tot_b / (lay_ms * 1e-3) / 1e9,
+                 "gate_up_ms": gu_ms_d, "gate_up_weight_GBps": gu_b / (gu_ms_d * 1e-3) / 1e9,
+                 "gate_up_frac_hbm": gu_b / (gu_ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                 "weight_bytes_touched": tot_b}
+            log(f"[bench] decode T={Td}: layer {lay_ms * 1e3:.1f} us ({d['layer_weight_GBps']:.0f} GB/s), "
+                f"gate_up {gu_ms_d * 1e3:.1f} us ({d['gate_up_weight_GBps']:.0f} GB/s)")
+            dec.append(d)
+        result["decode"] = dec
+        del flush
+
+    # ------------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        n = args.cpu_tokens
+        toks = list(range(n))
+        x_s = wl.x_np[:n]
+        log(f"[bench] cpu oracle on the first {n} tokens ...")
+        oracle.moe_layer(x_s[:1], cfg.x_dtype, wl.Wr_np, None, lambda e: wl.expert_uncached(e), E, k,
+                         tokens=[0])  # warm-up on a 1-token slice (decodes its 2 experts)
+        tc0 = time.perf_counter()
+        ref = oracle.moe_layer(x_s, cfg.x_dtype, wl.Wr_np, None, lambda e: wl.expert_uncached(e), E, k)
+        tc = time.perf_counter() - tc0
+        got = o[:n].cpu().numpy()
+        ok = ~ref["flagged"]
+        err = rel_l2_rows(got[ok], ref["out"][ok])
+        ids_ok = bool(np.array_equal(ids_.cpu().numpy()[:n][ok], ref["ids"][ok]))
+        result["cpu_baseline"] = {
+            "value": n / tc, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {n} of the {T} prefill tokens (all their experts decoded); "
+                      f"fp64 NumPy, {tc:.1f} s; BLAS threads {blas_threads}, block decoding single-threaded",
+        }
+        result["parity"] = {"tokens_checked": n, "max_row_rel_l2": float(err.max()),
+                            "ids_bit_exact": ids_ok, "tolerance": 2e-3}
+        log(f"[bench] oracle {n / tc:.3f} tokens/s; parity max row rel-L2 {err.max():.2e}, ids exact {ids_ok}")
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -29,8 +29,9 @@
  *    returns MOE_ERR_HIP.
  *  - Data-dependent trouble found on the device (an expert id out of range,
  *    NaN router logits) sets bits of the flag word at the start of the
- *    workspace (MOE_FLAG_*), readable after the stream synchronises. The
- *    flag word is cleared by every call that takes a workspace.
+ *    workspace (MOE_FLAG_*), readable after the stream synchronises.
+ *    moe_permute and moe_layer_forward clear it; the FFN phases only add
+ *    bits to it.
  *  - Matrices are row-major; int32 indices; fp32 weights of the router.
  */
 #ifndef MOEQ_H
@@ -72,7 +73,9 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_I8_X = 1, MOE_ACT_I8_XH = 2 } moe_actq;
 
 enum {
   MOE_FLAG_BAD_EXPERT_ID = 1u << 0, /* an id outside [0,E) reached moe_permute */
-  MOE_FLAG_NAN_LOGIT = 1u << 1      /* a router logit was NaN (routing undefined) */
+  MOE_FLAG_NAN_LOGIT = 1u << 1,     /* a router logit was NaN (routing undefined) */
+  MOE_FLAG_FORMAT_NOT_LAUNCHED = 1u << 2 /* an expert with rows has a format outside
+                                            fmt_mask: its rows were not computed */
 };
 
 /* One weight matrix W[rows, cols] in the canonical block format.
@@ -130,6 +133,16 @@ size_t moe_packed_expert_bytes(const moe_expert_canon* src);
 moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t dst_bytes,
                            moe_packed_expert* out_desc, void* stream);
 
+/* Bit mask of the block formats used by E packed experts (host array of the
+ * descriptors moe_pack_expert filled): bit i is set when some gate/up or
+ * down matrix has format i, with i = 4*c + g, c = 0 asym 4-bit, 1 asym 2-bit,
+ * 2 e2m1, and g = 0,1,2,3 for group 16, 32, 64, 128. The FFN entry points
+ * take this mask (fmt_mask) and run one kernel per format in it; 0 means
+ * every supported format (correct for any expert set, but each absent format
+ * still costs a launch). Experts whose format is missing from a non-zero mask
+ * are skipped and flag MOE_FLAG_FORMAT_NOT_LAUNCHED. Host only. */
+uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
+
 /* Workspace bytes the layer entry points need for these sizes. Host only. */
 size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
 
@@ -140,7 +153,7 @@ size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
  * Outputs (device): topk_ids int32 [T,k] (descending logit), topk_w fp32
  * [T,k] (softmax over the k selected logits, computed in fp64), logits fp32
  * [T,E] (optional, NULL to skip). Constraints: 1 <= k <= min(E, 32),
- * E <= 512, H % 8 == 0, x/Wr 16-byte aligned. T == 0 is a no-op. */
+ * E <= 256, H % 8 == 0, x/Wr 16-byte aligned. T == 0 is a no-op. */
 moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b,
                      int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
                      float* logits, void* stream);
@@ -149,8 +162,8 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
  * topk_ids (device) int32 [T,k]. Outputs (device, int32): counts [E],
  * offsets [E+1] (exclusive prefix sum, offsets[E] = T*k), perm_token [T*k]
  * (token of the r-th sorted assignment; ascending token inside each
- * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: workspace of at
- * least moe_workspace_size(T, 1, 1, E, k, MOE_ACT_NONE) bytes (flag word).
+ * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: at least 256
+ * bytes, 256-byte aligned (its first word is the flag word).
  * Ids outside [0,E) are dropped and flag MOE_FLAG_BAD_EXPERT_ID. */
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
@@ -159,30 +172,38 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
 /* Grouped expert FFN over the permuted assignments (steps 3-5):
  * for every sorted row r of expert e (offsets[e] <= r < offsets[e+1]):
  *   Y[r,:] = FFN_e(x[perm_token[r], :]).
- * experts (device): moe_packed_expert [E]. Y (device): fp32 [T*k, H].
+ * experts (device): moe_packed_expert [E]; fmt_mask: see moe_format_mask.
+ * Y (device): fp32 [T*k, H].
  * Decoded weights and the SwiGLU output h run through fp16 matrix-core
  * operations with fp32 accumulation; with int8 activations the int8 codes
  * enter the matrix cores exactly and the per-row scales are applied in fp32.
  * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes, 256-aligned.
  * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I. */
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
-                             const int32_t* offsets, const int32_t* perm_token, int T, int H,
-                             int I, int E, int k, moe_actq aq, float* Y, void* ws,
+                             uint32_t fmt_mask, const int32_t* offsets, const int32_t* perm_token,
+                             int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* The two halves of moe_grouped_ffn_q, for callers that time or overlap them.
- * moe_ffn_gate_up: gathers (and optionally quantises) the expert inputs and
- * runs the fused gate/up + SwiGLU, leaving h in the workspace.
- * moe_ffn_down: (optionally quantises h and) runs the down projection into
- * Y (fp32 [T*k, H]). Same arguments and workspace as moe_grouped_ffn_q; call
- * gate_up then down on the same stream with the same workspace. */
-moe_status moe_ffn_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
-                           const int32_t* offsets, const int32_t* perm_token, int T, int H,
-                           int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
-                           void* stream);
-moe_status moe_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T,
-                        int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
-                        size_t ws_bytes, void* stream);
+/* The three phases of moe_grouped_ffn_q, for callers that time or overlap
+ * them; call them in this order on one stream with one workspace (same
+ * arguments and workspace size as moe_grouped_ffn_q).
+ * moe_ffn_gather: copies the expert input rows x[perm_token[r]] into the
+ *   workspace as fp16 (or, under MOE_ACT_I8_*, as their int8 codes plus
+ *   per-row scales). One kernel.
+ * moe_ffn_gate_up: fused gate/up projection + SwiGLU of every sorted row,
+ *   leaving h in the workspace. One kernel.
+ * moe_ffn_down: (under MOE_ACT_I8_XH, per-row int8 quantisation of h, then)
+ *   the down projection into Y (fp32 [T*k, H]); at decode sizes the K range
+ *   is split over blocks and a reduction kernel sums the parts into Y. */
+moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_token, int T, int H,
+                          int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
+                          void* stream);
+moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
+                           const int32_t* offsets, int T, int H, int I, int E, int k,
+                           moe_actq aq, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
+                        const int32_t* offsets, int T, int H, int I, int E, int k, moe_actq aq,
+                        float* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted combine (step 5's sum): out[t,:] = sum_j topk_w[t,j] * Y[inv[t*k+j], :],
  * accumulated in fp32 in slot order j = 0..k-1. out (device): [T,H] fp32 or
@@ -194,8 +215,8 @@ moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, 
  * topk_ids / topk_w (device, optional): receive the routing when non-NULL.
  * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes. */
 moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, const float* b,
-                             const moe_packed_expert* experts, int T, int H, int I, int E,
-                             int k, moe_actq aq, void* out, moe_dtype out_dt,
+                             const moe_packed_expert* experts, uint32_t fmt_mask, int T, int H,
+                             int I, int E, int k, moe_actq aq, void* out, moe_dtype out_dt,
                              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                              void* stream);
 

@@ -2,7 +2,8 @@
 
 Every translation unit compiles in parallel to _build/*.o, then one link
 produces quantized_mixture_experts_router_amd/libmoeq.so.
-Usage: python -m quantized_mixture_experts_router_amd.build [-j N]
+Usage: python quantized_mixture_experts_router_amd/build.py [-j N]
+(run as a file: importing the package would load the library being rebuilt)
 """
 import argparse
 import concurrent.futures as cf

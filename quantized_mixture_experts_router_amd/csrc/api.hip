@@ -6,7 +6,7 @@ using namespace moeq;
 
 namespace {
 
-constexpr int kMaxE = 512;
+constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -67,23 +67,29 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 
 inline char* ws_at(void* ws, size_t off) { return (char*)ws + off; }
 
-// gate/up half of the grouped FFN (workspace already validated)
-moe_status run_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
-                       const int32_t* offsets, const int32_t* perm, int T, int H, int I, int E,
-                       int k, moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
-  const int R = T * k;
-  f16* a16 = (f16*)ws_at(ws, L.a16);
-  float* ascale = (float*)ws_at(ws, L.ascale);
-  MOE_TRY(launch_gather_a(x, xdt, perm, R, H, aq != MOE_ACT_NONE, a16, ascale, s));
-  MOE_TRY(launch_ffn_gate_up(experts, offsets, T, H, I, E, k, a16,
-                             aq != MOE_ACT_NONE ? ascale : nullptr, ws_at(ws, L.h),
-                             aq == MOE_ACT_I8_XH, L.decode, s));
+// phases of the grouped FFN (workspace already validated)
+moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, int H, int k,
+                      moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
+  MOE_TRY(launch_gather_a(x, xdt, perm, T * k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
+                          (float*)ws_at(ws, L.ascale), s));
   return MOE_OK;
 }
 
-moe_status run_down(const moe_packed_expert* experts, const int32_t* offsets, int T, int H,
-                    int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws, float* yp,
-                    hipStream_t s) {
+inline uint32_t effective_mask(uint32_t m) { return m ? m : ((1u << F_COUNT) - 1u); }
+
+moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
+                       int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
+                       hipStream_t s) {
+  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), (uint32_t*)ws_at(ws, L.flags),
+                             T, H, I, E, k, (const f16*)ws_at(ws, L.a16),
+                             aq != MOE_ACT_NONE ? (const float*)ws_at(ws, L.ascale) : nullptr,
+                             ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, s));
+  return MOE_OK;
+}
+
+moe_status run_down(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
+                    int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
+                    float* yp, hipStream_t s) {
   const int R = T * k;
   const f16* ain = (const f16*)ws_at(ws, L.h);
   const float* sc = nullptr;
@@ -94,20 +100,26 @@ moe_status run_down(const moe_packed_expert* experts, const int32_t* offsets, in
     ain = h16;
     sc = hs;
   }
-  MOE_TRY(launch_ffn_down(experts, offsets, T, H, I, E, k, ain, sc, yp, L.splits, L.decode, s));
+  MOE_TRY(launch_ffn_down(experts, offsets, effective_mask(mask), (uint32_t*)ws_at(ws, L.flags), T,
+                          H, I, E, k, ain, sc, yp, L.splits, L.decode, s));
   return MOE_OK;
 }
 
-moe_status check_ffn_args(const void* experts, const int32_t* offsets, bool need_offsets, int T,
-                          int H, int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
-                          WsLayout& L) {
+moe_status check_ws(int T, int H, int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
+                    WsLayout& L) {
   moe_status st = check_sizes(T, H, I, E, k);
   if (st != MOE_OK) return st;
   if (aq < MOE_ACT_NONE || aq > MOE_ACT_I8_XH) return MOE_ERR_INVALID_ARG;
-  if (!experts || !ws || (need_offsets && !offsets)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(ws, 256) || !aligned(experts, 16)) return MOE_ERR_ALIGNMENT;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   L = ws_layout(T, H, I, E, k, aq);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status check_experts(const void* experts, const int32_t* offsets) {
+  if (!experts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (!aligned(experts, 16) || !aligned(offsets, 4)) return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }
 
@@ -168,6 +180,18 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
   return MOE_OK;
 }
 
+uint32_t moe_format_mask(const moe_packed_expert* descs, int E) {
+  if (!descs || E <= 0) return 0;
+  uint32_t m = 0;
+  for (int e = 0; e < E; ++e) {
+    int a = fmt_id(descs[e].gu_fmt, descs[e].gu_bits, descs[e].gu_group);
+    int b = fmt_id(descs[e].dn_fmt, descs[e].dn_bits, descs[e].dn_group);
+    if (a >= 0) m |= 1u << a;
+    if (b >= 0) m |= 1u << b;
+  }
+  return m;
+}
+
 size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
   return ws_layout(T, H, I, E, k, aq).total;
@@ -202,46 +226,65 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
   return MOE_OK;
 }
 
-moe_status moe_ffn_gate_up(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
-                           const int32_t* offsets, const int32_t* perm_token, int T, int H, int I,
-                           int E, int k, moe_actq aq, void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_token, int T, int H,
+                          int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
+                          void* stream) {
   WsLayout L;
-  moe_status st = check_ffn_args(experts, offsets, true, T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!x || !perm_token)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  return run_gate_up(x, xdt, experts, offsets, perm_token, T, H, I, E, k, aq, L, ws,
-                     (hipStream_t)stream);
+  if (!x || !perm_token) return MOE_ERR_INVALID_ARG;
+  return run_gather(x, xdt, perm_token, T, H, k, aq, L, ws, (hipStream_t)stream);
 }
 
-moe_status moe_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T, int H,
-                        int I, int E, int k, moe_actq aq, float* Y, void* ws, size_t ws_bytes,
-                        void* stream) {
+moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
+                           const int32_t* offsets, int T, int H, int I, int E, int k, moe_actq aq,
+                           void* ws, size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ffn_args(experts, offsets, true, T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
+  if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  return run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
+                        const int32_t* offsets, int T, int H, int I, int E, int k, moe_actq aq,
+                        float* Y, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout L;
+  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  if (st != MOE_OK) return st;
+  if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T > 0 && !Y) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   const size_t n = (size_t)T * k * H;
   if (L.decode && L.splits > 1) {
     float* yp = (float*)ws_at(ws, L.yp);
-    st = run_down(experts, offsets, T, H, I, E, k, aq, L, ws, yp, s);
+    st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, yp, s);
     if (st != MOE_OK) return st;
     return hip_status(launch_reduce_splits(yp, L.splits, n, Y, s));
   }
-  return run_down(experts, offsets, T, H, I, E, k, aq, L, ws, Y, s);
+  return run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, Y, s);
 }
 
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
-                             const int32_t* offsets, const int32_t* perm_token, int T, int H,
-                             int I, int E, int k, moe_actq aq, float* Y, void* ws,
+                             uint32_t fmt_mask, const int32_t* offsets, const int32_t* perm_token,
+                             int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
                              size_t ws_bytes, void* stream) {
-  moe_status st = moe_ffn_gate_up(x, xdt, experts, offsets, perm_token, T, H, I, E, k, aq, ws,
-                                  ws_bytes, stream);
+  WsLayout L;
+  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
-  return moe_ffn_down(experts, offsets, T, H, I, E, k, aq, Y, ws, ws_bytes, stream);
+  if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !perm_token || !Y) return MOE_ERR_INVALID_ARG;
+  st = moe_ffn_gather(x, xdt, perm_token, T, H, I, E, k, aq, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, Y, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, int T, int H,
@@ -255,12 +298,15 @@ moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, 
 }
 
 moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, const float* b,
-                             const moe_packed_expert* experts, int T, int H, int I, int E, int k,
-                             moe_actq aq, void* out, moe_dtype out_dt, int32_t* topk_ids,
+                             const moe_packed_expert* experts, uint32_t fmt_mask, int T, int H,
+                             int I, int E, int k, moe_actq aq, void* out, moe_dtype out_dt,
+                             int32_t* topk_ids,
                              float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ffn_args(experts, nullptr, false, T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
+  if (!experts) return MOE_ERR_INVALID_ARG;
+  if (!aligned(experts, 16)) return MOE_ERR_ALIGNMENT;
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -279,9 +325,11 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
   MOE_TRY(launch_zero_u32(flags, 64, s));
   MOE_TRY(launch_route(x, xdt, Wr, b, T, H, E, k, ids, w, nullptr, flags, s));
   MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
-  st = run_gate_up(x, xdt, experts, offsets, perm, T, H, I, E, k, aq, L, ws, s);
+  st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
   if (st != MOE_OK) return st;
-  st = run_down(experts, offsets, T, H, I, E, k, aq, L, ws, yp, s);
+  st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, s);
+  if (st != MOE_OK) return st;
+  st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, yp, s);
   if (st != MOE_OK) return st;
   return hip_status(launch_combine(yp, L.decode ? L.splits : 1, w, inv, T, H, k, out, out_dt, s));
 }

@@ -30,7 +30,7 @@ enum FmtId : int {
   F_COUNT
 };
 
-__host__ __device__ inline int fmt_id(int fmt, int bits, int group) {
+__host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   int g = group == 16 ? 0 : group == 32 ? 1 : group == 64 ? 2 : group == 128 ? 3 : -1;
   if (g < 0) return -1;
   if (fmt == MOE_W_ASYM && bits == 4) return F_A4G16 + g;
@@ -52,6 +52,7 @@ __host__ __device__ inline int fmt_id(int fmt, int bits, int group) {
 //    fp16 s = 2 B each). Stored [row tile][entry][32 rows][EB bytes].
 template <int FMT, int BITS, int GROUP>
 struct Fmt {
+  static constexpr int ID = fmt_id(FMT, BITS, GROUP);
   static constexpr int kFmt = FMT;
   static constexpr int kBits = BITS;
   static constexpr int kGroup = GROUP;
@@ -154,12 +155,14 @@ hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* 
                                  hipStream_t s);
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
                                hipStream_t s);
-hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets, int T,
-                              int H, int I, int E, int k, const f16* a16, const float* ascale,
-                              void* h, int h_f32, bool decode, hipStream_t s);
-hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets, int T,
-                           int H, int I, int E, int k, const f16* a, const float* ascale,
-                           float* yp, int splits, bool decode, hipStream_t s);
+hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
+                              uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
+                              int k, const f16* a16, const float* ascale, void* h, int h_f32,
+                              bool decode, hipStream_t s);
+hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
+                           uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
+                           const f16* ain, const float* ascale, float* yp, int splits,
+                           bool decode, hipStream_t s);
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);

@@ -16,6 +16,14 @@
 
 namespace moeq {
 
+// Global-address-space views: loads through them compile to global_load_*
+// (not flat_load_*), which keeps LDS and memory wait counters separate.
+#define MOEQ_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ inline const MOEQ_GLOBAL T* gptr(const void* p) {
+  return (const MOEQ_GLOBAL T*)(p);
+}
+
 __device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -24,18 +32,18 @@ struct PBuf;
 template <>
 struct PBuf<2> {
   uint32_t w[1];
-  __device__ inline void load(const uint8_t* p) { w[0] = *reinterpret_cast<const uint16_t*>(p); }
+  __device__ inline void load(const uint8_t* p) { w[0] = *gptr<uint16_t>(p); }
 };
 template <>
 struct PBuf<4> {
   uint32_t w[1];
-  __device__ inline void load(const uint8_t* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ inline void load(const uint8_t* p) { w[0] = *gptr<uint32_t>(p); }
 };
 template <>
 struct PBuf<8> {
   uint32_t w[2];
   __device__ inline void load(const uint8_t* p) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    u32x2 v = *gptr<u32x2>(p);
     w[0] = v.x;
     w[1] = v.y;
   }
@@ -44,7 +52,7 @@ template <>
 struct PBuf<16> {
   uint32_t w[4];
   __device__ inline void load(const uint8_t* p) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    u32x4 v = *gptr<u32x4>(p);
     w[0] = v.x;
     w[1] = v.y;
     w[2] = v.z;

@@ -1,0 +1,507 @@
+// Grouped expert GEMMs: gate/up + SwiGLU and the down projection, on weights
+// decoded in registers from packed 4-/2-bit blocks.
+//
+// Expert FFN: three matrices per expert, gate/up/down ("AlphaQ" blog,
+// section 2.2; MoE mixed-precision notes, section 3.3), in the gated SwiGLU
+// form h = silu(a Wg^T) * (a Wu^T), y = h Wd^T. SwiGLU is fused into the
+// gate/up epilogue (the notes fuse the expert activation into the linear,
+// section 3.6). Only the experts a token was routed to are read ("Sparse
+// activation ... 2% activation", section 3.1: the saving is in bandwidth).
+//
+// Two kernel families share the tile layout and the in-register decoding:
+//  * decode (few rows per expert): a block is 4 wavefronts on the same 32-row
+//    token tile and the same 64 weight rows, splitting K; weights stream from
+//    HBM straight into registers (16-byte loads per lane, 1 KiB per wave and
+//    tile), are decoded to fp16 and fed to v_mfma_f32_32x32x16_f16 with the
+//    token rows padded to 32. The 4 partial sums meet in LDS.
+//  * prefill (many rows per expert): a block owns 128 token rows and 256
+//    weight rows; the token tile is staged in LDS (double-buffered, shared by
+//    the 4 wavefronts) and each wavefront streams its own 64 weight rows into
+//    registers; weights are decoded one K tile ahead of the matrix cores,
+//    overlapping the vector-ALU decode with the MFMAs.
+// Every kernel is instantiated per block format; a launch handles the experts
+// of its format. Tasks are (expert, n-tile, m-tile), expert-major, so blocks
+// that share weight tiles run together; each block derives its task from the
+// segment offsets, so no host synchronisation is needed.
+#include "common.h"
+#include "deq.h"
+
+namespace moeq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int FID>
+struct FmtOf;
+template <> struct FmtOf<F_A4G16> { using T = Fmt<MOE_W_ASYM, 4, 16>; };
+template <> struct FmtOf<F_A4G32> { using T = Fmt<MOE_W_ASYM, 4, 32>; };
+template <> struct FmtOf<F_A4G64> { using T = Fmt<MOE_W_ASYM, 4, 64>; };
+template <> struct FmtOf<F_A4G128> { using T = Fmt<MOE_W_ASYM, 4, 128>; };
+template <> struct FmtOf<F_A2G16> { using T = Fmt<MOE_W_ASYM, 2, 16>; };
+template <> struct FmtOf<F_A2G32> { using T = Fmt<MOE_W_ASYM, 2, 32>; };
+template <> struct FmtOf<F_A2G64> { using T = Fmt<MOE_W_ASYM, 2, 64>; };
+template <> struct FmtOf<F_A2G128> { using T = Fmt<MOE_W_ASYM, 2, 128>; };
+template <> struct FmtOf<F_E4G16> { using T = Fmt<MOE_W_E2M1, 4, 16>; };
+template <> struct FmtOf<F_E4G32> { using T = Fmt<MOE_W_E2M1, 4, 32>; };
+template <> struct FmtOf<F_E4G64> { using T = Fmt<MOE_W_E2M1, 4, 64>; };
+template <> struct FmtOf<F_E4G128> { using T = Fmt<MOE_W_E2M1, 4, 128>; };
+
+__device__ inline f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Row of accumulator register r for lane `lane` in a 32x32 MFMA output tile.
+__device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+struct FfnArgs {
+  const moe_packed_expert* experts;
+  const int32_t* offsets;
+  uint32_t* flags;
+  uint32_t fmt_mask;
+  int E;
+  int K;          // reduction dim (H for gate/up, I for down)
+  int N;          // outputs per expert (I for gate/up, H for down)
+  const f16* a;   // [R, K] rows in sorted order
+  const float* ascale;  // per-row scale (int8 inputs) or null
+  void* out;      // gate/up: h [R, N] (f16 or f32); down: [splits][R][N] f32
+  int out_f32;
+  int R;
+  int splits;
+};
+
+struct Task {
+  int e, row0, mcount, nt;
+};
+
+// Format id of expert e's gate/up (GU) or down matrices.
+template <bool GU>
+__device__ inline int expert_fid(const moe_packed_expert* experts, int e) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(experts + e)[GU ? 0 : 1];
+  return fmt_id(w & 0xff, (w >> 8) & 0xff, w >> 16);
+}
+
+// Task lookup over the experts of format `fid`: tasks of expert e =
+// ceil(count_e / BM) * NB, expert-major, then n-tile, then m-tile.
+// The first block also flags experts with rows whose format is not in the
+// launch mask (their rows would otherwise be left uncomputed).
+template <bool GU>
+__device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task& task) {
+  __shared__ int s_wsum[kThreads / 64];
+  __shared__ int s_res[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_res[0] = -1;
+  int cnt[2], ntk[2];
+  int local = 0;
+  bool missing = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    int c = 0, f = -1;
+    if (e < a.E) {
+      c = a.offsets[e + 1] - a.offsets[e];
+      f = expert_fid<GU>(a.experts, e);
+      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
+    }
+    cnt[q] = c;
+    ntk[q] = f == fid ? ((c + BM - 1) / BM) * NB : 0;
+    local += ntk[q];
+  }
+  if (missing && blockIdx.x == 0 && blockIdx.y == 0 && a.flags)
+    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int start = incl - local;
+  for (int w = 0; w < wave; ++w) start += s_wsum[w];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (L >= start && L < start + ntk[q]) {
+      const int e = 2 * tid + q;
+      const int rel = L - start;
+      const int mt = (cnt[q] + BM - 1) / BM;
+      const int mi = rel % mt;
+      s_res[0] = e;
+      s_res[1] = a.offsets[e] + mi * BM;
+      s_res[2] = min(BM, cnt[q] - mi * BM);
+      s_res[3] = rel / mt;
+    }
+    start += ntk[q];
+  }
+  __syncthreads();
+  task.e = s_res[0];
+  task.row0 = s_res[1];
+  task.mcount = s_res[2];
+  task.nt = s_res[3];
+  return task.e >= 0;
+}
+
+__device__ inline void store_gu(const FfnArgs& a, int row, int col, float g, float u) {
+  const float sc = a.ascale ? a.ascale[row] : 1.0f;
+  const float h = silu_mul(g * sc, u * sc);
+  if (a.out_f32)
+    reinterpret_cast<float*>(a.out)[(size_t)row * a.N + col] = h;
+  else
+    reinterpret_cast<f16*>(a.out)[(size_t)row * a.N + col] = (f16)h;
+}
+
+__device__ inline void store_dn(const FfnArgs& a, int split, int row, int col, float y) {
+  const float sc = a.ascale ? a.ascale[row] : 1.0f;
+  reinterpret_cast<float*>(a.out)[((size_t)split * a.R + row) * a.N + col] = y * sc;
+}
+
+template <class F>
+struct BTile {
+  u32x4 w0, w1;
+  PBuf<F::EB> q0, q1;
+};
+
+// ===========================================================================
+// Decode family
+// ===========================================================================
+template <class F, bool GU>
+__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
+  __shared__ float red[4 * 2 * 16 * 64];
+  const int NB = GU ? a.N / 32 : a.N / 64;
+  Task t;
+  if (!find_task<GU>(a, F::ID, 32, NB, blockIdx.x, t)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, kh = lane >> 5;
+  const int KTn = a.K / F::KT;
+  const int NE = a.K / F::GE;
+  const moe_packed_expert* ex = a.experts + t.e;
+  const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
+  const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
+  const int rt0 = 2 * t.nt;  // gate tile (gate/up) or first of two row tiles (down)
+  const uint8_t* c0 = codes + (size_t)rt0 * KTn * 1024 + lane * 16;
+  const uint8_t* c1 = c0 + (size_t)KTn * 1024;
+  const uint8_t* p0 = params + ((size_t)rt0 * NE * 32 + n) * F::EB;
+  const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
+
+  const int split = blockIdx.y;
+  const int per = (KTn + a.splits - 1) / a.splits;
+  const int kb = split * per, ke = min(KTn, kb + per);
+
+  const bool arow = n < t.mcount;
+  const f16* ap = a.a + (size_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN;
+
+  auto load = [&](int kt, BTile<F>& b, f16x8* av) {
+    b.w0 = *gptr<u32x4>(c0 + (size_t)kt * 1024);
+    b.w1 = *gptr<u32x4>(c1 + (size_t)kt * 1024);
+    const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
+    b.q0.load(p0 + (size_t)ei * 32 * F::EB);
+    b.q1.load(p1 + (size_t)ei * 32 * F::EB);
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s)
+      av[s] = arow ? *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s) : f16x8{};
+  };
+  f32x16 acc0 = {}, acc1 = {};
+  auto compute = [&](const BTile<F>& b, const f16x8* av) {
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s) {
+      const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s);
+      const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s);
+      acc0 = mfma32(av[s], b0, acc0);
+      acc1 = mfma32(av[s], b1, acc1);
+    }
+  };
+  // two K tiles in flight per wavefront
+  for (int kt = kb + wave; kt < ke; kt += 8) {
+    BTile<F> b0, b1;
+    f16x8 av0[F::STEPS], av1[F::STEPS];
+    const bool two = kt + 4 < ke;
+    load(kt, b0, av0);
+    if (two) load(kt + 4, b1, av1);
+    compute(b0, av0);
+    if (two) compute(b1, av1);
+  }
+
+  // reduce the 4 wavefronts' partial sums: red[w][m][r][lane]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[((wave * 2 + 0) * 16 + r) * 64 + lane] = acc0[r];
+    red[((wave * 2 + 1) * 16 + r) * 64 + lane] = acc1[r];
+  }
+  __syncthreads();
+  // wavefront w finalises registers r = 4w .. 4w+3
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * wave + rr;
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v0 += red[((w * 2 + 0) * 16 + r) * 64 + lane];
+      v1 += red[((w * 2 + 1) * 16 + r) * 64 + lane];
+    }
+    const int i = acc_row(r, lane);
+    if (i < t.mcount) {
+      const int row = t.row0 + i;
+      if (GU) {
+        store_gu(a, row, 32 * t.nt + n, v0, v1);
+      } else {
+        store_dn(a, split, row, 64 * t.nt + n, v0);
+        store_dn(a, split, row, 64 * t.nt + 32 + n, v1);
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Prefill family
+// ===========================================================================
+constexpr int kBM = 128;
+constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
+
+__device__ inline int xcd_remap(int b, int nblk) {
+  // blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+  // range of tasks so that blocks sharing weight tiles share an L2
+  const int xcd = b & 7, slot = b >> 3;
+  const int q = nblk >> 3, r = nblk & 7;
+  return xcd * q + min(xcd, r) + slot;
+}
+
+template <class F, bool GU>
+__global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
+  constexpr int STR = F::KT + 8;  // LDS row stride in halves (16-byte pad)
+  __shared__ __attribute__((aligned(16))) f16 lds[2 * kBM * STR];
+  const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
+  Task t;
+  if (!find_task<GU>(a, F::ID, kBM, NB, xcd_remap(blockIdx.x, gridDim.x), t)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, kh = lane >> 5;
+  const int KTn = a.K / F::KT;
+  const int NE = a.K / F::GE;
+  const moe_packed_expert* ex = a.experts + t.e;
+  const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
+  const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
+  // gate/up: wavefront w owns output tile 4*nt + w = row tiles (2j, 2j+1);
+  // down: wavefront w owns row tiles 8*nt + 2w and 8*nt + 2w + 1.
+  const int rt0 = GU ? 2 * (4 * t.nt + wave) : 8 * t.nt + 2 * wave;
+  const bool on = GU || rt0 < a.N / 32;
+  // a wavefront past the last row tile (down, N % 256 != 0) streams a valid
+  // tile and discards it, so every wavefront runs the same straight-line loop
+  const int rtl = on ? rt0 : a.N / 32 - 2;
+  const uint8_t* c0 = codes + (size_t)rtl * KTn * 1024 + lane * 16;
+  const uint8_t* c1 = c0 + (size_t)KTn * 1024;
+  const uint8_t* p0 = params + ((size_t)rtl * NE * 32 + n) * F::EB;
+  const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
+
+  // A staging: kBM rows x KT halves in 16-byte chunks; rows past the segment
+  // repeat its last row (their outputs are never stored)
+  constexpr int CPR = F::KT / 8;
+  constexpr int CPT = kBM * CPR / kThreads;
+  const f16* asrc[CPT];
+  int adst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads;
+    const int r = ch / CPR, c = ch % CPR;
+    asrc[i] = a.a + (size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c;
+    adst[i] = r * STR + 8 * c;
+  }
+  struct ARegs {
+    f16x8 v[CPT];
+  };
+  auto load_a = [&](int kt, ARegs& ar) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) ar.v[i] = *gptr<f16x8>(asrc[i] + (size_t)kt * F::KT);
+  };
+  auto store_a = [&](f16* buf, const ARegs& ar) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<f16x8*>(buf + adst[i]) = ar.v[i];
+  };
+  auto load_b = [&](int kt, BTile<F>& b) {
+    b.w0 = *gptr<u32x4>(c0 + (size_t)kt * 1024);
+    b.w1 = *gptr<u32x4>(c1 + (size_t)kt * 1024);
+    const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
+    b.q0.load(p0 + (size_t)ei * 32 * F::EB);
+    b.q1.load(p1 + (size_t)ei * 32 * F::EB);
+  };
+  struct BDeq {
+    f16x8 b0[F::STEPS], b1[F::STEPS];
+  };
+  auto decode_b = [&](const BTile<F>& b, BDeq& d) {
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s) {
+      d.b0[s] = dequant_step<F>(b.w0, b.q0, s);
+      d.b1[s] = dequant_step<F>(b.w1, b.q1, s);
+    }
+  };
+  f32x16 acc[kMT][2];
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi) {
+    acc[mi][0] = f32x16{};
+    acc[mi][1] = f32x16{};
+  }
+  const int aoff = n * STR + kh * F::SPAN;
+
+  // Pipeline. During tile kt the matrix cores consume the fp16 weights of
+  // tile kt (decoded one tile earlier) while the vector ALUs decode the raw
+  // codes of tile kt+1; raw codes are fetched three tiles ahead and token
+  // tiles two tiles ahead. Prefetches past the last tile re-read the last
+  // tile (unused) so the loop body stays branch-free and the wait counters
+  // exact.
+  f16* const LB0 = lds;
+  f16* const LB1 = lds + kBM * STR;
+  BTile<F> R0, R1;  // raw weight codes (tile parity)
+  ARegs A0, A1;     // token tile registers (tile parity)
+  BDeq D0, D1;      // decoded fp16 weights (tile parity)
+  auto mma_decode = [&](const f16* buf, const BDeq& d, const BTile<F>& raw, BDeq& dn) {
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s) {
+      dn.b0[s] = dequant_step<F>(raw.w0, raw.q0, s);
+      dn.b1[s] = dequant_step<F>(raw.w1, raw.q1, s);
+      if (on) {
+#pragma unroll
+        for (int mi = 0; mi < kMT; ++mi) {
+          const f16x8 av = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff + 8 * s);
+          acc[mi][0] = mfma32(av, d.b0[s], acc[mi][0]);
+          acc[mi][1] = mfma32(av, d.b1[s], acc[mi][1]);
+        }
+      }
+    }
+  };
+  load_b(0, R0);
+  load_a(0, A0);
+  load_b(min(1, KTn - 1), R1);
+  load_a(min(1, KTn - 1), A1);
+  store_a(LB0, A0);
+  decode_b(R0, D0);
+  load_b(min(2, KTn - 1), R0);
+  __syncthreads();
+  auto even_tile = [&](int kt) {  // LDS buffer 0, decoded D0; decodes R1 -> D1
+    load_a(min(kt + 2, KTn - 1), A0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
+    mma_decode(LB0, D0, R1, D1);
+    load_b(min(kt + 3, KTn - 1), R1);
+    store_a(LB1, A1);
+    __syncthreads();
+  };
+  auto odd_tile = [&](int kt) {  // LDS buffer 1, decoded D1; decodes R0 -> D0
+    load_a(min(kt + 2, KTn - 1), A1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_decode(LB1, D1, R0, D0);
+    load_b(min(kt + 3, KTn - 1), R0);
+    store_a(LB0, A0);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < KTn; kt += 2) {
+    even_tile(kt);
+    odd_tile(kt + 1);
+  }
+  if (kt < KTn) even_tile(kt);
+
+  if (!on) return;
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = mi * 32 + acc_row(r, lane);
+      if (i < t.mcount) {
+        const int row = t.row0 + i;
+        if (GU) {
+          store_gu(a, row, 32 * (4 * t.nt + wave) + n, acc[mi][0][r], acc[mi][1][r]);
+        } else {
+          store_dn(a, 0, row, 32 * rt0 + n, acc[mi][0][r]);
+          store_dn(a, 0, row, 32 * (rt0 + 1) + n, acc[mi][1][r]);
+        }
+      }
+    }
+  }
+}
+
+inline int max_tiles(int R, int E, int BM) { return (R + BM - 1) / BM + (R < E ? R : E); }
+
+template <int FID, bool GU>
+hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
+  using F = typename FmtOf<FID>::T;
+  if (decode) {
+    const int NB = GU ? a.N / 32 : a.N / 64;
+    dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
+    hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
+    dim3 grid(max_tiles(a.R, a.E, kBM) * NB);
+    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <bool GU>
+hipError_t launch_all(const FfnArgs& a, bool decode, hipStream_t s) {
+  if (a.R == 0) return hipSuccess;
+  const uint32_t mask = a.fmt_mask;
+  hipError_t e = hipSuccess;
+#define MOEQ_LAUNCH(FID)                                              \
+  if (e == hipSuccess && ((mask >> FID) & 1u)) e = launch_one<FID, GU>(a, decode, s);
+  MOEQ_LAUNCH(F_A4G16)
+  MOEQ_LAUNCH(F_A4G32)
+  MOEQ_LAUNCH(F_A4G64)
+  MOEQ_LAUNCH(F_A4G128)
+  MOEQ_LAUNCH(F_A2G16)
+  MOEQ_LAUNCH(F_A2G32)
+  MOEQ_LAUNCH(F_A2G64)
+  MOEQ_LAUNCH(F_A2G128)
+  MOEQ_LAUNCH(F_E4G16)
+  MOEQ_LAUNCH(F_E4G32)
+  MOEQ_LAUNCH(F_E4G64)
+  MOEQ_LAUNCH(F_E4G128)
+#undef MOEQ_LAUNCH
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
+                              uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
+                              int k, const f16* a16, const float* ascale, void* h, int h_f32,
+                              bool decode, hipStream_t s) {
+  FfnArgs a;
+  a.experts = experts;
+  a.offsets = offsets;
+  a.flags = flags;
+  a.fmt_mask = fmt_mask;
+  a.E = E;
+  a.K = H;
+  a.N = I;
+  a.a = a16;
+  a.ascale = ascale;
+  a.out = h;
+  a.out_f32 = h_f32;
+  a.R = T * k;
+  a.splits = 1;
+  return launch_all<true>(a, decode, s);
+}
+
+hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
+                           uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
+                           const f16* ain, const float* ascale, float* yp, int splits,
+                           bool decode, hipStream_t s) {
+  FfnArgs a;
+  a.experts = experts;
+  a.offsets = offsets;
+  a.flags = flags;
+  a.fmt_mask = fmt_mask;
+  a.E = E;
+  a.K = I;
+  a.N = H;
+  a.a = ain;
+  a.ascale = ascale;
+  a.out = yp;
+  a.out_f32 = 1;
+  a.R = T * k;
+  a.splits = decode ? splits : 1;
+  return launch_all<false>(a, decode, s);
+}
+
+}  // namespace moeq

@@ -8,6 +8,12 @@
 // experts), so logits are accumulated in fp64: products of bf16/fp32 inputs
 // with fp32 weights are exact in fp64 and the sum carries ~1e-16 relative
 // error, far below the 1e-6 gap at which a token counts as a near-tie.
+//
+// One block = 2..16 tokens x all experts. Each thread owns a 2-token x 8-expert
+// register tile and a slice of the hidden dimension: slices are 8 columns
+// wide and interleaved, so neighbouring lanes read neighbouring 16-/32-byte
+// chunks of the same rows. Partial sums meet in LDS, then each wavefront runs
+// the top-k of 4 tokens with wave-wide (value desc, index asc) argmax rounds.
 #include "common.h"
 
 namespace moeq {
@@ -15,104 +21,149 @@ namespace moeq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTB = 16;   // tokens per block
-constexpr int kHC = 16;   // hidden chunk staged in LDS
-constexpr int kMaxE = 512;
+constexpr int kTM = 2;         // tokens per thread
+constexpr int kEM = 8;         // experts per thread
 constexpr int kInvalid = 0x7fffffff;
 
-__device__ inline double load_x(const void* x, int xdt, size_t idx) {
-  if (xdt == MOE_BF16) {
-    uint32_t u = (uint32_t)((const uint16_t*)x)[idx] << 16;
-    return (double)__uint_as_float(u);
-  }
-  return (double)((const float*)x)[idx];
+// Token groups per block (2 tokens each): as few as keep the grid near 1024
+// blocks (small batches spread the hidden dimension over every thread), but
+// enough that re-reading the router weights per block stays under ~256 MB of
+// L2 traffic (large E*H), and at most 8 (kTG * expert groups <= 256 threads).
+__host__ __device__ inline int route_tgroups(int T, int H, int E) {
+  int tg = 1;
+  while (tg < 8 && (T + 2 * tg - 1) / (2 * tg) > 1024) tg *= 2;
+  const double traffic = 2.0 * T * E * H;  // bytes of Wr reads with one group
+  while (tg < 8 && traffic / tg > 256e6) tg *= 2;
+  const int EG = (E + 7) / 8;
+  while (tg > 1 && tg * EG > 256) tg /= 2;
+  return tg;
 }
 
-struct StageBufs {
-  double xs[kTB][kHC + 1];
-  float ws[kMaxE][kHC + 1];
-};
-constexpr size_t kStageBytes = sizeof(StageBufs);
-constexpr size_t kLogitBytes = sizeof(double) * kTB * (kMaxE + 1);
-constexpr size_t kSmemBytes = kStageBytes > kLogitBytes ? kStageBytes : kLogitBytes;
+__device__ inline void load_x8(const void* x, int xdt, size_t idx, double* o) {
+  if (xdt == MOE_BF16) {
+    u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)x + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = (double)__uint_as_float(v[i] << 16);
+      o[2 * i + 1] = (double)__uint_as_float(v[i] & 0xffff0000u);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>((const float*)x + idx);
+    f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = (double)a[i];
+      o[4 + i] = (double)b[i];
+    }
+  }
+}
 
-// One block: kTB tokens x all E experts. Thread (tg = tid / 64, eg = tid % 64)
-// owns tokens 4*tg .. 4*tg+3 and experts eg, eg+64, eg+128, ... (< E).
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const void* __restrict__ x, int xdt, const float* __restrict__ Wr,
     const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, float* __restrict__ logits_out, uint32_t* __restrict__ flags) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
-  StageBufs& st = *reinterpret_cast<StageBufs*>(smem);
-  double (*lg)[kMaxE + 1] = reinterpret_cast<double (*)[kMaxE + 1]>(smem);
-
+  extern __shared__ double smem[];  // [KS*TG*EG*kTM*kEM partials][kTB*(E+1) logits]
   const int tid = threadIdx.x;
+  const int kTG = route_tgroups(T, H, E);
+  const int kTB = kTG * kTM;
   const int t0 = blockIdx.x * kTB;
-  const int tg = tid / 64, eg = tid % 64;
-  const int EPT = (E + 63) / 64;  // experts per thread (<= 8)
+  const int EG = (E + kEM - 1) / kEM;             // expert groups
+  const int KS = max(1, kThreads / (kTG * EG));   // hidden-dimension slices
+  const int active = KS * kTG * EG;               // threads with work (<= 256)
+  // lane -> (slice, token group, expert group); slice varies fastest
+  const int ks = tid % KS;
+  const int tg = (tid / KS) % kTG;
+  const int eg = tid / (KS * kTG);
+  const bool on = tid < active;
 
-  double acc[4][8];
+  double acc[kTM][kEM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < kEM; ++j) acc[i][j] = 0.0;
 
-  for (int h0 = 0; h0 < H; h0 += kHC) {
-    for (int i = tid; i < kTB * kHC; i += kThreads) {
-      int tt = i / kHC, hh = i % kHC;
-      int t = t0 + tt, h = h0 + hh;
-      st.xs[tt][hh] = (t < T && h < H) ? load_x(x, xdt, (size_t)t * H + h) : 0.0;
+  if (on) {
+    int trow[kTM];
+    bool tval[kTM];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      int t = t0 + tg * kTM + i;
+      tval[i] = t < T;
+      trow[i] = tval[i] ? t : 0;
     }
-    for (int i = tid; i < E * kHC; i += kThreads) {
-      int e = i / kHC, hh = i % kHC;
-      int h = h0 + hh;
-      st.ws[e][hh] = h < H ? Wr[(size_t)e * H + h] : 0.f;
-    }
-    __syncthreads();
+    int erow[kEM];
+#pragma unroll
+    for (int j = 0; j < kEM; ++j) erow[j] = min(eg * kEM + j, E - 1);
 #pragma unroll 4
-    for (int hh = 0; hh < kHC; ++hh) {
-      double xv[4];
+    for (int h = 8 * ks; h < H; h += 8 * KS) {
+      double xv[kTM][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = st.xs[4 * tg + i][hh];
+      for (int i = 0; i < kTM; ++i) load_x8(x, xdt, (size_t)trow[i] * H + h, xv[i]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < EPT) {
-          int e = eg + 64 * j;
-          double wv = e < E ? (double)st.ws[e][hh] : 0.0;
+      for (int j = 0; j < kEM; ++j) {
+        const f32x4* wp = reinterpret_cast<const f32x4*>(Wr + (size_t)erow[j] * H + h);
+        f32x4 wa = wp[0], wb = wp[1];
+        double wv[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = fma(xv[i], wv, acc[i][j]);
+        for (int q = 0; q < 4; ++q) {
+          wv[q] = (double)wa[q];
+          wv[4 + q] = (double)wb[q];
         }
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[i][j] = fma(xv[i][q], wv[q], acc[i][j]);
       }
     }
-    __syncthreads();
   }
 
-  // add the bias; logits to LDS (fp64) and optionally to global (fp32)
+  // reduce the hidden slices: partial[slot][ks] with slot = (tg, eg, i, j)
+  double* part = smem;
+  if (KS > 1 && on) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < EPT) {
-      int e = eg + 64 * j;
-      if (e < E) {
-        double bv = bias ? (double)bias[e] : 0.0;
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int tt = 4 * tg + i;
-          double v = acc[i][j] + bv;
-          lg[tt][e] = v;
-          int t = t0 + tt;
-          if (logits_out && t < T) logits_out[(size_t)t * E + e] = (float)v;
-        }
-      }
+      for (int j = 0; j < kEM; ++j)
+        part[(((size_t)(eg * kTG + tg) * kTM + i) * kEM + j) * KS + ks] = acc[i][j];
+  }
+  __syncthreads();
+  double* lg = smem + (KS > 1 ? (size_t)KS * kTG * EG * kTM * kEM : 0);  // [kTB][E+1]
+  if (KS > 1) {
+    const int nslots = kTG * EG * kTM * kEM;
+    for (int slot = tid; slot < nslots; slot += kThreads) {
+      double s = 0.0;
+      for (int q = 0; q < KS; ++q) s += part[(size_t)slot * KS + q];
+      const int j = slot % kEM, i = (slot / kEM) % kTM, g = slot / (kEM * kTM);
+      const int tgi = g % kTG, egi = g / kTG;
+      const int e = egi * kEM + j, tt = tgi * kTM + i;
+      if (e < E) lg[tt * (E + 1) + e] = s;
     }
+  } else if (on) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kEM; ++j) {
+        const int e = eg * kEM + j;
+        if (e < E) lg[(tg * kTM + i) * (E + 1) + e] = acc[i][j];
+      }
+  }
+  __syncthreads();
+  // bias; optional fp32 logits
+  for (int i = tid; i < kTB * E; i += kThreads) {
+    const int tt = i / E, e = i % E;
+    double v = lg[tt * (E + 1) + e] + (bias ? (double)bias[e] : 0.0);
+    lg[tt * (E + 1) + e] = v;
+    if (logits_out && t0 + tt < T) logits_out[(size_t)(t0 + tt) * E + e] = (float)v;
   }
   __syncthreads();
 
-  // top-k: wave w handles tokens 4w .. 4w+3
+  // top-k: wavefront w handles tokens w, w+4, ...
   const int wave = tid / 64, lane = tid % 64;
-  for (int q = 0; q < 4; ++q) {
-    const int tt = wave * 4 + q;
+  const int EPL = (E + 63) / 64;  // candidates per lane (<= 4)
+  for (int tt = wave; tt < kTB; tt += 4) {
     const int t = t0 + tt;
     if (t >= T) break;
+    const double* row = lg + tt * (E + 1);
     uint32_t taken = 0;
     bool nan_seen = false;
     double my_v = 0.0, top_v = 0.0;
@@ -120,10 +171,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     for (int r = 0; r < k; ++r) {
       double bv = 0.0;
       int bi = kInvalid;
-      for (int j = 0; j < EPT; ++j) {
+      for (int j = 0; j < EPL; ++j) {
         int e = lane + 64 * j;
         if (e < E && !((taken >> j) & 1u)) {
-          double v = lg[tt][e];
+          double v = row[e];
           if (v != v) nan_seen = true;
           if (bi == kInvalid || v > bv) {  // increasing e: ties keep the lower index
             bv = v;
@@ -135,8 +186,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       for (int off = 32; off >= 1; off >>= 1) {
         double ov = __shfl_xor(bv, off);
         int oi = __shfl_xor(bi, off);
-        bool better = oi != kInvalid &&
-                      (bi == kInvalid || ov > bv || (ov == bv && oi < bi));
+        bool better = oi != kInvalid && (bi == kInvalid || ov > bv || (ov == bv && oi < bi));
         if (better) {
           bv = ov;
           bi = oi;
@@ -167,8 +217,13 @@ hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b,
                         int E, int k, int32_t* ids, float* w, float* logits, uint32_t* flags,
                         hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((T + kTB - 1) / kTB);
-  hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), 0, s, x, xdt, Wr, b, T, H, E, k, ids, w,
+  const int TG = route_tgroups(T, H, E), TB = TG * kTM;
+  const int EG = (E + kEM - 1) / kEM;
+  const int KS = kThreads / (TG * EG) > 1 ? kThreads / (TG * EG) : 1;
+  size_t part = KS > 1 ? (size_t)KS * TG * EG * kTM * kEM : 0;
+  size_t smem = sizeof(double) * (part + (size_t)TB * (E + 1));
+  dim3 grid((T + TB - 1) / TB);
+  hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), smem, s, x, xdt, Wr, b, T, H, E, k, ids, w,
                      logits, flags);
   return hipGetLastError();
 }

@@ -49,7 +49,7 @@ def _route(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(k=0), -1), (dict(k=9), -1), (dict(E=0), -1), (dict(E=513, k=2), -1),
+    (dict(k=0), -1), (dict(k=9), -1), (dict(E=0), -1), (dict(E=257, k=2), -1),
     (dict(H=60), -1), (dict(xdt=7), -1), (dict(x=None), -1), (dict(ids=None), -1),
     (dict(x=17), -3), (dict(T=-1), -1), (dict(k=33, E=64), -1),
 ])
@@ -88,19 +88,16 @@ def test_packed_bytes_value():
 
 def test_ffn_rejects_small_workspace():
     L = _lib.LIB
+    p = ctypes.c_void_p(256)
     need = L.moe_workspace_size(8, 256, 256, 4, 2, 0)
-    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
-                           ctypes.c_void_p(256), 8, 256, 256, 4, 2, 0, ctypes.c_void_p(256),
-                           need - 1, None)
-    assert st == -4
-    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
-                           ctypes.c_void_p(256), 8, 256, 256, 4, 2, 0, ctypes.c_void_p(260),
-                           need, None)
-    assert st == -3
-    st = L.moe_ffn_gate_up(ctypes.c_void_p(256), 1, ctypes.c_void_p(256), ctypes.c_void_p(256),
-                           ctypes.c_void_p(256), 8, 200, 256, 4, 2, 0, ctypes.c_void_p(256),
-                           need, None)
-    assert st == -1
+    assert L.moe_ffn_gate_up(p, 0, p, 8, 256, 256, 4, 2, 0, p, need - 1, None) == -4
+    assert L.moe_ffn_gate_up(p, 0, p, 8, 256, 256, 4, 2, 0, ctypes.c_void_p(260), need, None) == -3
+    assert L.moe_ffn_gate_up(p, 0, p, 8, 200, 256, 4, 2, 0, p, need, None) == -1
+    assert L.moe_ffn_gate_up(None, 0, p, 8, 256, 256, 4, 2, 0, p, need, None) == -1
+    assert L.moe_ffn_gather(p, 1, p, 8, 256, 256, 4, 2, 0, p, need - 1, None) == -4
+    assert L.moe_ffn_gather(p, 1, None, 8, 256, 256, 4, 2, 0, p, need, None) == -1
+    assert L.moe_ffn_down(p, 0, p, 8, 256, 256, 4, 2, 3, p, p, need, None) == -1
+    assert L.moe_ffn_gather(p, 1, None, 0, 256, 256, 4, 2, 0, p, need, None) == 0
 
 
 def test_layer_forward_rejects():
@@ -108,10 +105,10 @@ def test_layer_forward_rejects():
     p = ctypes.c_void_p(256)
     ws = L.moe_workspace_size(4, 256, 256, 8, 2, 0)
     # k > E
-    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 9, 0, p, 0, None, None, p, ws, None) == -1
+    assert L.moe_layer_forward(p, 1, p, None, p, 0, 4, 256, 256, 8, 9, 0, p, 0, None, None, p, ws, None) == -1
     # bad activation mode
-    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 2, 5, p, 0, None, None, p, ws, None) == -1
+    assert L.moe_layer_forward(p, 1, p, None, p, 0, 4, 256, 256, 8, 2, 5, p, 0, None, None, p, ws, None) == -1
     # bad output dtype
-    assert L.moe_layer_forward(p, 1, p, None, p, 4, 256, 256, 8, 2, 0, p, 9, None, None, p, ws, None) == -1
+    assert L.moe_layer_forward(p, 1, p, None, p, 0, 4, 256, 256, 8, 2, 0, p, 9, None, None, p, ws, None) == -1
     # T = 0 is a no-op
-    assert L.moe_layer_forward(p, 1, p, None, p, 0, 256, 256, 8, 2, 0, p, 0, None, None, p, ws, None) == 0
+    assert L.moe_layer_forward(p, 1, p, None, p, 0, 0, 256, 256, 8, 2, 0, p, 0, None, None, p, ws, None) == 0
