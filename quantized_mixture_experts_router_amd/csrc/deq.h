@@ -2,14 +2,12 @@
 //
 // Asymmetric blocks (w = s*q + m; AWQ-style zero point of the "sparse
 // activation" page, section 4.4; the per-expert bit widths of the AlphaQ blog,
-// section 4.2): a pair of b-bit codes is masked into the mantissas of two
-// fp16 numbers with exponent field 25 (value 1024 + q, exact), 1024 is
-// subtracted (exact), and one packed fp16 fma applies the group scale and
-// minimum (one rounding to fp16).
-// e2m1 blocks: placing the three magnitude bits at fp16 bits 9..11 and the
-// sign at bit 15 gives exactly v(q) * 2^-14 for all 16 codes (code 1 lands in
-// the fp16 subnormal 2^-15 = 0.5 * 2^-14); one exact multiply by 2^14 and one
-// multiply by the group scale follow.
+// section 4.2): a pair of b-bit codes is OR-ed into the mantissas of two fp16
+// numbers (exact), the fp16 offset is subtracted (exact), and one packed fp16
+// fma applies the group scale and minimum (one rounding to fp16).
+// e2m1 blocks (the 4-bit floating-point weights of the quantized-MoE
+// article): the gfx950 fp4 converter yields the exact fp16 value of each code,
+// then one fp16 multiply by the group scale (one rounding).
 #pragma once
 
 #include "common.h"
@@ -60,46 +58,91 @@ struct PBuf<16> {
   }
 };
 
-// Decode the 8 codes of MFMA step `s` from a lane's 16-byte code block.
+// Constants of the decoders, held in VGPRs for the whole kernel: gfx9 VOP3
+// encodings take no literal operand, so v_and_or_b32 needs its mask and its
+// exponent pattern in registers. `opaque` stops the compiler from folding
+// them back into literals.
+__device__ inline uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Asymmetric b-bit codes: within a 32-bit word the pair (code 2i, code 2i+1)
+// sits in the two 16-bit halves at the same bit offset o = b*i (mod 8 after a
+// shift by 8 for the upper pairs). OR-ing the masked field into the mantissa
+// of an fp16 number whose last mantissa bit weighs 2^-o, i.e. 2^(10-o), gives
+// exactly 2^(10-o) + q; subtracting 2^(10-o) leaves q.
+struct DeqConsts {
+  uint32_t mask[4];   // field masks for offsets 0, b, 2b, 3b (b = bits), both halves
+  uint32_t magic[4];  // fp16 pairs 2^(10 - offset)
+};
+
 template <class F>
-__device__ inline f16x8 dequant_step(const u32x4& c, const PBuf<F::EB>& pb, int s) {
+__device__ inline DeqConsts make_deq_consts() {
+  DeqConsts k;
+  const uint32_t fm = (1u << F::kBits) - 1u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int off = F::kBits * j;
+    const bool used = F::kFmt == MOE_W_ASYM && (F::kBits == 2 || j < 2);
+    const uint32_t mk = ((fm << off) | (fm << (16 + off)));
+    const uint32_t e = 25u - off;  // fp16 exponent field of 2^(10 - off)
+    const uint32_t mg = (e << 10) | (e << 26);
+    k.mask[j] = used ? opaque(mk) : 0u;
+    k.magic[j] = used ? opaque(mg) : 0u;
+  }
+  return k;
+}
+
+__device__ inline f16x2 magic_sub(int off) {
+  // -(2^(10 - off)) in both halves (exact)
+  const uint32_t e = 25u - off;
+  return -as_f16x2((e << 10) | (e << 26));
+}
+
+// Decode the 8 codes of MFMA step `s` from a lane's 16-byte code block into
+// the fp16 B fragment (values in the K order the packer laid out).
+template <class F>
+__device__ inline f16x8 dequant_step(const u32x4& c, const PBuf<F::EB>& pb, int s,
+                                     const DeqConsts& k) {
   // parameter index inside the entry for lane-local codes [8s, 8s+8)
   const int p = F::kGroup < F::SPAN ? (8 * s) / F::kGroup : 0;
-  uint32_t d;
-  int base_sh;
-  if (F::kBits == 4) {
-    d = c[s];
-    base_sh = 0;
-  } else {
-    d = c[s >> 1];
-    base_sh = (s & 1) * 8;  // fields 4..7 of the pair sequence start at bit 8
-  }
   f16x2 out[4];
   if (F::kFmt == MOE_W_ASYM) {
     const uint32_t sm = pb.w[p];
     const f16x2 s2 = as_f16x2((sm & 0xffffu) * 0x10001u);
     const f16x2 m2 = as_f16x2((sm >> 16) * 0x10001u);
-    const f16x2 k1024 = as_f16x2(0x64006400u);
+    if (F::kBits == 4) {
+      // word s: pairs at offsets 0, 4 (low byte) and 0, 4 after >> 8
+      const uint32_t d = c[s];
+      const uint32_t e = d >> 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t t;
-      if (F::kBits == 4)
-        t = ((d >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-      else
-        t = ((d >> (base_sh + 2 * i)) & 0x00030003u) | 0x64006400u;
-      f16x2 q = as_f16x2(t) - k1024;
-      out[i] = __builtin_elementwise_fma(q, s2, m2);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t src = i < 2 ? d : e;
+        const int j = i & 1;
+        const uint32_t t = (src & k.mask[j]) | k.magic[j];
+        out[i] = __builtin_elementwise_fma(as_f16x2(t) + magic_sub(4 * j), s2, m2);
+      }
+    } else {
+      // word s/2 holds two steps; step s uses offsets 0, 2, 4, 6 of byte (s & 1)
+      const uint32_t d = c[s >> 1];
+      const uint32_t src = (s & 1) ? d >> 8 : d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = (src & k.mask[j]) | k.magic[j];
+        out[j] = __builtin_elementwise_fma(as_f16x2(t) + magic_sub(2 * j), s2, m2);
+      }
     }
   } else {
+    // e2m1: natural nibble order; the gfx950 converter maps byte b of the word
+    // to (low nibble, high nibble) exactly (scale 1.0), then one fp16 multiply
     const uint32_t sw = (pb.w[p >> 1] >> (16 * (p & 1))) & 0xffffu;
     const f16x2 s2 = as_f16x2(sw * 0x10001u);
-    const f16x2 two14 = as_f16x2(0x74007400u);  // 16384.0
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t t = d >> (4 * i);
-      uint32_t h = ((t & 0x00070007u) << 9) | ((t & 0x00080008u) << 12);
-      out[i] = (as_f16x2(h) * two14) * s2;
-    }
+    const uint32_t d = c[s];
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * s2;
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * s2;
+    out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * s2;
+    out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * s2;
   }
   f16x8 r;
   r[0] = out[0][0];

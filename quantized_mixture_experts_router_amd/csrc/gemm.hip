@@ -17,8 +17,8 @@
 //  * prefill (many rows per expert): a block owns 128 token rows and 256
 //    weight rows; the token tile is staged in LDS (double-buffered, shared by
 //    the 4 wavefronts) and each wavefront streams its own 64 weight rows into
-//    registers; weights are decoded one K tile ahead of the matrix cores,
-//    overlapping the vector-ALU decode with the MFMAs.
+//    registers; two blocks share a CU so that one block's vector-ALU decode
+//    overlaps the other's MFMAs.
 // Every kernel is instantiated per block format; a launch handles the experts
 // of its format. Tasks are (expert, n-tile, m-tile), expert-major, so blocks
 // that share weight tiles run together; each block derives its task from the
@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
   const uint8_t* p0 = params + ((size_t)rt0 * NE * 32 + n) * F::EB;
   const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
 
+  const DeqConsts dk = make_deq_consts<F>();
   const int split = blockIdx.y;
   const int per = (KTn + a.splits - 1) / a.splits;
   const int kb = split * per, ke = min(KTn, kb + per);
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
   auto compute = [&](const BTile<F>& b, const f16x8* av) {
 #pragma unroll
     for (int s = 0; s < F::STEPS; ++s) {
-      const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s);
-      const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s);
+      const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s, dk);
+      const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s, dk);
       acc0 = mfma32(av[s], b0, acc0);
       acc1 = mfma32(av[s], b1, acc1);
     }
@@ -269,7 +270,7 @@ __device__ inline int xcd_remap(int b, int nblk) {
 }
 
 template <class F, bool GU>
-__global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
   constexpr int STR = F::KT + 8;  // LDS row stride in halves (16-byte pad)
   __shared__ __attribute__((aligned(16))) f16 lds[2 * kBM * STR];
   const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
   const uint8_t* p0 = params + ((size_t)rtl * NE * 32 + n) * F::EB;
   const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
 
+  const DeqConsts dk = make_deq_consts<F>();
   // A staging: kBM rows x KT halves in 16-byte chunks; rows past the segment
   // repeat its last row (their outputs are never stored)
   constexpr int CPR = F::KT / 8;
@@ -326,16 +328,6 @@ __global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
     b.q0.load(p0 + (size_t)ei * 32 * F::EB);
     b.q1.load(p1 + (size_t)ei * 32 * F::EB);
   };
-  struct BDeq {
-    f16x8 b0[F::STEPS], b1[F::STEPS];
-  };
-  auto decode_b = [&](const BTile<F>& b, BDeq& d) {
-#pragma unroll
-    for (int s = 0; s < F::STEPS; ++s) {
-      d.b0[s] = dequant_step<F>(b.w0, b.q0, s);
-      d.b1[s] = dequant_step<F>(b.w1, b.q1, s);
-    }
-  };
   f32x16 acc[kMT][2];
 #pragma unroll
   for (int mi = 0; mi < kMT; ++mi) {
@@ -344,30 +336,52 @@ __global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
   }
   const int aoff = n * STR + kh * F::SPAN;
 
-  // Pipeline. During tile kt the matrix cores consume the fp16 weights of
-  // tile kt (decoded one tile earlier) while the vector ALUs decode the raw
-  // codes of tile kt+1; raw codes are fetched three tiles ahead and token
-  // tiles two tiles ahead. Prefetches past the last tile re-read the last
-  // tile (unused) so the loop body stays branch-free and the wait counters
-  // exact.
+  // Pipeline: raw weight codes and token tiles are fetched two K tiles ahead;
+  // inside a tile the codes of MFMA step s+1 are decoded while the MFMAs of
+  // step s run. Two blocks share a CU, so one block's decode and barriers
+  // overlap the other's matrix-core work. Prefetches past the last tile
+  // re-read the last tile (unused) so the loop body stays branch-free and the
+  // wait counters exact.
   f16* const LB0 = lds;
   f16* const LB1 = lds + kBM * STR;
   BTile<F> R0, R1;  // raw weight codes (tile parity)
   ARegs A0, A1;     // token tile registers (tile parity)
-  BDeq D0, D1;      // decoded fp16 weights (tile parity)
-  auto mma_decode = [&](const f16* buf, const BDeq& d, const BTile<F>& raw, BDeq& dn) {
+  auto mma_jit = [&](const f16* buf, const BTile<F>& raw) {
+    // step s: token fragments of step s+1 are read from LDS and weight codes
+    // of step s+1 decoded while the 2*kMT MFMAs of step s run
+    f16x8 av[kMT];
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+      av[mi] = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff);
+    f16x8 c0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
+    f16x8 c1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
 #pragma unroll
     for (int s = 0; s < F::STEPS; ++s) {
-      dn.b0[s] = dequant_step<F>(raw.w0, raw.q0, s);
-      dn.b1[s] = dequant_step<F>(raw.w1, raw.q1, s);
+      f16x8 an[kMT];
+      f16x8 n0 = c0, n1 = c1;
+      if (s + 1 < F::STEPS) {
+#pragma unroll
+        for (int mi = 0; mi < kMT; ++mi)
+          an[mi] = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff + 8 * (s + 1));
+        n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
+        n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
+      }
+      // LDS reads of step s+1 stay above the MFMAs of step s (vector and
+      // scalar ALU work may still move across)
+      __builtin_amdgcn_sched_barrier(0x0006);
       if (on) {
 #pragma unroll
         for (int mi = 0; mi < kMT; ++mi) {
-          const f16x8 av = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff + 8 * s);
-          acc[mi][0] = mfma32(av, d.b0[s], acc[mi][0]);
-          acc[mi][1] = mfma32(av, d.b1[s], acc[mi][1]);
+          acc[mi][0] = mfma32(av[mi], c0, acc[mi][0]);
+          acc[mi][1] = mfma32(av[mi], c1, acc[mi][1]);
         }
       }
+      if (s + 1 < F::STEPS) {
+#pragma unroll
+        for (int mi = 0; mi < kMT; ++mi) av[mi] = an[mi];
+      }
+      c0 = n0;
+      c1 = n1;
     }
   };
   load_b(0, R0);
@@ -375,22 +389,20 @@ __global__ __launch_bounds__(kThreads) void ffn_prefill_kernel(FfnArgs a) {
   load_b(min(1, KTn - 1), R1);
   load_a(min(1, KTn - 1), A1);
   store_a(LB0, A0);
-  decode_b(R0, D0);
-  load_b(min(2, KTn - 1), R0);
   __syncthreads();
-  auto even_tile = [&](int kt) {  // LDS buffer 0, decoded D0; decodes R1 -> D1
-    load_a(min(kt + 2, KTn - 1), A0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
-    mma_decode(LB0, D0, R1, D1);
-    load_b(min(kt + 3, KTn - 1), R1);
+  auto even_tile = [&](int kt) {  // LDS buffer 0, raw slot 0
+    mma_jit(LB0, R0);
+    const int kn = min(kt + 2, KTn - 1);
+    load_b(kn, R0);
+    load_a(kn, A0);
     store_a(LB1, A1);
     __syncthreads();
   };
-  auto odd_tile = [&](int kt) {  // LDS buffer 1, decoded D1; decodes R0 -> D0
-    load_a(min(kt + 2, KTn - 1), A1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_decode(LB1, D1, R0, D0);
-    load_b(min(kt + 3, KTn - 1), R0);
+  auto odd_tile = [&](int kt) {  // LDS buffer 1, raw slot 1
+    mma_jit(LB1, R1);
+    const int kn = min(kt + 2, KTn - 1);
+    load_b(kn, R1);
+    load_a(kn, A1);
     store_a(LB0, A0);
     __syncthreads();
   };

@@ -54,11 +54,13 @@ __global__ void pack_codes_kernel(PackArgs a) {
   uint32_t out[4];
   const int per = 32 / a.bits;        // codes per word (8 or 16)
   const int half = per / 2;
+  const bool pairs = a.fmt == MOE_W_ASYM;  // e2m1 keeps the natural order
   for (int d = 0; d < 4; ++d) {
     uint32_t v = 0;
     for (int p = 0; p < per; ++p) {
-      // field p of word d holds code per*d + (p < half ? 2p : 2(p-half)+1)
-      int c = per * d + (p < half ? 2 * p : 2 * (p - half) + 1);
+      // asymmetric: field p of word d holds code per*d + (p < half ? 2p : 2(p-half)+1),
+      // so each 16-bit half carries one code of every consecutive pair
+      int c = pairs ? per * d + (p < half ? 2 * p : 2 * (p - half) + 1) : per * d + p;
       v |= get_field(w, c, a.bits) << (p * a.bits);
     }
     out[d] = v;
