@@ -103,33 +103,36 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// one block per token; out[t] = sum_j w[t,j] * sum_s yp[s][inv[t*k+j]]
+// out[t] = sum_j w[t,j] * sum_s yp[s][inv[t*k+j]]: one thread per (token,
+// 4 columns); the partial-sum loads of all slots and splits are independent
+// and issued together. Summation order is fixed (deterministic).
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ yp, int splits,
                                                          size_t split_stride,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ inv, int H,
                                                          int k, void* __restrict__ out, int out_dt) {
-  const int t = blockIdx.x;
-  for (int c4 = threadIdx.x; c4 < H / 4; c4 += kThreads) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = inv[(size_t)t * k + j];
-      if (r < 0) continue;  // dropped assignment (out-of-range expert id)
-      const float wt = w[(size_t)t * k + j];
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < splits; ++q)
-        y += *reinterpret_cast<const f32x4*>(yp + q * split_stride + (size_t)r * H + 4 * c4);
-      acc += wt * y;
-    }
-    if (out_dt == MOE_F32) {
-      *reinterpret_cast<f32x4*>((float*)out + (size_t)t * H + 4 * c4) = acc;
-    } else {
-      uint16_t* o = (uint16_t*)out + (size_t)t * H + 4 * c4;
-      o[0] = f32_to_bf16_rne(acc[0]);
-      o[1] = f32_to_bf16_rne(acc[1]);
-      o[2] = f32_to_bf16_rne(acc[2]);
-      o[3] = f32_to_bf16_rne(acc[3]);
-    }
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * kThreads + threadIdx.x;
+  if (c4 >= H / 4) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(size_t)t * k + j];
+    if (r < 0) continue;  // dropped assignment (out-of-range expert id)
+    const float wt = w[(size_t)t * k + j];
+    const float* src = yp + (size_t)r * H + 4 * c4;
+    f32x4 y = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll 8
+    for (int q = 1; q < splits; ++q) y += *reinterpret_cast<const f32x4*>(src + q * split_stride);
+    acc += wt * y;
+  }
+  if (out_dt == MOE_F32) {
+    *reinterpret_cast<f32x4*>((float*)out + (size_t)t * H + 4 * c4) = acc;
+  } else {
+    uint16_t* o = (uint16_t*)out + (size_t)t * H + 4 * c4;
+    o[0] = f32_to_bf16_rne(acc[0]);
+    o[1] = f32_to_bf16_rne(acc[1]);
+    o[2] = f32_to_bf16_rne(acc[2]);
+    o[3] = f32_to_bf16_rne(acc[3]);
   }
 }
 
@@ -173,8 +176,9 @@ hipError_t launch_combine(const float* yp, int splits, const float* w, const int
                           int H, int k, void* out, int out_dt, hipStream_t s) {
   if (T == 0) return hipSuccess;
   size_t stride = (size_t)T * k * H;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kThreads), 0, s, yp, splits, stride, w, inv, H,
-                     k, out, out_dt);
+  dim3 grid((H / 4 + kThreads - 1) / kThreads, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, yp, splits, stride, w, inv, H, k,
+                     out, out_dt);
   return hipGetLastError();
 }
 

@@ -25,23 +25,35 @@ __device__ inline const MOEQ_GLOBAL T* gptr(const void* p) {
 __device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Loads of weight streams. NT = non-temporal: data read once per call (the
+// decode GEMVs) streams past the caches, which sustains a much higher HBM
+// read rate than cached loads.
+template <bool NT, class T>
+__device__ inline T ldg(const void* p) {
+  if (NT) return __builtin_nontemporal_load(gptr<T>(p));
+  return *gptr<T>(p);
+}
+
 template <int EB>
 struct PBuf;
 template <>
 struct PBuf<2> {
   uint32_t w[1];
-  __device__ inline void load(const uint8_t* p) { w[0] = *gptr<uint16_t>(p); }
+  template <bool NT = false>
+  __device__ inline void load(const uint8_t* p) { w[0] = ldg<NT, uint16_t>(p); }
 };
 template <>
 struct PBuf<4> {
   uint32_t w[1];
-  __device__ inline void load(const uint8_t* p) { w[0] = *gptr<uint32_t>(p); }
+  template <bool NT = false>
+  __device__ inline void load(const uint8_t* p) { w[0] = ldg<NT, uint32_t>(p); }
 };
 template <>
 struct PBuf<8> {
   uint32_t w[2];
+  template <bool NT = false>
   __device__ inline void load(const uint8_t* p) {
-    u32x2 v = *gptr<u32x2>(p);
+    u32x2 v = ldg<NT, u32x2>(p);
     w[0] = v.x;
     w[1] = v.y;
   }
@@ -49,8 +61,9 @@ struct PBuf<8> {
 template <>
 struct PBuf<16> {
   uint32_t w[4];
+  template <bool NT = false>
   __device__ inline void load(const uint8_t* p) {
-    u32x4 v = *gptr<u32x4>(p);
+    u32x4 v = ldg<NT, u32x4>(p);
     w[0] = v.x;
     w[1] = v.y;
     w[2] = v.z;

@@ -11,8 +11,8 @@
 // Two kernel families share the tile layout and the in-register decoding:
 //  * decode (few rows per expert): a block is 4 wavefronts on the same 32-row
 //    token tile and the same 64 weight rows, splitting K; weights stream from
-//    HBM straight into registers (16-byte loads per lane, 1 KiB per wave and
-//    tile), are decoded to fp16 and fed to v_mfma_f32_32x32x16_f16 with the
+//    HBM straight into registers (non-temporal 16-byte loads per lane, 1 KiB
+//    per wave and tile), are decoded to fp16 and fed to v_mfma_f32_32x32x16_f16 with the
 //    token rows padded to 32. The 4 partial sums meet in LDS.
 //  * prefill (many rows per expert): a block owns 128 token rows and 256
 //    weight rows; the token tile is staged in LDS (double-buffered, shared by
@@ -194,35 +194,56 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
   const bool arow = n < t.mcount;
   const f16* ap = a.a + (size_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN;
 
-  auto load = [&](int kt, BTile<F>& b, f16x8* av) {
-    b.w0 = *gptr<u32x4>(c0 + (size_t)kt * 1024);
-    b.w1 = *gptr<u32x4>(c1 + (size_t)kt * 1024);
+  struct AFrag {
+    f16x8 v[F::STEPS];
+  };
+  // tiles of this wavefront: kt_i = kb + wave + 4 i, i < nt. Prefetches past
+  // the last tile re-read a valid tile (result unused) so that the loop body
+  // has no conditional loads and exact wait counts.
+  const int nt = ke > kb + wave ? (ke - kb - wave + 3) / 4 : 0;
+  auto tile_of = [&](int i) { return min(kb + wave + 4 * i, KTn - 1); };
+  auto load_b = [&](int i, BTile<F>& b) {
+    const int kt = tile_of(i);
+    b.w0 = ldg<true, u32x4>(c0 + (size_t)kt * 1024);
+    b.w1 = ldg<true, u32x4>(c1 + (size_t)kt * 1024);
     const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
-    b.q0.load(p0 + (size_t)ei * 32 * F::EB);
-    b.q1.load(p1 + (size_t)ei * 32 * F::EB);
+    b.q0.template load<true>(p0 + (size_t)ei * 32 * F::EB);
+    b.q1.template load<true>(p1 + (size_t)ei * 32 * F::EB);
+  };
+  auto load_a = [&](int i, AFrag& af) {
+    const int kt = tile_of(i);
 #pragma unroll
-    for (int s = 0; s < F::STEPS; ++s)
-      av[s] = arow ? *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s) : f16x8{};
+    for (int s = 0; s < F::STEPS; ++s) {
+      // every lane loads (rows past the tile read the tile's first row) and
+      // padding lanes select zero: no divergent branch around the load
+      const f16x8 v = *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s);
+      af.v[s] = arow ? v : f16x8{};
+    }
   };
   f32x16 acc0 = {}, acc1 = {};
-  auto compute = [&](const BTile<F>& b, const f16x8* av) {
+  auto compute = [&](const BTile<F>& b, const AFrag& af) {
 #pragma unroll
     for (int s = 0; s < F::STEPS; ++s) {
       const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s, dk);
       const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s, dk);
-      acc0 = mfma32(av[s], b0, acc0);
-      acc1 = mfma32(av[s], b1, acc1);
+      acc0 = mfma32(af.v[s], b0, acc0);
+      acc1 = mfma32(af.v[s], b1, acc1);
     }
   };
-  // two K tiles in flight per wavefront
-  for (int kt = kb + wave; kt < ke; kt += 8) {
-    BTile<F> b0, b1;
-    f16x8 av0[F::STEPS], av1[F::STEPS];
-    const bool two = kt + 4 < ke;
-    load(kt, b0, av0);
-    if (two) load(kt + 4, b1, av1);
-    compute(b0, av0);
-    if (two) compute(b1, av1);
+  // weights two tiles ahead (three slots), token fragments one tile ahead
+  BTile<F> B0, B1, B2;
+  AFrag A0, A1;
+  load_b(0, B0);
+  load_a(0, A0);
+  load_b(1, B1);
+  for (int i = 0; i < nt; i += 6) {
+    // slot pattern repeats every 6 tiles (lcm of 3 weight and 2 token slots)
+    load_a(i + 1, A1); load_b(i + 2, B2); if (i < nt) compute(B0, A0);
+    load_a(i + 2, A0); load_b(i + 3, B0); if (i + 1 < nt) compute(B1, A1);
+    load_a(i + 3, A1); load_b(i + 4, B1); if (i + 2 < nt) compute(B2, A0);
+    load_a(i + 4, A0); load_b(i + 5, B2); if (i + 3 < nt) compute(B0, A1);
+    load_a(i + 5, A1); load_b(i + 6, B0); if (i + 4 < nt) compute(B1, A0);
+    load_a(i + 6, A0); load_b(i + 7, B1); if (i + 5 < nt) compute(B2, A1);
   }
 
   // reduce the 4 wavefronts' partial sums: red[w][m][r][lane]
@@ -259,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
 // Prefill family
 // ===========================================================================
 constexpr int kBM = 128;
+constexpr bool kPrefillNT = true;  // weight tiles: non-temporal loads
 constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 
 __device__ inline int xcd_remap(int b, int nblk) {
@@ -322,11 +344,11 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
     for (int i = 0; i < CPT; ++i) *reinterpret_cast<f16x8*>(buf + adst[i]) = ar.v[i];
   };
   auto load_b = [&](int kt, BTile<F>& b) {
-    b.w0 = *gptr<u32x4>(c0 + (size_t)kt * 1024);
-    b.w1 = *gptr<u32x4>(c1 + (size_t)kt * 1024);
+    b.w0 = ldg<kPrefillNT, u32x4>(c0 + (size_t)kt * 1024);
+    b.w1 = ldg<kPrefillNT, u32x4>(c1 + (size_t)kt * 1024);
     const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
-    b.q0.load(p0 + (size_t)ei * 32 * F::EB);
-    b.q1.load(p1 + (size_t)ei * 32 * F::EB);
+    b.q0.template load<kPrefillNT>(p0 + (size_t)ei * 32 * F::EB);
+    b.q1.template load<kPrefillNT>(p1 + (size_t)ei * 32 * F::EB);
   };
   f32x16 acc[kMT][2];
 #pragma unroll

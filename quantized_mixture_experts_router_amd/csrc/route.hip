@@ -29,6 +29,13 @@ constexpr int kInvalid = 0x7fffffff;
 // blocks (small batches spread the hidden dimension over every thread), but
 // enough that re-reading the router weights per block stays under ~256 MB of
 // L2 traffic (large E*H), and at most 8 (kTG * expert groups <= 256 threads).
+// hidden-dimension slices per (token group, expert group): a power of two
+__host__ __device__ inline int route_slices(int TG, int EG) {
+  int ks = 1;
+  while (2 * ks * TG * EG <= 256) ks *= 2;
+  return ks;
+}
+
 __host__ __device__ inline int route_tgroups(int T, int H, int E) {
   int tg = 1;
   while (tg < 8 && (T + 2 * tg - 1) / (2 * tg) > 1024) tg *= 2;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int kTB = kTG * kTM;
   const int t0 = blockIdx.x * kTB;
   const int EG = (E + kEM - 1) / kEM;             // expert groups
-  const int KS = max(1, kThreads / (kTG * EG));   // hidden-dimension slices
+  const int KS = route_slices(kTG, EG);           // hidden-dimension slices
   const int active = KS * kTG * EG;               // threads with work (<= 256)
   // lane -> (slice, token group, expert group); slice varies fastest
   const int ks = tid % KS;
@@ -117,28 +124,39 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     }
   }
 
-  // reduce the hidden slices: partial[slot][ks] with slot = (tg, eg, i, j)
-  double* part = smem;
-  if (KS > 1 && on) {
+  // reduce the hidden slices. Slices of one (token group, expert group) are
+  // adjacent lanes (KS is a power of two): butterfly within the wavefront,
+  // then across wavefronts through LDS when KS > 64.
+  const int KW = KS < 64 ? KS : 64;  // slices per wavefront
+  if (KS > 1) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kEM; ++j)
-        part[(((size_t)(eg * kTG + tg) * kTM + i) * kEM + j) * KS + ks] = acc[i][j];
+        for (int off = 1; off < KW; off <<= 1) acc[i][j] += __shfl_xor(acc[i][j], off);
+  }
+  const int NW = KS / KW;  // wavefronts per (token group, expert group)
+  double* part = smem;     // [group][i][j][NW]
+  if (NW > 1 && on && (ks % KW) == 0) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kEM; ++j)
+        part[(((size_t)(eg * kTG + tg) * kTM + i) * kEM + j) * NW + ks / KW] = acc[i][j];
   }
   __syncthreads();
-  double* lg = smem + (KS > 1 ? (size_t)KS * kTG * EG * kTM * kEM : 0);  // [kTB][E+1]
-  if (KS > 1) {
+  double* lg = smem + (NW > 1 ? (size_t)NW * kTG * EG * kTM * kEM : 0);  // [kTB][E+1]
+  if (NW > 1) {
     const int nslots = kTG * EG * kTM * kEM;
     for (int slot = tid; slot < nslots; slot += kThreads) {
-      double s = 0.0;
-      for (int q = 0; q < KS; ++q) s += part[(size_t)slot * KS + q];
+      double v = 0.0;
+      for (int q = 0; q < NW; ++q) v += part[(size_t)slot * NW + q];
       const int j = slot % kEM, i = (slot / kEM) % kTM, g = slot / (kEM * kTM);
       const int tgi = g % kTG, egi = g / kTG;
       const int e = egi * kEM + j, tt = tgi * kTM + i;
-      if (e < E) lg[tt * (E + 1) + e] = s;
+      if (e < E) lg[tt * (E + 1) + e] = v;
     }
-  } else if (on) {
+  } else if (on && ks == 0) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -219,8 +237,9 @@ hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b,
   if (T == 0) return hipSuccess;
   const int TG = route_tgroups(T, H, E), TB = TG * kTM;
   const int EG = (E + kEM - 1) / kEM;
-  const int KS = kThreads / (TG * EG) > 1 ? kThreads / (TG * EG) : 1;
-  size_t part = KS > 1 ? (size_t)KS * TG * EG * kTM * kEM : 0;
+  const int KS = route_slices(TG, EG);
+  const int NW = KS > 64 ? KS / 64 : 1;
+  size_t part = NW > 1 ? (size_t)NW * TG * EG * kTM * kEM : 0;
   size_t smem = sizeof(double) * (part + (size_t)TB * (E + 1));
   dim3 grid((T + TB - 1) / TB);
   hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), smem, s, x, xdt, Wr, b, T, H, E, k, ids, w,
