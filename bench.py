@@ -1,13 +1,16 @@
 """Benchmark of the quantized MoE layer on one MI355X.
 
 One step = one pass of the whole layer (router + top-k/softmax, permutation,
-expert-input gather, gate/up + SwiGLU, down projection, weighted combine) over
-one batch of synthetic tokens already resident in HBM. Default workload: the
-Mixtral-8x7B-shaped layer (hidden 4096, 8 experts, top-2, intermediate 14336,
-4-bit group-32 asymmetric weights with fp16 scale+min, bf16 activations) at
-prefill, 2048 tokens. Decode batches of 1/8/32 tokens of the same layer are
-measured alongside (weight GB/s against HBM peak), each repetition preceded by
-a 1 GiB buffer write so the 256 MB last-level cache holds no weights.
+expert-input gather (+ int8 quantisation), gate/up + SwiGLU, down projection,
+weighted combine) over one batch of synthetic tokens already resident in HBM.
+
+Default workload: the Mixtral-8x7B-shaped layer (hidden 4096, 8 experts, top-2,
+intermediate 14336, 4-bit group-32 asymmetric weights with fp16 scale+min,
+bf16 activations) at prefill, 2048 tokens. `--workload` selects one of the
+other synthetic layers (fine_e2m1, hotcold, w4a8, tiny). Decode batches of the
+same layer are measured alongside (weight GB/s against HBM peak), each
+repetition preceded by a 1 GiB buffer write so that the 256 MB last-level cache
+holds no weights.
 
 Prints one JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
@@ -29,6 +32,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["quantized_mixture_experts_router_amd/csrc/gemm.hip",
                   "quantized_mixture_experts_router_amd/csrc/deq.h",
                   "quantized_mixture_experts_router_amd/csrc/common.h"]
+FMT_NAMES = {1: "asym", 2: "e2m1"}
 
 
 def kernel_source_hash():
@@ -58,13 +62,30 @@ def read_traffic(name):
         return None
 
 
-def packed_payload_bytes(cfg, e):
-    """Algorithmic weight bytes of expert e: codes + scales (+ mins)."""
+def payload_bytes(cfg, e):
+    """Algorithmic weight bytes of expert e (codes + scales (+ mins)):
+    (all three matrices, gate+up only)."""
     import synth
     fmt, bits, group = synth.expert_format(cfg, e)
     psz = 4 if fmt == synth.FMT_ASYM else 2
-    w = 3 * cfg.H * cfg.I
-    return w * bits // 8 + (w // group) * psz, (2 * cfg.H * cfg.I * bits // 8 + (2 * cfg.H * cfg.I // group) * psz)
+    w3, w2 = 3 * cfg.H * cfg.I, 2 * cfg.H * cfg.I
+    return w3 * bits // 8 + (w3 // group) * psz, w2 * bits // 8 + (w2 // group) * psz
+
+
+def kernel_names(cfg):
+    import synth
+    fmts = sorted({synth.expert_format(cfg, e) for e in range(cfg.E)})
+    return [f"ffn_prefill_kernel<moeq::Fmt<{f}, {b}, {g}>, true>" for f, b, g in fmts]
+
+
+def weights_desc(cfg):
+    f, b, g = cfg.fmt
+    s = f"{FMT_NAMES[f]} {b}-bit, group {g}, fp16 scale" + ("+min" if f == 1 else "")
+    if cfg.cold_fmt is not None:
+        f2, b2, g2 = cfg.cold_fmt
+        s = (f"{cfg.n_hot} hot experts {s}; the others {FMT_NAMES[f2]} {b2}-bit, group {g2}, "
+             f"fp16 scale+min; Zipf-skewed router bias")
+    return s
 
 
 def main():
@@ -72,9 +93,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["mixtral", "fine_e2m1", "hotcold", "w4a8", "tiny"])
+    ap.add_argument("--tokens", type=int, default=None, help="prefill tokens (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--decode-reps", type=int, default=50)
+    ap.add_argument("--decode-warmup", type=int, default=10)
     ap.add_argument("--decode-only", action="store_true",
                     help="profiling aid: run only the decode repetitions")
     ap.add_argument("--cpu-tokens", type=int, default=16)
@@ -84,7 +109,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(multi-GPU sharding is designed, not built)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -92,7 +117,7 @@ def main():
 
     import synth
     import quantized_mixture_experts_router_amd as moeq
-    from layer_cases import Workload, rel_l2_rows
+    from layer_cases import Workload, rel_l2_rows, tolerance
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -111,31 +136,32 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
     # ------------------------------------------------------------------ prefill
-    cfg = synth.get_config("mixtral")
-    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    log(f"[bench] building workload {cfg.name} T={T} H={H} I={I} E={E} k={k}")
+    cfg = synth.get_config(args.workload, T=args.tokens)
+    T, H, I, E, k, act = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act
+    log(f"[bench] building workload {cfg.name} T={T} H={H} I={I} E={E} k={k} act={act}")
     t0 = time.time()
     wl = Workload(cfg, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] packed {wl.packed.nbytes() / 1e6:.1f} MB of experts in {time.time() - t0:.1f}s")
 
-    ws = moeq.workspace(T, H, I, E, k, 0, dev)
-    out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = moeq.workspace(T, H, I, E, k, act, dev)
     Y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
 
+    # every launch goes to torch's current stream, which the events time
     def step(evs=None):
         ids_, w_ = moeq.route(wl.x, wl.Wr, wl.b, k)
         counts, offsets, perm, inv, _ = moeq.permute(ids_, E, ws)
-        moeq.ffn_gather(wl.x, perm, k, wl.packed, 0, ws)
+        moeq.ffn_gather(wl.x, perm, k, wl.packed, act, ws)
         if evs is not None:
             evs[0].record()
-        moeq.ffn_gate_up(T, wl.packed, offsets, k, 0, ws)
+        moeq.ffn_gate_up(T, wl.packed, offsets, k, act, ws)
         if evs is not None:
             evs[1].record()
-        moeq.ffn_down(T, wl.packed, offsets, k, 0, Y, ws)
+        moeq.ffn_down(T, wl.packed, offsets, k, act, Y, ws)
         if evs is not None:
             evs[2].record()
         o = moeq.combine(Y, w_, inv, T, k)
@@ -146,7 +172,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[event() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -165,7 +191,7 @@ def main():
         f"down {dn_ms:.3f} ms ({dn_tflops:.0f} TFLOP/s)")
 
     # the same layer through the one-shot entry point (must agree bit for bit)
-    out1, ids1, w1 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, k, ws=ws)
+    out1, ids1, w1 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, k, act=act, ws=ws)
     torch.cuda.synchronize()
     same = bool(torch.equal(out1, o))
 
@@ -182,14 +208,16 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": "Mixtral-8x7B-shaped quantized MoE layer, prefill",
+        "config": {"workload": f"{cfg.name} quantized MoE layer, prefill",
                    "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-                   "weights": "asym 4-bit, group 32, fp16 scale+min", "activations": "bf16",
+                   "weights": weights_desc(cfg), "activations": cfg.x_dtype,
+                   "expert_inputs": "per-token int8 (x and h)" if act == 2 else
+                                    ("per-token int8 (x)" if act == 1 else "fp16"),
                    "router": "fp32 weights, fp64 accumulation", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "ffn_prefill_kernel<true> (gate/up + SwiGLU)",
+        "roofline": {"bound": "mfma", "kernel": " + ".join(kernel_names(cfg)) + " (gate/up + SwiGLU)",
                      "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_FP16_TFLOPS,
-                     "traffic": read_traffic("ffn_prefill_gate_up_mixtral_T2048_traffic.txt"),
+                     "traffic": read_traffic(f"ffn_prefill_gate_up_{cfg.name}_T{T}_traffic.txt"),
                      "avg_launch_ms": gu_ms, "flop_per_launch": flop_gu},
         "phases": {"gate_up_ms": gu_ms, "down_ms": dn_ms, "down_tflops": dn_tflops,
                    "layer_tflops": flop_layer / (ms_step * 1e-3) / 1e12},
@@ -197,46 +225,53 @@ def main():
     }
 
     # ------------------------------------------------------------------ decode
-    if not args.no_decode:
+    if not args.no_decode and cfg.decode_T:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dec = []
         for Td in cfg.decode_T:
             x_d = wl.x[:Td].contiguous()
-            ws_d = moeq.workspace(Td, H, I, E, k, 0, dev)
+            ws_d = moeq.workspace(Td, H, I, E, k, act, dev)
             Yd = torch.empty((Td * k, H), dtype=torch.float32, device=dev)
-            reps = args.decode_reps
-            lay, gu = [], []
-            for r in range(reps + 3):
+            lay, gu, dn = [], [], []
+            for r in range(args.decode_warmup + args.decode_reps):
                 flush.zero_()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = event(), event()
                 e0.record()
-                moeq.layer_forward(x_d, wl.Wr, wl.b, wl.packed, k, ws=ws_d)
+                moeq.layer_forward(x_d, wl.Wr, wl.b, wl.packed, k, act=act, ws=ws_d)
                 e1.record()
                 flush.zero_()
                 ids_d, w_d = moeq.route(x_d, wl.Wr, wl.b, k)
                 counts_d, off_d, perm_d, inv_d, _ = moeq.permute(ids_d, E, ws_d)
-                moeq.ffn_gather(x_d, perm_d, k, wl.packed, 0, ws_d)
-                g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                moeq.ffn_gather(x_d, perm_d, k, wl.packed, act, ws_d)
+                g0, g1, g2 = event(), event(), event()
                 g0.record()
-                moeq.ffn_gate_up(Td, wl.packed, off_d, k, 0, ws_d)
+                moeq.ffn_gate_up(Td, wl.packed, off_d, k, act, ws_d)
                 g1.record()
-                moeq.ffn_down(Td, wl.packed, off_d, k, 0, Yd, ws_d)
+                moeq.ffn_down(Td, wl.packed, off_d, k, act, Yd, ws_d)
+                g2.record()
                 torch.cuda.synchronize()
-                if r >= 3:
+                if r >= args.decode_warmup:
                     lay.append(e0.elapsed_time(e1))
                     gu.append(g0.elapsed_time(g1))
+                    dn.append(g1.elapsed_time(g2))
             touched = np.nonzero(counts_d.cpu().numpy())[0]
-            tot_b = sum(packed_payload_bytes(cfg, int(e))[0] for e in touched)
-            gu_b = sum(packed_payload_bytes(cfg, int(e))[1] for e in touched)
-            lay_ms, gu_ms_d = float(np.median(lay)), float(np.median(gu))
+            tot_b = sum(payload_bytes(cfg, int(e))[0] for e in touched)
+            gu_b = sum(payload_bytes(cfg, int(e))[1] for e in touched)
+            lay_ms, gu_ms_d, dn_ms_d = (float(np.median(v)) for v in (lay, gu, dn))
+            ffn_ms = gu_ms_d + dn_ms_d
             d = {"tokens": Td, "experts_touched": int(len(touched)),
-                 "layer_ms": lay_ms, "layer_tokens_per_s": Td / (lay_ms * 1e-3),
+                 "layer_ms": lay_ms,
+                 "layer_ms_p10_p90": [float(np.percentile(lay, 10)), float(np.percentile(lay, 90))],
+                 "layer_tokens_per_s": Td / (lay_ms * 1e-3),
                  "layer_weight_GBps": tot_b / (lay_ms * 1e-3) / 1e9,
+                 "ffn_ms": ffn_ms, "ffn_weight_GBps": tot_b / (ffn_ms * 1e-3) / 1e9,
+                 "ffn_frac_hbm": tot_b / (ffn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                  "gate_up_ms": gu_ms_d, "gate_up_weight_GBps": gu_b / (gu_ms_d * 1e-3) / 1e9,
                  "gate_up_frac_hbm": gu_b / (gu_ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS,
                  "weight_bytes_touched": tot_b}
             log(f"[bench] decode T={Td}: layer {lay_ms * 1e3:.1f} us ({d['layer_weight_GBps']:.0f} GB/s), "
-                f"gate_up {gu_ms_d * 1e3:.1f} us ({d['gate_up_weight_GBps']:.0f} GB/s)")
+                f"gate_up {gu_ms_d * 1e3:.1f} us ({d['gate_up_weight_GBps']:.0f} GB/s), "
+                f"down {dn_ms_d * 1e3:.1f} us, ffn {d['ffn_weight_GBps']:.0f} GB/s")
             dec.append(d)
         result["decode"] = dec
         del flush
@@ -249,14 +284,14 @@ def main():
             blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         except Exception:
             blas_threads = 1
-        n = args.cpu_tokens
-        toks = list(range(n))
+        n = min(args.cpu_tokens, T)
         x_s = wl.x_np[:n]
+        b_np = wl.b_np if cfg.zipf_alpha > 0 else None
         log(f"[bench] cpu oracle on the first {n} tokens ...")
-        oracle.moe_layer(x_s[:1], cfg.x_dtype, wl.Wr_np, None, lambda e: wl.expert_uncached(e), E, k,
-                         tokens=[0])  # warm-up on a 1-token slice (decodes its 2 experts)
+        oracle.moe_layer(x_s[:1], cfg.x_dtype, wl.Wr_np, b_np, wl.expert_uncached, E, k, act=act,
+                         tokens=[0])  # warm-up on a 1-token slice
         tc0 = time.perf_counter()
-        ref = oracle.moe_layer(x_s, cfg.x_dtype, wl.Wr_np, None, lambda e: wl.expert_uncached(e), E, k)
+        ref = oracle.moe_layer(x_s, cfg.x_dtype, wl.Wr_np, b_np, wl.expert_uncached, E, k, act=act)
         tc = time.perf_counter() - tc0
         got = o[:n].cpu().numpy()
         ok = ~ref["flagged"]
@@ -264,11 +299,11 @@ def main():
         ids_ok = bool(np.array_equal(ids_.cpu().numpy()[:n][ok], ref["ids"][ok]))
         result["cpu_baseline"] = {
             "value": n / tc, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"first {n} of the {T} prefill tokens (all their experts decoded); "
+            "sample": f"first {n} of the {T} prefill tokens (every expert they route to decoded); "
                       f"fp64 NumPy, {tc:.1f} s; BLAS threads {blas_threads}, block decoding single-threaded",
         }
         result["parity"] = {"tokens_checked": n, "max_row_rel_l2": float(err.max()),
-                            "ids_bit_exact": ids_ok, "tolerance": 2e-3}
+                            "ids_bit_exact": ids_ok, "tolerance": tolerance(cfg)}
         log(f"[bench] oracle {n / tc:.3f} tokens/s; parity max row rel-L2 {err.max():.2e}, ids exact {ids_ok}")
 
     print(json.dumps(result))
