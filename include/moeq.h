@@ -178,7 +178,8 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
  * operations with fp32 accumulation; with int8 activations the int8 codes
  * enter the matrix cores exactly and the per-row scales are applied in fp32.
  * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes, 256-aligned.
- * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I. */
+ * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I;
+ * x 16-byte aligned. */
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
                              uint32_t fmt_mask, const int32_t* offsets, const int32_t* perm_token,
                              int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,

@@ -235,6 +235,7 @@ moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_toke
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm_token) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return MOE_ERR_ALIGNMENT;
   return run_gather(x, xdt, perm_token, T, H, k, aq, L, ws, (hipStream_t)stream);
 }
 

@@ -43,44 +43,138 @@ __device__ inline float quant_i8(float v, float s) {
   return fminf(fmaxf(q, -127.f), 127.f);
 }
 
-// one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes
+// 8 consecutive elements of a bf16 or fp32 row as fp32 (16-/32-byte loads)
+__device__ inline void load8(const void* x, int dt, size_t idx, float* v) {
+  if (dt == MOE_BF16) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>((const uint16_t*)x + idx);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(u[q] << 16);
+      v[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>((const float*)x + idx);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = a[q];
+      v[4 + q] = b[q];
+    }
+  }
+}
+
+__device__ inline void store8_f16(f16* dst, const float* v) {
+  f16x8 h;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) h[q] = (f16)v[q];
+  *reinterpret_cast<f16x8*>(dst) = h;
+}
+
+// one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes;
+// each thread moves 8 columns at a time (H % 8 == 0, x 16-byte aligned)
 __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restrict__ x, int dt,
                                                           const int32_t* __restrict__ perm, int H,
                                                           int quant, f16* __restrict__ a16,
                                                           float* __restrict__ ascale) {
+  __shared__ float s_red[kThreads / 64];
   const int r = blockIdx.x;
   const int t = perm[r];
   const size_t base = (size_t)t * H;
   f16* dst = a16 + (size_t)r * H;
   if (quant) {
-    float amax = row_absmax(x, dt, base, H);
-    float s = __fdiv_rn(amax, 127.f);
-    for (int c = threadIdx.x; c < H; c += kThreads) dst[c] = (f16)quant_i8(load_val(x, dt, base + c), s);
+    float m = 0.f;
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
+      float v[8];
+      load8(x, dt, base + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float s = __fdiv_rn(amax, 127.f);
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
+      float v[8];
+      load8(x, dt, base + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
+      store8_f16(dst + c, v);
+    }
     if (threadIdx.x == 0) ascale[r] = s;
   } else {
-    for (int c = threadIdx.x; c < H; c += kThreads) dst[c] = (f16)load_val(x, dt, base + c);
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
+      float v[8];
+      load8(x, dt, base + c, v);
+      store8_f16(dst + c, v);
+    }
   }
 }
 
+// Block-wide absmax of a row, 8 columns per thread at a time.
+__device__ inline float row_absmax8(const void* x, int dt, size_t base, int cols) {
+  __shared__ float s_red[kThreads / 64];
+  float m = 0.f;
+  for (int c = 8 * threadIdx.x; c < cols; c += 8 * kThreads) {
+    float v[8];
+    load8(x, dt, base + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+// h (fp32 [R, I], I % 8 == 0) -> int8 codes held as fp16, per-row scales
 __global__ __launch_bounds__(kThreads) void quant_rows_f32_kernel(const float* __restrict__ h,
                                                                 int I, f16* __restrict__ h16,
                                                                 float* __restrict__ hscale) {
   const int r = blockIdx.x;
   const size_t base = (size_t)r * I;
-  float amax = row_absmax(h, MOE_F32, base, I);
-  float s = __fdiv_rn(amax, 127.f);
-  for (int c = threadIdx.x; c < I; c += kThreads) h16[base + c] = (f16)quant_i8(h[base + c], s);
+  const float s = __fdiv_rn(row_absmax8(h, MOE_F32, base, I), 127.f);
+  for (int c = 8 * threadIdx.x; c < I; c += 8 * kThreads) {
+    float v[8];
+    load8(h, MOE_F32, base + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
+    store8_f16(h16 + base + c, v);
+  }
   if (threadIdx.x == 0) hscale[r] = s;
 }
 
+// standalone per-row int8 quantisation; vec (cols % 8 == 0, v 16-byte and q
+// 8-byte aligned) moves 8 columns per load, otherwise one element at a time
 __global__ __launch_bounds__(kThreads) void act_quant_i8_kernel(const void* __restrict__ v, int dt,
-                                                              int cols, int8_t* __restrict__ q,
+                                                              int cols, int vec,
+                                                              int8_t* __restrict__ q,
                                                               float* __restrict__ sc) {
   const int r = blockIdx.x;
   const size_t base = (size_t)r * cols;
-  float amax = row_absmax(v, dt, base, cols);
-  float s = __fdiv_rn(amax, 127.f);
-  for (int c = threadIdx.x; c < cols; c += kThreads) q[base + c] = (int8_t)quant_i8(load_val(v, dt, base + c), s);
+  float amax;
+  if (vec) {
+    amax = row_absmax8(v, dt, base, cols);
+  } else {
+    amax = row_absmax(v, dt, base, cols);
+  }
+  const float s = __fdiv_rn(amax, 127.f);
+  if (vec) {
+    for (int c = 8 * threadIdx.x; c < cols; c += 8 * kThreads) {
+      float f[8];
+      load8(v, dt, base + c, f);
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        w[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)quant_i8(f[j], s)) << (8 * (j & 3));
+      *reinterpret_cast<u32x2*>(q + base + c) = u32x2{w[0], w[1]};
+    }
+  } else {
+    for (int c = threadIdx.x; c < cols; c += kThreads)
+      q[base + c] = (int8_t)quant_i8(load_val(v, dt, base + c), s);
+  }
   if (threadIdx.x == 0) sc[r] = s;
 }
 
@@ -161,7 +255,8 @@ hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* 
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
                                hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(act_quant_i8_kernel, dim3(rows), dim3(kThreads), 0, s, v, dt, cols, q, sc);
+  const int vec = cols % 8 == 0 && ((uintptr_t)v % 16) == 0 && ((uintptr_t)q % 8) == 0;
+  hipLaunchKernelGGL(act_quant_i8_kernel, dim3(rows), dim3(kThreads), 0, s, v, dt, cols, vec, q, sc);
   return hipGetLastError();
 }
 

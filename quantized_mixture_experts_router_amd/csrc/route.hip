@@ -46,27 +46,76 @@ __host__ __device__ inline int route_tgroups(int T, int H, int E) {
   return tg;
 }
 
-__device__ inline void load_x8(const void* x, int xdt, size_t idx, double* o) {
-  if (xdt == MOE_BF16) {
-    u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)x + idx);
+// Raw operands of one 8-column slice: x of kTM tokens (bf16 pairs or fp32)
+// and Wr of kEM experts. Loaded for a whole batch of slices before any use,
+// so that a thread waits for memory once per batch.
+template <int XDT>
+struct Slice {
+  static constexpr int XW = XDT == MOE_BF16 ? 4 : 8;  // 32-bit words of x per token
+  uint32_t x[kTM][XW];
+  f32x4 w[kEM][2];
+};
+
+template <int XDT>
+__device__ inline void load_slice(const void* x, const float* Wr, const int* trow, const int* erow,
+                                  int H, int h, Slice<XDT>& o) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = (double)__uint_as_float(v[i] << 16);
-      o[2 * i + 1] = (double)__uint_as_float(v[i] & 0xffff0000u);
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>((const float*)x + idx);
-    f32x4 a = p[0], b = p[1];
+  for (int i = 0; i < kTM; ++i) {
+    if (XDT == MOE_BF16) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)x + (size_t)trow[i] * H + h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[i] = (double)a[i];
-      o[4 + i] = (double)b[i];
+      for (int q = 0; q < 4; ++q) o.x[i][q] = v[q];
+    } else {
+      const u32x4* p = reinterpret_cast<const u32x4*>((const float*)x + (size_t)trow[i] * H + h);
+      const u32x4 a = p[0], b = p[1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o.x[i][q] = a[q];
+        o.x[i][4 + q] = b[q];
+      }
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kEM; ++j) {
+    const f32x4* wp = reinterpret_cast<const f32x4*>(Wr + (size_t)erow[j] * H + h);
+    o.w[j][0] = wp[0];
+    o.w[j][1] = wp[1];
   }
 }
 
+template <int XDT>
+__device__ inline void fma_slice(const Slice<XDT>& o, double (&acc)[kTM][kEM]) {
+  double xv[kTM][8];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (XDT == MOE_BF16) {
+        xv[i][2 * q] = (double)__uint_as_float(o.x[i][q] << 16);
+        xv[i][2 * q + 1] = (double)__uint_as_float(o.x[i][q] & 0xffff0000u);
+      } else {
+        xv[i][q] = (double)__uint_as_float(o.x[i][q]);
+        xv[i][4 + q] = (double)__uint_as_float(o.x[i][4 + q]);
+      }
+    }
+#pragma unroll
+  for (int j = 0; j < kEM; ++j) {
+    double wv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wv[q] = (double)o.w[j][0][q];
+      wv[4 + q] = (double)o.w[j][1][q];
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[i][j] = fma(xv[i][q], wv[q], acc[i][j]);
+  }
+}
+
+template <int XDT>
 __global__ __launch_bounds__(kThreads) void route_kernel(
-    const void* __restrict__ x, int xdt, const float* __restrict__ Wr,
+    const void* __restrict__ x, const float* __restrict__ Wr,
     const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, float* __restrict__ logits_out, uint32_t* __restrict__ flags) {
   extern __shared__ double smem[];  // [KS*TG*EG*kTM*kEM partials][kTB*(E+1) logits]
@@ -101,26 +150,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     int erow[kEM];
 #pragma unroll
     for (int j = 0; j < kEM; ++j) erow[j] = min(eg * kEM + j, E - 1);
-#pragma unroll 4
-    for (int h = 8 * ks; h < H; h += 8 * KS) {
-      double xv[kTM][8];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) load_x8(x, xdt, (size_t)trow[i] * H + h, xv[i]);
-#pragma unroll
-      for (int j = 0; j < kEM; ++j) {
-        const f32x4* wp = reinterpret_cast<const f32x4*>(Wr + (size_t)erow[j] * H + h);
-        f32x4 wa = wp[0], wb = wp[1];
-        double wv[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          wv[q] = (double)wa[q];
-          wv[4 + q] = (double)wb[q];
-        }
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc[i][j] = fma(xv[i][q], wv[q], acc[i][j]);
-      }
+    // slices h = 8 ks + 8 KS i, i < ns, in pairs whose loads are all issued
+    // before either slice is used; an odd last slice on its own
+    const int ns = 8 * ks < H ? (H - 8 * ks + 8 * KS - 1) / (8 * KS) : 0;
+    int i = 0;
+    for (; i + 1 < ns; i += 2) {
+      Slice<XDT> s0, s1;
+      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * i, s0);
+      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * (i + 1), s1);
+      __builtin_amdgcn_sched_barrier(0);  // keep every load of the pair ahead of the FMAs
+      fma_slice<XDT>(s0, acc);
+      fma_slice<XDT>(s1, acc);
+    }
+    if (i < ns) {
+      Slice<XDT> s0;
+      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * i, s0);
+      fma_slice<XDT>(s0, acc);
     }
   }
 
@@ -242,8 +287,12 @@ hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b,
   size_t part = NW > 1 ? (size_t)NW * TG * EG * kTM * kEM : 0;
   size_t smem = sizeof(double) * (part + (size_t)TB * (E + 1));
   dim3 grid((T + TB - 1) / TB);
-  hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), smem, s, x, xdt, Wr, b, T, H, E, k, ids, w,
-                     logits, flags);
+  if (xdt == MOE_BF16)
+    hipLaunchKernelGGL(route_kernel<MOE_BF16>, grid, dim3(kThreads), smem, s, x, Wr, b, T, H, E, k,
+                       ids, w, logits, flags);
+  else
+    hipLaunchKernelGGL(route_kernel<MOE_F32>, grid, dim3(kThreads), smem, s, x, Wr, b, T, H, E, k,
+                       ids, w, logits, flags);
   return hipGetLastError();
 }
 

@@ -115,10 +115,11 @@ def test_permute_flags_bad_ids(moeq):
 
 
 # --------------------------------------------------------------------------- int8
+@pytest.mark.parametrize("cols", [1000, 999])  # 8-column vector path / element path
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_act_quant_bit_exact(moeq, dtype):
+def test_act_quant_bit_exact(moeq, dtype, cols):
     rng = np.random.default_rng(5)
-    v = rng.standard_normal((67, 1000)).astype(np.float32)
+    v = rng.standard_normal((67, cols)).astype(np.float32)
     v[3] = 0.0
     v[5, 7] = 37.0
     v[6] *= 1e-30
