@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+# MOEQ_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("MOEQ_LIBRARY") or os.path.join(_HERE, "libmoeq.so")
 
 MOE_OK = 0
 MOE_F32, MOE_BF16 = 0, 1

@@ -279,8 +279,11 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
 // ===========================================================================
 // Prefill family
 // ===========================================================================
+#ifndef MOEQ_PF_NT
+#define MOEQ_PF_NT 1
+#endif
 constexpr int kBM = 128;
-constexpr bool kPrefillNT = true;  // weight tiles: non-temporal loads
+constexpr bool kPrefillNT = MOEQ_PF_NT;  // weight tiles: non-temporal loads
 constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 
 __device__ inline int xcd_remap(int b, int nblk) {
@@ -293,8 +296,17 @@ __device__ inline int xcd_remap(int b, int nblk) {
 
 template <class F, bool GU>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
-  constexpr int STR = F::KT + 8;  // LDS row stride in halves (16-byte pad)
-  __shared__ __attribute__((aligned(16))) f16 lds[2 * kBM * STR];
+  // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
+  // 16-byte chunks of row r stored at chunk ^ (r & 7), so that the 8 lanes of
+  // an MFMA fragment read that hit one bank group read 8 different chunks.
+  constexpr int ROWB = F::KT * 2;
+  constexpr int TILEB = kBM * ROWB;           // 16 KiB (4-bit) or 32 KiB (2-bit)
+  constexpr int CPR = F::KT / 8;              // 16-byte chunks per row
+  constexpr int NI = TILEB / (4 * 64 * 16);   // LDS-DMA instructions per wave and tile
+  // two separate arrays: the compiler can then tell that a DMA into one
+  // buffer does not feed reads of the other, and waits only where needed
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TILEB];
   const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
   Task t;
   if (!find_task<GU>(a, F::ID, kBM, NB, xcd_remap(blockIdx.x, gridDim.x), t)) return;
@@ -319,29 +331,26 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
   const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
 
   const DeqConsts dk = make_deq_consts<F>();
-  // A staging: kBM rows x KT halves in 16-byte chunks; rows past the segment
-  // repeat its last row (their outputs are never stored)
-  constexpr int CPR = F::KT / 8;
-  constexpr int CPT = kBM * CPR / kThreads;
-  const f16* asrc[CPT];
-  int adst[CPT];
+  // Token tile DMA: instruction j of wavefront w fills LDS slots
+  // [(w NI + j) 64, +64) of the buffer, one 16-byte slot per lane. Slot ->
+  // (row, stored chunk) -> logical chunk; rows past the segment repeat its
+  // last row (their outputs are never stored). Offsets are in bytes from
+  // the start of K tile kt of the token matrix.
+  uint32_t doff[NI];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + i * kThreads;
-    const int r = ch / CPR, c = ch % CPR;
-    asrc[i] = a.a + (size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c;
-    adst[i] = r * STR + 8 * c;
+  for (int j = 0; j < NI; ++j) {
+    const int slot = (wave * NI + j) * 64 + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    const int c = pc ^ (r & 7);
+    doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
   }
-  struct ARegs {
-    f16x8 v[CPT];
-  };
-  auto load_a = [&](int kt, ARegs& ar) {
+  auto dma_a = [&](int kt, uint8_t* buf) {
+    const uint8_t* src = (const uint8_t*)a.a + (size_t)kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) ar.v[i] = *gptr<f16x8>(asrc[i] + (size_t)kt * F::KT);
-  };
-  auto store_a = [&](f16* buf, const ARegs& ar) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<f16x8*>(buf + adst[i]) = ar.v[i];
+    for (int j = 0; j < NI; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const MOEQ_GLOBAL void*)(src + doff[j]),
+          (__attribute__((address_space(3))) void*)(buf + (wave * NI + j) * 1024), 16, 0, 0);
   };
   auto load_b = [&](int kt, BTile<F>& b) {
     b.w0 = ldg<kPrefillNT, u32x4>(c0 + (size_t)kt * 1024);
@@ -356,84 +365,82 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
     acc[mi][0] = f32x16{};
     acc[mi][1] = f32x16{};
   }
-  const int aoff = n * STR + kh * F::SPAN;
+  // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
+  // kh*SPAN/8 + s; (mi*32 + n) & 7 == n & 7
+  auto afrag = [&](const uint8_t* buf, int mi, int s) {
+    const int c = (kh * (F::SPAN / 8) + s) ^ (n & 7);
+    return *reinterpret_cast<const f16x8*>(buf + (mi * 32 + n) * ROWB + c * 16);
+  };
 
-  // Pipeline: raw weight codes and token tiles are fetched two K tiles ahead;
-  // inside a tile the codes of MFMA step s+1 are decoded while the MFMAs of
-  // step s run. Two blocks share a CU, so one block's decode and barriers
-  // overlap the other's matrix-core work. Prefetches past the last tile
-  // re-read the last tile (unused) so the loop body stays branch-free and the
-  // wait counters exact.
-  f16* const LB0 = lds;
-  f16* const LB1 = lds + kBM * STR;
+  // Pipeline, one barrier per K tile. At the start of tile kt the wavefront
+  // waits for its own DMA of token tile kt and its weight codes of tile kt
+  // (everything but the 4 weight loads of tile kt+1 issued at the end of
+  // tile kt-1), then the barrier makes every wavefront's DMA visible and
+  // frees the other buffer; the DMA of tile kt+1 goes out, tile kt is
+  // computed (codes of MFMA step s+1 decoded while the MFMAs of step s run),
+  // and the weight codes of tile kt+2 are fetched into the slot just used.
+  // Prefetches past the last tile re-read the last tile (unused).
   BTile<F> R0, R1;  // raw weight codes (tile parity)
-  ARegs A0, A1;     // token tile registers (tile parity)
-  auto mma_jit = [&](const f16* buf, const BTile<F>& raw) {
-    // step s: token fragments of step s+1 are read from LDS and weight codes
-    // of step s+1 decoded while the 2*kMT MFMAs of step s run
+  auto mma_jit = [&](const uint8_t* buf, const BTile<F>& raw) {
     f16x8 av[kMT];
 #pragma unroll
-    for (int mi = 0; mi < kMT; ++mi)
-      av[mi] = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff);
-    f16x8 c0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
-    f16x8 c1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
+    for (int mi = 0; mi < kMT; ++mi) av[mi] = afrag(buf, mi, 0);
+    f16x8 d0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
+    f16x8 d1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
 #pragma unroll
     for (int s = 0; s < F::STEPS; ++s) {
       f16x8 an[kMT];
-      f16x8 n0 = c0, n1 = c1;
+      f16x8 n0 = d0, n1 = d1;
       if (s + 1 < F::STEPS) {
 #pragma unroll
-        for (int mi = 0; mi < kMT; ++mi)
-          an[mi] = *reinterpret_cast<const f16x8*>(buf + mi * 32 * STR + aoff + 8 * (s + 1));
+        for (int mi = 0; mi < kMT; ++mi) an[mi] = afrag(buf, mi, s + 1);
         n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
         n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
       }
       // LDS reads of step s+1 stay above the MFMAs of step s (vector and
       // scalar ALU work may still move across)
       __builtin_amdgcn_sched_barrier(0x0006);
-      if (on) {
+      // (a wavefront with no row tile of its own computes on the clamped
+      // tile and stores nothing: no branch around the matrix-core chain)
 #pragma unroll
-        for (int mi = 0; mi < kMT; ++mi) {
-          acc[mi][0] = mfma32(av[mi], c0, acc[mi][0]);
-          acc[mi][1] = mfma32(av[mi], c1, acc[mi][1]);
-        }
+      for (int mi = 0; mi < kMT; ++mi) {
+        acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
+        acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
       }
       if (s + 1 < F::STEPS) {
 #pragma unroll
         for (int mi = 0; mi < kMT; ++mi) av[mi] = an[mi];
       }
-      c0 = n0;
-      c1 = n1;
+      d0 = n0;
+      d1 = n1;
     }
   };
+  auto tile_start = [&](int kt, uint8_t* next) {
+    // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // past the last tile this re-fills the idle buffer (no branch in the loop)
+    dma_a(min(kt + 1, KTn - 1), next);
+  };
+  dma_a(0, lds0);
   load_b(0, R0);
-  load_a(0, A0);
   load_b(min(1, KTn - 1), R1);
-  load_a(min(1, KTn - 1), A1);
-  store_a(LB0, A0);
-  __syncthreads();
-  auto even_tile = [&](int kt) {  // LDS buffer 0, raw slot 0
-    mma_jit(LB0, R0);
-    const int kn = min(kt + 2, KTn - 1);
-    load_b(kn, R0);
-    load_a(kn, A0);
-    store_a(LB1, A1);
-    __syncthreads();
-  };
-  auto odd_tile = [&](int kt) {  // LDS buffer 1, raw slot 1
-    mma_jit(LB1, R1);
-    const int kn = min(kt + 2, KTn - 1);
-    load_b(kn, R1);
-    load_a(kn, A1);
-    store_a(LB0, A0);
-    __syncthreads();
-  };
   int kt = 0;
   for (; kt + 1 < KTn; kt += 2) {
-    even_tile(kt);
-    odd_tile(kt + 1);
+    tile_start(kt, lds1);
+    mma_jit(lds0, R0);
+    load_b(min(kt + 2, KTn - 1), R0);
+    tile_start(kt + 1, lds0);
+    mma_jit(lds1, R1);
+    load_b(min(kt + 3, KTn - 1), R1);
   }
-  if (kt < KTn) even_tile(kt);
+  if (kt < KTn) {
+    tile_start(kt, lds1);
+    mma_jit(lds0, R0);
+  }
+  // no LDS DMA may still be in flight when the block's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (!on) return;
 #pragma unroll
