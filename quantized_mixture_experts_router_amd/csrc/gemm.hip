@@ -89,7 +89,7 @@ __device__ inline int expert_fid(const moe_packed_expert* experts, int e) {
 // launch mask (their rows would otherwise be left uncomputed).
 template <bool GU>
 __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task& task) {
-  __shared__ int s_wsum[kThreads / 64];
+  __shared__ int s_wsum[16];  // up to 1024 threads
   __shared__ int s_res[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_res[0] = -1;
@@ -280,11 +280,23 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
 // Prefill family
 // ===========================================================================
 #ifndef MOEQ_PF_NT
-#define MOEQ_PF_NT 1
+#define MOEQ_PF_NT 0
+#endif
+#ifndef MOEQ_PF_DEEP
+#define MOEQ_PF_DEEP 1
+#endif
+#ifndef MOEQ_PF_WAVES
+#define MOEQ_PF_WAVES 4
+#endif
+#ifndef MOEQ_PF_PRIO
+#define MOEQ_PF_PRIO 0
 #endif
 constexpr int kBM = 128;
 constexpr bool kPrefillNT = MOEQ_PF_NT;  // weight tiles: non-temporal loads
 constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
+// wavefronts per prefill block: they share one token tile in LDS, each
+// streaming its own 64 weight rows (one block per CU at 8)
+constexpr int kPW = MOEQ_PF_WAVES;
 
 __device__ inline int xcd_remap(int b, int nblk) {
   // blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous
@@ -295,19 +307,26 @@ __device__ inline int xcd_remap(int b, int nblk) {
 }
 
 template <class F, bool GU>
-__global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
+__global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs a) {
   // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
-  // 16-byte chunks of row r stored at chunk ^ (r & 7), so that the 8 lanes of
-  // an MFMA fragment read that hit one bank group read 8 different chunks.
+  // 16-byte chunks of row r stored at chunk ^ swz(r). The LDS serves a 16-byte
+  // read of 16 lanes (16 consecutive rows, one logical chunk) per cycle from
+  // 64 banks; swz makes those 16 reads land on 16 different 4-bank groups.
   constexpr int ROWB = F::KT * 2;
   constexpr int TILEB = kBM * ROWB;           // 16 KiB (4-bit) or 32 KiB (2-bit)
   constexpr int CPR = F::KT / 8;              // 16-byte chunks per row
-  constexpr int NI = TILEB / (4 * 64 * 16);   // LDS-DMA instructions per wave and tile
+  constexpr int NI = TILEB / (kPW * 64 * 16);  // LDS-DMA instructions per wave and tile
   // two separate arrays: the compiler can then tell that a DMA into one
   // buffer does not feed reads of the other, and waits only where needed
+  // 16 KiB tiles (4-bit) get three buffers and a deeper pipeline
+  constexpr bool DEEP = MOEQ_PF_DEEP && TILEB <= 16384;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[TILEB];
-  const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[DEEP ? TILEB : 16];
+  // unit of one wavefront: gate/up output tile j (row tiles 2j, 2j+1), or
+  // the down row-tile pair (2j, 2j+1); a block covers kPW consecutive units
+  const int NU = a.N / (GU ? 32 : 64);
+  const int NB = (NU + kPW - 1) / kPW;
   Task t;
   if (!find_task<GU>(a, F::ID, kBM, NB, xcd_remap(blockIdx.x, gridDim.x), t)) return;
 
@@ -318,13 +337,12 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
   const moe_packed_expert* ex = a.experts + t.e;
   const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
   const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
-  // gate/up: wavefront w owns output tile 4*nt + w = row tiles (2j, 2j+1);
-  // down: wavefront w owns row tiles 8*nt + 2w and 8*nt + 2w + 1.
-  const int rt0 = GU ? 2 * (4 * t.nt + wave) : 8 * t.nt + 2 * wave;
-  const bool on = GU || rt0 < a.N / 32;
-  // a wavefront past the last row tile (down, N % 256 != 0) streams a valid
-  // tile and discards it, so every wavefront runs the same straight-line loop
-  const int rtl = on ? rt0 : a.N / 32 - 2;
+  const int unit = kPW * t.nt + wave;
+  const bool on = unit < NU;
+  // a wavefront past the last unit streams a valid tile and discards it, so
+  // every wavefront runs the same straight-line loop
+  const int rt0 = 2 * unit;
+  const int rtl = 2 * min(unit, NU - 1);
   const uint8_t* c0 = codes + (size_t)rtl * KTn * 1024 + lane * 16;
   const uint8_t* c1 = c0 + (size_t)KTn * 1024;
   const uint8_t* p0 = params + ((size_t)rtl * NE * 32 + n) * F::EB;
@@ -336,12 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
   // (row, stored chunk) -> logical chunk; rows past the segment repeat its
   // last row (their outputs are never stored). Offsets are in bytes from
   // the start of K tile kt of the token matrix.
+  // 128-byte rows: two rows per 64 banks, so rows 2i and 2i+1 share a chunk
+  // pattern and differ in bank half; 256-byte rows fill all banks each.
+  auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
   uint32_t doff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int slot = (wave * NI + j) * 64 + lane;
     const int r = slot / CPR, pc = slot % CPR;
-    const int c = pc ^ (r & 7);
+    const int c = pc ^ swz(r);
     doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
   }
   auto dma_a = [&](int kt, uint8_t* buf) {
@@ -366,9 +387,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
     acc[mi][1] = f32x16{};
   }
   // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
-  // kh*SPAN/8 + s; (mi*32 + n) & 7 == n & 7
+  // kh*SPAN/8 + s; swz(mi*32 + n) == swz(n)
   auto afrag = [&](const uint8_t* buf, int mi, int s) {
-    const int c = (kh * (F::SPAN / 8) + s) ^ (n & 7);
+    const int c = (kh * (F::SPAN / 8) + s) ^ swz(n);
     return *reinterpret_cast<const f16x8*>(buf + (mi * 32 + n) * ROWB + c * 16);
   };
 
@@ -402,11 +423,13 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0x0006);
       // (a wavefront with no row tile of its own computes on the clamped
       // tile and stores nothing: no branch around the matrix-core chain)
+      if (MOEQ_PF_PRIO) __builtin_amdgcn_s_setprio(MOEQ_PF_PRIO);
 #pragma unroll
       for (int mi = 0; mi < kMT; ++mi) {
         acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
         acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
       }
+      if (MOEQ_PF_PRIO) __builtin_amdgcn_s_setprio(0);
       if (s + 1 < F::STEPS) {
 #pragma unroll
         for (int mi = 0; mi < kMT; ++mi) av[mi] = an[mi];
@@ -415,29 +438,62 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
       d1 = n1;
     }
   };
-  auto tile_start = [&](int kt, uint8_t* next) {
-    // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
-    __builtin_amdgcn_s_waitcnt(0x0F74);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // past the last tile this re-fills the idle buffer (no branch in the loop)
-    dma_a(min(kt + 1, KTn - 1), next);
-  };
-  dma_a(0, lds0);
-  load_b(0, R0);
-  load_b(min(1, KTn - 1), R1);
-  int kt = 0;
-  for (; kt + 1 < KTn; kt += 2) {
-    tile_start(kt, lds1);
-    mma_jit(lds0, R0);
-    load_b(min(kt + 2, KTn - 1), R0);
-    tile_start(kt + 1, lds0);
-    mma_jit(lds1, R1);
-    load_b(min(kt + 3, KTn - 1), R1);
-  }
-  if (kt < KTn) {
-    tile_start(kt, lds1);
-    mma_jit(lds0, R0);
+  if constexpr (DEEP) {
+    // Three token buffers, three weight slots: the DMA of token tile kt+2
+    // goes out at the start of tile kt (into the buffer tile kt-1 used) and
+    // the weight codes of tile kt+3 at its end, so both are fetched two full
+    // tiles ahead. At the start of tile kt everything but the last 8 + NI
+    // memory operations (weights kt+1, DMA kt+1, weights kt+2) has landed.
+    BTile<F> R2;
+    constexpr int VM = 8 + NI;
+    auto tile = [&](int kt, uint8_t* cur, uint8_t* next2, BTile<F>& slot) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      dma_a(min(kt + 2, KTn - 1), next2);
+      mma_jit(cur, slot);
+      load_b(min(kt + 3, KTn - 1), slot);
+    };
+    load_b(0, R0);
+    dma_a(0, lds0);
+    load_b(min(1, KTn - 1), R1);
+    dma_a(min(1, KTn - 1), lds1);
+    load_b(min(2, KTn - 1), R2);
+    int kt = 0;
+    for (; kt + 2 < KTn; kt += 3) {
+      tile(kt, lds0, lds2, R0);
+      tile(kt + 1, lds1, lds0, R1);
+      tile(kt + 2, lds2, lds1, R2);
+    }
+    if (kt < KTn) tile(kt, lds0, lds2, R0);
+    if (kt + 1 < KTn) tile(kt + 1, lds1, lds0, R1);
+  } else {
+    // Two token buffers: the DMA of token tile kt+1 goes out at the start of
+    // tile kt, the weight codes of tile kt+2 at its end.
+    auto tile_start = [&](int kt, uint8_t* next) {
+      // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F74);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // past the last tile this re-fills the idle buffer (no branch in the loop)
+      dma_a(min(kt + 1, KTn - 1), next);
+    };
+    dma_a(0, lds0);
+    load_b(0, R0);
+    load_b(min(1, KTn - 1), R1);
+    int kt = 0;
+    for (; kt + 1 < KTn; kt += 2) {
+      tile_start(kt, lds1);
+      mma_jit(lds0, R0);
+      load_b(min(kt + 2, KTn - 1), R0);
+      tile_start(kt + 1, lds0);
+      mma_jit(lds1, R1);
+      load_b(min(kt + 3, KTn - 1), R1);
+    }
+    if (kt < KTn) {
+      tile_start(kt, lds1);
+      mma_jit(lds0, R0);
+    }
   }
   // no LDS DMA may still be in flight when the block's LDS is released
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -451,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(FfnArgs a) {
       if (i < t.mcount) {
         const int row = t.row0 + i;
         if (GU) {
-          store_gu(a, row, 32 * (4 * t.nt + wave) + n, acc[mi][0][r], acc[mi][1][r]);
+          store_gu(a, row, 32 * unit + n, acc[mi][0][r], acc[mi][1][r]);
         } else {
           store_dn(a, 0, row, 32 * rt0 + n, acc[mi][0][r]);
           store_dn(a, 0, row, 32 * (rt0 + 1) + n, acc[mi][1][r]);
@@ -471,9 +527,10 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
     dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
     hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a);
   } else {
-    const int NB = GU ? a.N / 128 : (a.N + 255) / 256;
+    const int NU = a.N / (GU ? 32 : 64);
+    const int NB = (NU + kPW - 1) / kPW;
     dim3 grid(max_tiles(a.R, a.E, kBM) * NB);
-    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(64 * kPW), 0, s, a);
   }
   return hipGetLastError();
 }
