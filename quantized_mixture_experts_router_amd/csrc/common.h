@@ -104,15 +104,22 @@ struct WsLayout {
 
 // Choice of kernel family and split-K factor from host-known sizes only.
 inline bool use_decode_path(int T, int k, int E) { return (long)T * k < 48L * E; }
+#ifndef MOEQ_DEC_TARGET
+#define MOEQ_DEC_TARGET 384
+#endif
+// Down projection at decode sizes: the K range is split over blocks so that
+// about MOEQ_DEC_TARGET blocks stream weights (long streams per wavefront),
+// at least 8 K tiles per wavefront.
 inline int down_splits(int T, int H, int I, int E, int k) {
   if (!use_decode_path(T, k, E)) return 1;
   long rows = (long)T * k;
   long mtiles = rows < E ? rows : E;  // at most one 32-row tile per touched expert
   long blocks = mtiles * (H / 64);    // one block = 2 row tiles of 32
-  int kt_total = I / 64;              // upper bound on K tiles (4-bit)
-  int s = 1;
-  while (blocks * s < 2048 && s * 2 * 8 <= kt_total) s *= 2;
-  return s;
+  if (blocks <= 0) return 1;
+  int kt_total = I / 64;              // K tiles of a 4-bit matrix
+  long s = (MOEQ_DEC_TARGET + blocks / 2) / blocks;
+  if (s > kt_total / 32) s = kt_total / 32;
+  return s < 1 ? 1 : (int)s;
 }
 
 inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {

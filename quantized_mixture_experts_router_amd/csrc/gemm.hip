@@ -167,20 +167,29 @@ struct BTile {
 // Decode family
 // ===========================================================================
 template <class F, bool GU>
-__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
+__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
+  // The 4 wavefronts of a block form 4/ksw row groups of ksw wavefronts; the
+  // ksw wavefronts of a group split the K tiles of the block's K range and
+  // meet in LDS. A row group is the gate/up pair (output tile j: row tiles
+  // 2j, 2j+1) or the down row-tile pair (2j, 2j+1).
   __shared__ float red[4 * 2 * 16 * 64];
-  const int NB = GU ? a.N / 32 : a.N / 64;
+  const int G = 4 / ksw;
+  const int NRG = GU ? a.N / 32 : a.N / 64;
+  const int NB = (NRG + G - 1) / G;
   Task t;
   if (!find_task<GU>(a, F::ID, 32, NB, blockIdx.x, t)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, kh = lane >> 5;
+  const int grp = wave / ksw, ks = wave % ksw;
+  const int rg = t.nt * G + grp;
+  const bool on = rg < NRG;
   const int KTn = a.K / F::KT;
   const int NE = a.K / F::GE;
   const moe_packed_expert* ex = a.experts + t.e;
   const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
   const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
-  const int rt0 = 2 * t.nt;  // gate tile (gate/up) or first of two row tiles (down)
+  const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
   const uint8_t* c0 = codes + (size_t)rt0 * KTn * 1024 + lane * 16;
   const uint8_t* c1 = c0 + (size_t)KTn * 1024;
   const uint8_t* p0 = params + ((size_t)rt0 * NE * 32 + n) * F::EB;
@@ -197,11 +206,11 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
   struct AFrag {
     f16x8 v[F::STEPS];
   };
-  // tiles of this wavefront: kt_i = kb + wave + 4 i, i < nt. Prefetches past
+  // tiles of this wavefront: kt_i = kb + ks + ksw i, i < nt. Prefetches past
   // the last tile re-read a valid tile (result unused) so that the loop body
   // has no conditional loads and exact wait counts.
-  const int nt = ke > kb + wave ? (ke - kb - wave + 3) / 4 : 0;
-  auto tile_of = [&](int i) { return min(kb + wave + 4 * i, KTn - 1); };
+  const int nt = ke > kb + ks ? (ke - kb - ks + ksw - 1) / ksw : 0;
+  auto tile_of = [&](int i) { return min(kb + ks + ksw * i, KTn - 1); };
   auto load_b = [&](int i, BTile<F>& b) {
     const int kt = tile_of(i);
     b.w0 = ldg<true, u32x4>(c0 + (size_t)kt * 1024);
@@ -246,31 +255,39 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a) {
     load_a(i + 6, A0); load_b(i + 7, B1); if (i + 5 < nt) compute(B2, A1);
   }
 
-  // reduce the 4 wavefronts' partial sums: red[w][m][r][lane]
+  // reduce the ksw partial sums of each row group: red[w][m][r][lane];
+  // wavefront ks of a group finalises registers r = (16/ksw) ks .. +16/ksw
+  if (ksw > 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[((wave * 2 + 0) * 16 + r) * 64 + lane] = acc0[r];
+      red[((wave * 2 + 1) * 16 + r) * 64 + lane] = acc1[r];
+    }
+    __syncthreads();
+  }
+  if (!on) return;
+  const int RPW = 16 / ksw;
+  const int w0 = grp * ksw;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    red[((wave * 2 + 0) * 16 + r) * 64 + lane] = acc0[r];
-    red[((wave * 2 + 1) * 16 + r) * 64 + lane] = acc1[r];
-  }
-  __syncthreads();
-  // wavefront w finalises registers r = 4w .. 4w+3
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = 4 * wave + rr;
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      v0 += red[((w * 2 + 0) * 16 + r) * 64 + lane];
-      v1 += red[((w * 2 + 1) * 16 + r) * 64 + lane];
+    if (r / RPW != ks) continue;
+    float v0 = acc0[r], v1 = acc1[r];
+    if (ksw > 1) {
+      v0 = 0.f;
+      v1 = 0.f;
+      for (int w = 0; w < ksw; ++w) {
+        v0 += red[(((w0 + w) * 2 + 0) * 16 + r) * 64 + lane];
+        v1 += red[(((w0 + w) * 2 + 1) * 16 + r) * 64 + lane];
+      }
     }
     const int i = acc_row(r, lane);
     if (i < t.mcount) {
       const int row = t.row0 + i;
       if (GU) {
-        store_gu(a, row, 32 * t.nt + n, v0, v1);
+        store_gu(a, row, 32 * rg + n, v0, v1);
       } else {
-        store_dn(a, split, row, 64 * t.nt + n, v0);
-        store_dn(a, split, row, 64 * t.nt + 32 + n, v1);
+        store_dn(a, split, row, 64 * rg + n, v0);
+        store_dn(a, split, row, 64 * rg + 32 + n, v1);
       }
     }
   }
@@ -523,9 +540,14 @@ template <int FID, bool GU>
 hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   using F = typename FmtOf<FID>::T;
   if (decode) {
-    const int NB = GU ? a.N / 32 : a.N / 64;
+    // wavefronts splitting K inside a block: as many as keep >= 16 K tiles
+    // (per split) on each
+    const int KTn = a.K / F::KT / (GU ? 1 : a.splits);
+    const int ksw = KTn >= 64 ? 4 : (KTn >= 32 ? 2 : 1);
+    const int NRG = GU ? a.N / 32 : a.N / 64;
+    const int NB = (NRG + 4 / ksw - 1) / (4 / ksw);
     dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
-    hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a, ksw);
   } else {
     const int NU = a.N / (GU ? 32 : 64);
     const int NB = (NU + kPW - 1) / kPW;

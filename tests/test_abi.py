@@ -33,6 +33,14 @@ def test_status_strings():
     assert L.moe_status_string(-4) == b"workspace too small"
 
 
+def test_workspace_size_empty_and_decode_shapes():
+    # T = 0 and every decode shape of the workloads size without error
+    for T in (0, 1, 8, 16, 32, 64):
+        for (H, I, E, k) in ((4096, 14336, 8, 2), (2048, 512, 256, 6), (8192, 16384, 64, 2), (256, 128, 8, 2)):
+            for act in (0, 2):
+                assert moeq.workspace_size(T, H, I, E, k, act) >= 256
+
+
 def test_workspace_size_monotone():
     a = moeq.workspace_size(16, 4096, 14336, 8, 2)
     b = moeq.workspace_size(2048, 4096, 14336, 8, 2)
