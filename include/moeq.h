@@ -30,8 +30,8 @@
  *  - Data-dependent trouble found on the device (an expert id out of range,
  *    NaN router logits) sets bits of the flag word at the start of the
  *    workspace (MOE_FLAG_*), readable after the stream synchronises.
- *    moe_permute and moe_layer_forward clear it; the FFN phases only add
- *    bits to it.
+ *    moe_permute and moe_layer_forward set it (overwriting what a previous
+ *    call left); the FFN phases only add bits to it.
  *  - Matrices are row-major; int32 indices; fp32 weights of the router.
  */
 #ifndef MOEQ_H
@@ -77,6 +77,11 @@ enum {
   MOE_FLAG_FORMAT_NOT_LAUNCHED = 1u << 2 /* an expert with rows has a format outside
                                             fmt_mask: its rows were not computed */
 };
+
+/* Routing id that moe_route writes in every slot of a token whose router
+ * logits include a NaN (the token's weights are 0). moe_permute drops such
+ * assignments and raises MOE_FLAG_NAN_LOGIT. */
+#define MOE_ID_NAN (-2)
 
 /* One weight matrix W[rows, cols] in the canonical block format.
  * Groups of `group` consecutive elements along cols (the GEMM's K).
@@ -152,7 +157,8 @@ size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
  * selection matches an exact evaluation except on near-ties.
  * Outputs (device): topk_ids int32 [T,k] (descending logit), topk_w fp32
  * [T,k] (softmax over the k selected logits, computed in fp64), logits fp32
- * [T,E] (optional, NULL to skip). Constraints: 1 <= k <= min(E, 32),
+ * [T,E] (optional, NULL to skip). A token whose logits include a NaN gets
+ * MOE_ID_NAN in every slot and weights 0. Constraints: 1 <= k <= min(E, 32),
  * E <= 256, H % 8 == 0, x/Wr 16-byte aligned. T == 0 is a no-op. */
 moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b,
                      int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
@@ -164,7 +170,9 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
  * (token of the r-th sorted assignment; ascending token inside each
  * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: at least 256
  * bytes, 256-byte aligned (its first word is the flag word).
- * Ids outside [0,E) are dropped and flag MOE_FLAG_BAD_EXPERT_ID. */
+ * Ids outside [0,E) are dropped (inv = -1): MOE_ID_NAN raises
+ * MOE_FLAG_NAN_LOGIT, any other MOE_FLAG_BAD_EXPERT_ID. The flag word is
+ * written with exactly the bits this call found. */
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
                        size_t ws_bytes, void* stream);

@@ -3,7 +3,7 @@
 The compute lives in libmoeq.so (hand-written HIP kernels behind the C ABI of
 include/moeq.h); this package is its thin Python binding.
 """
-from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT,
+from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT, ID_NAN,
                    MOE_BF16, MOE_F32, MOE_W_ASYM, MOE_W_E2M1, EXPORTED, LIB, LIB_PATH,
                    DeviceQMat, MoeError, PackedExperts, act_quant_i8, combine, ffn_down,
                    ffn_gather, ffn_gate_up, grouped_ffn, layer_forward, pack_expert, pack_experts,
@@ -11,7 +11,8 @@ from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_L
                    workspace_size)
 
 __all__ = [
-    "ACT_I8_X", "ACT_I8_XH", "ACT_NONE", "FLAG_BAD_EXPERT_ID", "FLAG_NAN_LOGIT", "MOE_BF16",
+    "ACT_I8_X", "ACT_I8_XH", "ACT_NONE", "FLAG_BAD_EXPERT_ID", "FLAG_NAN_LOGIT", "ID_NAN",
+    "MOE_BF16",
     "MOE_F32", "MOE_W_ASYM", "MOE_W_E2M1", "EXPORTED", "LIB", "LIB_PATH", "DeviceQMat",
     "MoeError", "PackedExperts", "act_quant_i8", "combine", "ffn_down", "ffn_gather",
     "ffn_gate_up",

@@ -19,6 +19,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_W_ASYM, MOE_W_E2M1 = 1, 2
 ACT_NONE, ACT_I8_X, ACT_I8_XH = 0, 1, 2
 FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT, FLAG_FORMAT_NOT_LAUNCHED = 1, 2, 4
+ID_NAN = -2  # routing id of a token whose router logits include a NaN
 
 
 class MoeError(RuntimeError):

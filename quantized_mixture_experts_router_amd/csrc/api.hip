@@ -70,7 +70,7 @@ inline char* ws_at(void* ws, size_t off) { return (char*)ws + off; }
 // phases of the grouped FFN (workspace already validated)
 moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, int H, int k,
                       moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
-  MOE_TRY(launch_gather_a(x, xdt, perm, T * k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
+  MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
                           (float*)ws_at(ws, L.ascale), s));
   return MOE_OK;
 }
@@ -207,7 +207,7 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
   if (T == 0) return MOE_OK;
   if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(Wr, 16)) return MOE_ERR_ALIGNMENT;
-  return hip_status(launch_route(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, logits, nullptr,
+  return hip_status(launch_route(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, logits,
                                  (hipStream_t)stream));
 }
 
@@ -221,7 +221,6 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
   if (ws_bytes < 256) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* flags = (uint32_t*)ws;
-  MOE_TRY(launch_zero_u32(flags, 64, s));
   MOE_TRY(launch_permute(topk_ids, T, k, E, counts, offsets, perm_token, inv, flags, s));
   return MOE_OK;
 }
@@ -323,11 +322,17 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
   int32_t* perm = (int32_t*)ws_at(ws, L.perm);
   int32_t* inv = (int32_t*)ws_at(ws, L.inv);
   float* yp = (float*)ws_at(ws, L.yp);
-  MOE_TRY(launch_zero_u32(flags, 64, s));
-  MOE_TRY(launch_route(x, xdt, Wr, b, T, H, E, k, ids, w, nullptr, flags, s));
-  MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
-  st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
-  if (st != MOE_OK) return st;
+  if (L.decode && front_fits(T, H, E)) {
+    // small batch: routing, permutation and gather in one block
+    MOE_TRY(launch_front(x, xdt, Wr, b, T, H, E, k, ids, w, counts, offsets, perm, inv, flags,
+                         aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16), (float*)ws_at(ws, L.ascale),
+                         s));
+  } else {
+    MOE_TRY(launch_route(x, xdt, Wr, b, T, H, E, k, ids, w, nullptr, s));
+    MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
+    st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
+    if (st != MOE_OK) return st;
+  }
   st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, s);
   if (st != MOE_OK) return st;
   st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, yp, s);

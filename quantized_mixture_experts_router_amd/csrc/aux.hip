@@ -7,21 +7,19 @@
 // Weighted combine: Baidu Cloud quantized-MoE article, expert routing
 // section (output = sum of the top-k weights times the expert outputs).
 #include "common.h"
+#include "rows_dev.h"
 
 namespace moeq {
 
 namespace {
+
+using namespace rows;
 
 constexpr int kThreads = 256;
 
 // ===========================================================================
 // Per-token int8 quantisation and input gathering
 // ===========================================================================
-__device__ inline float load_val(const void* x, int dt, size_t idx) {
-  if (dt == MOE_BF16) return __uint_as_float((uint32_t)((const uint16_t*)x)[idx] << 16);
-  return ((const float*)x)[idx];
-}
-
 // Block-wide absmax of a row (256 threads).
 __device__ inline float row_absmax(const void* x, int dt, size_t base, int cols) {
   __shared__ float s_red[kThreads / 64];
@@ -36,51 +34,25 @@ __device__ inline float row_absmax(const void* x, int dt, size_t base, int cols)
   return r;
 }
 
-// q = clamp(rint(v / s), -127, 127) with IEEE fp32 division; s = absmax / 127.
-__device__ inline float quant_i8(float v, float s) {
-  if (s == 0.f) return 0.f;
-  float q = __builtin_rintf(__fdiv_rn(v, s));
-  return fminf(fmaxf(q, -127.f), 127.f);
-}
-
-// 8 consecutive elements of a bf16 or fp32 row as fp32 (16-/32-byte loads)
-__device__ inline void load8(const void* x, int dt, size_t idx, float* v) {
-  if (dt == MOE_BF16) {
-    const u32x4 u = *reinterpret_cast<const u32x4*>((const uint16_t*)x + idx);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = __uint_as_float(u[q] << 16);
-      v[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>((const float*)x + idx);
-    const f32x4 a = p[0], b = p[1];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[q] = a[q];
-      v[4 + q] = b[q];
-    }
-  }
-}
-
-__device__ inline void store8_f16(f16* dst, const float* v) {
-  f16x8 h;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) h[q] = (f16)v[q];
-  *reinterpret_cast<f16x8*>(dst) = h;
-}
-
 // one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes;
 // each thread moves 8 columns at a time (H % 8 == 0, x 16-byte aligned)
 __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restrict__ x, int dt,
-                                                          const int32_t* __restrict__ perm, int H,
+                                                          const int32_t* __restrict__ perm, int T,
+                                                          int H,
                                                           int quant, f16* __restrict__ a16,
                                                           float* __restrict__ ascale) {
   __shared__ float s_red[kThreads / 64];
   const int r = blockIdx.x;
   const int t = perm[r];
-  const size_t base = (size_t)t * H;
   f16* dst = a16 + (size_t)r * H;
+  if ((unsigned)t >= (unsigned)T) {
+    // a slot the permutation left unused (dropped assignments): never read x
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) store8_f16(dst + c, z);
+    if (quant && threadIdx.x == 0) ascale[r] = 0.f;
+    return;
+  }
+  const size_t base = (size_t)t * H;
   if (quant) {
     float m = 0.f;
     for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
@@ -230,18 +202,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
 
 }  // namespace
 
-hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int R, int H, int quant,
-                           f16* a16, float* ascale, hipStream_t s) {
+hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
+                           int quant, f16* a16, float* ascale, hipStream_t s) {
+  const int R = T * k;
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_a_kernel, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, H, quant, a16,
-                     ascale);
+  hipLaunchKernelGGL(gather_a_kernel, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, T, H, quant,
+                     a16, ascale);
   return hipGetLastError();
 }
 
@@ -277,9 +246,5 @@ hipError_t launch_combine(const float* yp, int splits, const float* w, const int
   return hipGetLastError();
 }
 
-hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s) {
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
 
 }  // namespace moeq

@@ -151,13 +151,18 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
 // error code from the launch.
 // ---------------------------------------------------------------------------
 hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
-                        int E, int k, int32_t* ids, float* w, float* logits, uint32_t* flags,
-                        hipStream_t s);
+                        int E, int k, int32_t* ids, float* w, float* logits, hipStream_t s);
+// fused small-batch front: routing, permutation, gather (+ int8) in one block
+bool front_fits(int T, int H, int E);
+hipError_t launch_front(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
+                        int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv, uint32_t* flags, int quant, f16* a16,
+                        float* ascale, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
                           hipStream_t s);
-hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int R, int H, int quant,
-                           f16* a16, float* ascale, hipStream_t s);
+hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
+                           int quant, f16* a16, float* ascale, hipStream_t s);
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
                                  hipStream_t s);
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
@@ -175,6 +180,5 @@ hipError_t launch_combine(const float* yp, int splits, const float* w, const int
                           int H, int k, void* out, int out_dt, hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,
                               void* params, hipStream_t s);
-hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 
 }  // namespace moeq

@@ -166,8 +166,14 @@ struct BTile {
 // ===========================================================================
 // Decode family
 // ===========================================================================
+#ifndef MOEQ_DEC_OCC
+#define MOEQ_DEC_OCC 1
+#endif
+#ifndef MOEQ_DEC_BSLOTS
+#define MOEQ_DEC_BSLOTS 3
+#endif
 template <class F, bool GU>
-__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
+__global__ __launch_bounds__(kThreads, MOEQ_DEC_OCC) void ffn_decode_kernel(FfnArgs a, int ksw) {
   // The 4 wavefronts of a block form 4/ksw row groups of ksw wavefronts; the
   // ksw wavefronts of a group split the K tiles of the block's K range and
   // meet in LDS. A row group is the gate/up pair (output tile j: row tiles
@@ -239,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
       acc1 = mfma32(af.v[s], b1, acc1);
     }
   };
+  if (MOEQ_DEC_BSLOTS == 3) {
   // weights two tiles ahead (three slots), token fragments one tile ahead
   BTile<F> B0, B1, B2;
   AFrag A0, A1;
@@ -253,6 +260,16 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
     load_a(i + 4, A0); load_b(i + 5, B2); if (i + 3 < nt) compute(B0, A1);
     load_a(i + 5, A1); load_b(i + 6, B0); if (i + 4 < nt) compute(B1, A0);
     load_a(i + 6, A0); load_b(i + 7, B1); if (i + 5 < nt) compute(B2, A1);
+  }
+  } else {
+  BTile<F> B0, B1;
+  AFrag A0, A1;
+  load_b(0, B0);
+  load_a(0, A0);
+  for (int i = 0; i < nt; i += 2) {
+    load_a(i + 1, A1); load_b(i + 1, B1); if (i < nt) compute(B0, A0);
+    load_a(i + 2, A0); load_b(i + 2, B0); if (i + 1 < nt) compute(B1, A1);
+  }
   }
 
   // reduce the ksw partial sums of each row group: red[w][m][r][lane];

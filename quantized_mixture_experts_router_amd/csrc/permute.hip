@@ -1,119 +1,18 @@
-// Stable counting-sort permutation of the T*k (token, slot) assignments by
-// expert, giving contiguous per-expert row segments for the grouped GEMMs.
-//
-// The pages give the grouping only as "route each token to its top-k experts"
-// (Baidu Cloud quantized-MoE article, expert routing section; "Sparse
-// activation ... 2% activation", section 2.2); the segment order is this
-// library's choice: ascending token inside each expert, which makes the
-// permutation unique and reproducible run to run.
-//
-// One block of 16 waves: wave w owns a contiguous chunk of assignments.
-//  1. per-wave expert histograms (LDS);
-//  2. counts, offsets and per-(wave, expert) bases by prefix sums;
-//  3. each wave walks its chunk 64 assignments at a time; a lane's rank among
-//     earlier lanes with the same expert comes from ballots over the expert
-//     id bits, so equal experts keep their assignment order.
-#include "common.h"
+// Permutation kernel: one block runs permute_block (permute_dev.h) and
+// stores the flag word of the call.
+#include "permute_dev.h"
 
 namespace moeq {
 
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = kWaves * 64;
-constexpr int kMaxE = 1024;
-
-__global__ __launch_bounds__(kThreads) void permute_kernel(
+__global__ __launch_bounds__(pm::kThreads) void permute_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     uint32_t* __restrict__ flags) {
   extern __shared__ int32_t sm[];
-  int32_t* base = sm;                       // [kWaves][E]
-  int32_t* scan = sm + kWaves * E;          // [kThreads] scan scratch
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-
-  for (int i = tid; i < kWaves * E; i += kThreads) base[i] = 0;
-  __syncthreads();
-
-  const int chunk = ((R + kWaves - 1) / kWaves + 63) / 64 * 64;
-  const int c0 = wave * chunk;
-  const int c1 = min(R, c0 + chunk);
-
-  // 1. histograms
-  bool bad = false;
-  for (int a = c0 + lane; a < c1; a += 64) {
-    int e = ids[a];
-    if (e >= 0 && e < E)
-      atomicAdd(&base[wave * E + e], 1);
-    else
-      bad = true;
-  }
-  if (bad && flags) atomicOr(flags, (uint32_t)MOE_FLAG_BAD_EXPERT_ID);
-  __syncthreads();
-
-  // 2. per-expert totals (thread e loops over waves), then exclusive scan
-  const int EPT = (E + kThreads - 1) / kThreads;  // experts per thread (1 for E <= 1024)
-  int local_total = 0;
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    if (e < E) {
-      int run = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        int c = base[w * E + e];
-        base[w * E + e] = run;
-        run += c;
-      }
-      counts[e] = run;
-      local_total += run;
-    }
-  }
-  scan[tid] = local_total;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int excl = scan[tid] - local_total;
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    if (e < E) {
-      int c = 0;
-      for (int w = 0; w < kWaves; ++w) base[w * E + e] += excl;
-      offsets[e] = excl;
-      // counts[e] was written above; recompute the running prefix
-      c = counts[e];
-      excl += c;
-    }
-  }
-  if (tid == kThreads - 1) offsets[E] = scan[kThreads - 1];
-  __syncthreads();
-
-  // 3. stable scatter
-  const int bits = 32 - __clz(E > 1 ? E - 1 : 1);
-  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int p = c0; p < c1; p += 64) {
-    int a = p + lane;
-    int e = a < c1 ? ids[a] : -1;
-    bool valid = e >= 0 && e < E;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      uint64_t bb = __ballot(valid && ((e >> b) & 1));
-      m &= ((e >> b) & 1) ? bb : ~bb;
-    }
-    if (valid) {
-      int rank = __popcll(m & lt_mask);
-      int pos = base[wave * E + e] + rank;
-      perm[pos] = a / k;
-      inv[a] = pos;
-      bool last = (m >> lane) == 1ull;  // no same-expert lane above this one
-      if (last) base[wave * E + e] += rank + 1;
-    } else if (a < c1) {
-      inv[a] = -1;
-    }
-  }
+  const uint32_t bits = pm::permute_block<pm::kWaves>(ids, R, k, E, counts, offsets, perm, inv, sm);
+  if (threadIdx.x == 0 && flags) *flags = bits;  // the call's flag word starts here
 }
 
 }  // namespace
@@ -121,9 +20,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
                           hipStream_t s) {
-  int R = T * k;
-  size_t smem = sizeof(int32_t) * ((size_t)kWaves * E + kThreads);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), smem, s, ids, R, k, E, counts,
+  const int R = T * k;
+  const size_t smem = sizeof(int32_t) * pm::permute_smem_words(pm::kWaves, E);
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(pm::kThreads), smem, s, ids, R, k, E, counts,
                      offsets, perm, inv, flags);
   return hipGetLastError();
 }

@@ -150,6 +150,9 @@ LAYER_CASES = [
     ("hotcold", 2048, 256, 128, 256, 8),
     ("w4a8", 16, 512, 512, 8, 2),
     ("w4a8", 300, 512, 512, 8, 2),
+    # small enough for the fused one-block front (T*E*H <= 2^16)
+    ("mixtral", 2, 512, 1024, 8, 2),
+    ("fine_e2m1", 1, 256, 256, 32, 6),
 ]
 
 
@@ -175,19 +178,29 @@ def test_layer_parity(moeq, name, T, H, I, E, k):
     assert err.max() <= tolerance(cfg), err.max()
 
 
-def test_split_api_matches_layer_forward(moeq):
-    cfg = synth.scaled_config("hotcold", T=300, H=256, I=128, E=64, k=8, weight_mode="quantize", n_hot=16)
+SPLIT_CASES = [
+    # name, T, H, I, E, k, n_hot: one case per front-end path of the layer
+    ("hotcold", 300, 256, 128, 64, 8, 16),   # separate router/permute/gather kernels
+    ("mixtral", 8, 512, 1024, 8, 2, None),   # fused small-batch front
+    ("w4a8", 16, 512, 512, 8, 2, None),      # fused front with int8 expert inputs
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,n_hot", SPLIT_CASES)
+def test_split_api_matches_layer_forward(moeq, name, T, H, I, E, k, n_hot):
+    cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode="quantize", n_hot=n_hot)
     wl = Workload(cfg)
-    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)
+    act = cfg.act
+    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=act)
     ids2, w2 = moeq.route(wl.x, wl.Wr, wl.b, cfg.k)
     counts, offsets, perm, inv, _ = moeq.permute(ids2, cfg.E)
-    Y = moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k)
+    Y = moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k, act=act)
     out2 = moeq.combine(Y, w2, inv, cfg.T, cfg.k)
-    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
-    moeq.ffn_gather(wl.x, perm, cfg.k, wl.packed, 0, ws)
-    moeq.ffn_gate_up(cfg.T, wl.packed, offsets, cfg.k, 0, ws)
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, act)
+    moeq.ffn_gather(wl.x, perm, cfg.k, wl.packed, act, ws)
+    moeq.ffn_gate_up(cfg.T, wl.packed, offsets, cfg.k, act, ws)
     Y3 = torch.empty_like(Y)
-    moeq.ffn_down(cfg.T, wl.packed, offsets, cfg.k, 0, Y3, ws)
+    moeq.ffn_down(cfg.T, wl.packed, offsets, cfg.k, act, Y3, ws)
     torch.cuda.synchronize()
     assert torch.equal(Y, Y3)
     assert torch.equal(ids, ids2) and torch.equal(w, w2)
@@ -205,6 +218,33 @@ def test_layer_deterministic(moeq):
     b = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k)[0]
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T", [6, 600])  # fused front / separate kernels
+def test_nan_token(moeq, T):
+    """A token with a NaN input: its routing is MOE_ID_NAN with weight 0, the
+    layer flags MOE_FLAG_NAN_LOGIT and leaves its row 0, and every other
+    token's output equals the layer run without that token's values."""
+    cfg = synth.scaled_config("tiny", T=T, H=256, I=512, E=8, k=2, weight_mode="quantize")
+    wl = Workload(cfg)
+    bad = T // 3
+    x_nan = wl.x.clone()
+    x_nan[bad, 5] = float("nan")
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    out, ids, w = moeq.layer_forward(x_nan, wl.Wr, wl.b, wl.packed, cfg.k, ws=ws)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) == moeq.FLAG_NAN_LOGIT
+    assert (ids[bad] == moeq.ID_NAN).all() and (w[bad] == 0).all()
+    assert (out[bad] == 0).all()
+    ref, ids_ref, _ = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, ws=ws)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) == 0  # the next call starts its own flag word
+    keep = torch.arange(T, device=out.device) != bad
+    assert torch.equal(ids[keep], ids_ref[keep])
+    assert torch.equal(out[keep], ref[keep])
+    ids2, w2 = moeq.route(x_nan, wl.Wr, wl.b, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids2, ids) and torch.equal(w2, w)
 
 
 def test_empty_batch(moeq):
