@@ -10,15 +10,19 @@
 //
 // Two kernel families share the tile layout and the in-register decoding:
 //  * decode (few rows per expert): a block is 4 wavefronts on the same 32-row
-//    token tile and the same 64 weight rows, splitting K; weights stream from
-//    HBM straight into registers (non-temporal 16-byte loads per lane, 1 KiB
-//    per wave and tile), are decoded to fp16 and fed to v_mfma_f32_32x32x16_f16 with the
-//    token rows padded to 32. The 4 partial sums meet in LDS.
-//  * prefill (many rows per expert): a block owns 128 token rows and 256
-//    weight rows; the token tile is staged in LDS (double-buffered, shared by
-//    the 4 wavefronts) and each wavefront streams its own 64 weight rows into
-//    registers; two blocks share a CU so that one block's vector-ALU decode
-//    overlaps the other's MFMAs.
+//    token tile; they form 4/ksw row groups (64 weight rows each) whose ksw
+//    wavefronts split the K tiles, ksw chosen from K so every wavefront
+//    streams at least 16 tiles. Weights stream from HBM straight into
+//    registers (non-temporal 16-byte loads per lane, 1 KiB per wave and
+//    tile, two tiles ahead), are decoded to fp16 and fed to
+//    v_mfma_f32_32x32x16_f16 with the token rows padded to 32; partial sums
+//    meet in LDS. The down projection also splits K across blocks.
+//  * prefill (many rows per expert): a block owns 128 token rows and 4 x 64
+//    weight rows; the token tile reaches LDS by DMA (global_load_lds, rows
+//    swizzled for the 64-bank LDS, three buffers for 4-bit tiles) and is
+//    shared by the 4 wavefronts, each of which streams its own weight rows
+//    into registers and decodes step s+1 while the MFMAs of step s run; two
+//    blocks share a CU so one block's decode overlaps the other's MFMAs.
 // Every kernel is instantiated per block format; a launch handles the experts
 // of its format. Tasks are (expert, n-tile, m-tile), expert-major, so blocks
 // that share weight tiles run together; each block derives its task from the
@@ -166,14 +170,13 @@ struct BTile {
 // ===========================================================================
 // Decode family
 // ===========================================================================
-#ifndef MOEQ_DEC_OCC
-#define MOEQ_DEC_OCC 1
-#endif
+// Weight-code register slots of the decode loop: 3 (two tiles of prefetch,
+// occupancy 3) measures best; 2 (one tile, occupancy 4) is the alternative.
 #ifndef MOEQ_DEC_BSLOTS
 #define MOEQ_DEC_BSLOTS 3
 #endif
 template <class F, bool GU>
-__global__ __launch_bounds__(kThreads, MOEQ_DEC_OCC) void ffn_decode_kernel(FfnArgs a, int ksw) {
+__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
   // The 4 wavefronts of a block form 4/ksw row groups of ksw wavefronts; the
   // ksw wavefronts of a group split the K tiles of the block's K range and
   // meet in LDS. A row group is the gate/up pair (output tile j: row tiles
@@ -313,6 +316,9 @@ __global__ __launch_bounds__(kThreads, MOEQ_DEC_OCC) void ffn_decode_kernel(FfnA
 // ===========================================================================
 // Prefill family
 // ===========================================================================
+// Prefill tuning knobs (defaults measured best on MI355X): non-temporal
+// weight loads (0: tiles are re-read by every m-tile of an expert), the
+// three-buffer pipeline for 16 KiB token tiles, wavefronts per block.
 #ifndef MOEQ_PF_NT
 #define MOEQ_PF_NT 0
 #endif
@@ -321,9 +327,6 @@ __global__ __launch_bounds__(kThreads, MOEQ_DEC_OCC) void ffn_decode_kernel(FfnA
 #endif
 #ifndef MOEQ_PF_WAVES
 #define MOEQ_PF_WAVES 4
-#endif
-#ifndef MOEQ_PF_PRIO
-#define MOEQ_PF_PRIO 0
 #endif
 constexpr int kBM = 128;
 constexpr bool kPrefillNT = MOEQ_PF_NT;  // weight tiles: non-temporal loads
@@ -457,13 +460,11 @@ __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs 
       __builtin_amdgcn_sched_barrier(0x0006);
       // (a wavefront with no row tile of its own computes on the clamped
       // tile and stores nothing: no branch around the matrix-core chain)
-      if (MOEQ_PF_PRIO) __builtin_amdgcn_s_setprio(MOEQ_PF_PRIO);
 #pragma unroll
       for (int mi = 0; mi < kMT; ++mi) {
         acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
         acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
       }
-      if (MOEQ_PF_PRIO) __builtin_amdgcn_s_setprio(0);
       if (s + 1 < F::STEPS) {
 #pragma unroll
         for (int mi = 0; mi < kMT; ++mi) av[mi] = an[mi];
