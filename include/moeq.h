@@ -151,18 +151,27 @@ uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 /* Workspace bytes the layer entry points need for these sizes. Host only. */
 size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
 
+/* Workspace bytes moe_route needs for these sizes (fp64 partial logits of
+ * its split hidden dimension; 0 when T <= 0). Host only. */
+size_t moe_route_workspace_size(int T, int H, int E);
+
 /* Router + top-k + softmax (steps 1-2 above).
  * x (device): [T,H] fp32 or bf16 (xdt). Wr (device): fp32 [E,H]. b (device):
  * fp32 [E] or NULL (no bias). Logits are accumulated in fp64 so that the
- * selection matches an exact evaluation except on near-ties.
+ * selection matches an exact evaluation except on near-ties; the partial
+ * sums of a split hidden dimension are added in a fixed order, so results
+ * are the same run to run.
  * Outputs (device): topk_ids int32 [T,k] (descending logit), topk_w fp32
  * [T,k] (softmax over the k selected logits, computed in fp64), logits fp32
  * [T,E] (optional, NULL to skip). A token whose logits include a NaN gets
- * MOE_ID_NAN in every slot and weights 0. Constraints: 1 <= k <= min(E, 32),
- * E <= 256, H % 8 == 0, x/Wr 16-byte aligned. T == 0 is a no-op. */
+ * MOE_ID_NAN in every slot and weights 0.
+ * ws (device): at least moe_route_workspace_size(T, H, E) bytes, 256-byte
+ * aligned; scratch, contents on return unspecified.
+ * Constraints: 1 <= k <= min(E, 32), E <= 256, H % 8 == 0, x/Wr 16-byte
+ * aligned. T == 0 is a no-op. */
 moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b,
                      int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
-                     float* logits, void* stream);
+                     float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* Stable counting sort of the T*k assignments a = t*k + j by expert.
  * topk_ids (device) int32 [T,k]. Outputs (device, int32): counts [E],

@@ -57,7 +57,8 @@ _SIGS = {
     "moe_packed_expert_bytes": ([ctypes.POINTER(ExpertCanonC)], _sz),
     "moe_pack_expert": ([ctypes.POINTER(ExpertCanonC), _vp, _sz, ctypes.POINTER(PackedExpertC), _vp], _i),
     "moe_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
-    "moe_route": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_route_workspace_size": ([_i, _i, _i], _sz),
+    "moe_route": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_permute": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_format_mask": ([ctypes.POINTER(PackedExpertC), _i], ctypes.c_uint32),
     "moe_grouped_ffn_q": ([_vp, _i, _vp, ctypes.c_uint32, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
@@ -217,15 +218,21 @@ def pack_experts(get_expert, E, device="cuda"):
 
 
 # ---------------------------------------------------------------- layer steps
-def route(x, Wr, b, k, want_logits=False):
+def route_workspace_size(T, H, E):
+    return int(LIB.moe_route_workspace_size(T, H, E))
+
+
+def route(x, Wr, b, k, want_logits=False, ws=None):
     x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
     T, H = x.shape
     E = Wr.shape[0]
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    if ws is None:
+        ws = torch.empty(max(route_workspace_size(T, H, E), 256), dtype=torch.uint8, device=x.device)
     _check(LIB.moe_route(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), T, H, E, k, _ptr(ids), _ptr(w),
-                         _ptr(logits), _stream()), "moe_route")
+                         _ptr(logits), _ptr(ws), ws.numel(), _stream()), "moe_route")
     return (ids, w, logits) if want_logits else (ids, w)
 
 

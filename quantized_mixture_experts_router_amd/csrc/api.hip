@@ -197,18 +197,24 @@ size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq) {
   return ws_layout(T, H, I, E, k, aq).total;
 }
 
+size_t moe_route_workspace_size(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return align256(route_plan(T, H, E).part_bytes);
+}
+
 moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b, int T, int H,
-                     int E, int k, int32_t* topk_ids, float* topk_w, float* logits,
-                     void* stream) {
+                     int E, int k, int32_t* topk_ids, float* topk_w, float* logits, void* ws,
+                     size_t ws_bytes, void* stream) {
   if (T < 0 || H <= 0 || E <= 0 || E > kMaxE || k < 1 || k > E || k > kMaxK)
     return MOE_ERR_INVALID_ARG;
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (H % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x || !Wr || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(Wr, 16)) return MOE_ERR_ALIGNMENT;
+  if (!x || !Wr || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < moe_route_workspace_size(T, H, E)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_route(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, logits,
-                                 (hipStream_t)stream));
+                                 (double*)ws, (hipStream_t)stream));
 }
 
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
@@ -322,13 +328,16 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
   int32_t* perm = (int32_t*)ws_at(ws, L.perm);
   int32_t* inv = (int32_t*)ws_at(ws, L.inv);
   float* yp = (float*)ws_at(ws, L.yp);
-  if (L.decode && front_fits(T, H, E)) {
-    // small batch: routing, permutation and gather in one block
-    MOE_TRY(launch_front(x, xdt, Wr, b, T, H, E, k, ids, w, counts, offsets, perm, inv, flags,
-                         aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16), (float*)ws_at(ws, L.ascale),
-                         s));
+  double* rpart = (double*)ws_at(ws, L.rpart);
+  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
+  const int kb = route_plan(T, H, E).kb;
+  if (L.decode && front_fits(T, H, E, k)) {
+    // small batch: top-k, permutation and gather in one block
+    MOE_TRY(launch_front(rpart, kb, x, xdt, b, T, H, E, k, ids, w, counts, offsets, perm, inv,
+                         flags, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
+                         (float*)ws_at(ws, L.ascale), s));
   } else {
-    MOE_TRY(launch_route(x, xdt, Wr, b, T, H, E, k, ids, w, nullptr, s));
+    MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
     MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
     st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
     if (st != MOE_OK) return st;

@@ -97,6 +97,8 @@ struct WsLayout {
   size_t h16;      // f16 [T*k, I] int8 codes of h (MOE_ACT_I8_XH)
   size_t hscale;   // f32 [T*k]
   size_t yp;       // f32 [splits, T*k, H] down-projection (partial) sums
+  size_t rpart;    // f64 [kb, T, E] router partial logits; aliases yp (routing ends
+                   // before the down projection writes it)
   size_t total;
   int splits;
   bool decode;
@@ -122,6 +124,39 @@ inline int down_splits(int T, int H, int I, int E, int k) {
   return s < 1 ? 1 : (int)s;
 }
 
+// Router plan (host-known sizes only). The fp64 logits kernel runs one
+// block per (16-token tile, group of ntw 16-expert tiles, K block); the
+// block's ks wavefronts split the K block's 16-column chunks, cpw chunks
+// each. K is split ks * kb ways in all, as few as give about
+// MOEQ_ROUTE_WAVES wavefronts (two per SIMD) with >= 4 chunks per wave;
+// expert tiles per wave drop below 4 first when the batch is too small for
+// that. kb > 1 leaves kb fp64 partial logits [kb][T][E] for the top-k to add.
+#ifndef MOEQ_ROUTE_WAVES
+#define MOEQ_ROUTE_WAVES 2048
+#endif
+struct RoutePlan {
+  int ntw, eg, ks, kb, cpw;
+  size_t part_bytes;  // workspace of the partial logits
+};
+inline RoutePlan route_plan(int T, int H, int E) {
+  RoutePlan p;
+  const long TT = (T + 15) / 16;
+  const int NT = (E + 15) / 16, NC = (H + 15) / 16;
+  int ntw = NT < 4 ? NT : 4;
+  while (ntw > 1 && TT * ((NT + ntw - 1) / ntw) * 16 < MOEQ_ROUTE_WAVES) ntw = (ntw + 1) / 2;
+  p.ntw = ntw;
+  p.eg = (NT + ntw - 1) / ntw;
+  int S = 1;
+  while (TT * p.eg * S < MOEQ_ROUTE_WAVES && NC / (2 * S) >= 4) S *= 2;
+  int ks = S < 16 ? S : 16;
+  while (ks * ntw > 32) ks /= 2;  // LDS of the in-block reduction <= 64 KiB
+  p.ks = ks;
+  p.kb = S / ks;
+  p.cpw = (NC + S - 1) / S;
+  p.part_bytes = (size_t)p.kb * (size_t)T * (size_t)E * sizeof(double);
+  return p;
+}
+
 inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   WsLayout L;
   size_t R = (size_t)T * k;
@@ -141,7 +176,10 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   L.hscale = take(R * 4);
   L.splits = down_splits(T, H, I, E, k);
   L.decode = use_decode_path(T, k, E);
-  L.yp = take((size_t)L.splits * R * H * 4);
+  const size_t yp_bytes = (size_t)L.splits * R * H * 4;
+  const size_t rp_bytes = route_plan(T, H, E).part_bytes;
+  L.yp = take(yp_bytes > rp_bytes ? yp_bytes : rp_bytes);
+  L.rpart = L.yp;
   L.total = o;
   return L;
 }
@@ -150,14 +188,22 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
 // Launchers (defined in the kernel translation units). All return a hip
 // error code from the launch.
 // ---------------------------------------------------------------------------
+// router: fp64 logits (partials P, route_plan(T, H, E).part_bytes), then
+// top-k + softmax; launch_route runs both
+hipError_t launch_route_logits(const void* x, int xdt, const float* Wr, int T, int H, int E,
+                               double* P, hipStream_t s);
+hipError_t launch_route_topk(const double* P, int KB, const float* b, int T, int E, int k,
+                             int32_t* ids, float* w, float* logits, hipStream_t s);
 hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
-                        int E, int k, int32_t* ids, float* w, float* logits, hipStream_t s);
-// fused small-batch front: routing, permutation, gather (+ int8) in one block
-bool front_fits(int T, int H, int E);
-hipError_t launch_front(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
-                        int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* inv, uint32_t* flags, int quant, f16* a16,
-                        float* ascale, hipStream_t s);
+                        int E, int k, int32_t* ids, float* w, float* logits, double* P,
+                        hipStream_t s);
+// fused small-batch front after the logits kernel: top-k, permutation,
+// gather (+ int8) in one block
+bool front_fits(int T, int H, int E, int k);
+hipError_t launch_front(const double* P, int KB, const void* x, int xdt, const float* b, int T,
+                        int H, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags, int quant,
+                        f16* a16, float* ascale, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
                           hipStream_t s);

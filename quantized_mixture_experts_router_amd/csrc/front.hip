@@ -1,12 +1,13 @@
-// Fused front of the layer for small batches: routing (logits, top-k,
-// softmax), the stable permutation by expert and the expert-input gather
-// (optionally quantised per token to int8) in one block of 8 wavefronts.
+// Fused front of the layer for small batches, run after the logits
+// kernel: top-k + softmax of every token, the stable permutation by expert
+// and the expert-input gather (optionally quantised per token to int8) in
+// one block of 8 wavefronts.
 //
 // At decode sizes each of these steps is a few microseconds of work but a
 // separate launch costs about as much again; one block that runs them back
-// to back replaces four launches (flag clearing, router, permutation,
-// gather). Used when the router's multiply-adds (T*E*H) take one CU only a
-// few microseconds; larger batches take the separate kernels.
+// to back replaces three launches (top-k, permutation, gather). Used while
+// the gathered rows and the logits stay small enough for one CU; larger
+// batches take the separate kernels.
 #include "permute_dev.h"
 #include "route_dev.h"
 #include "rows_dev.h"
@@ -16,31 +17,30 @@ namespace moeq {
 namespace {
 
 constexpr int kFW = 8;         // wavefronts
-constexpr int kFT = kFW * 64;  // threads (room for the router's 2-slice load batches)
+constexpr int kFT = kFW * 64;  // threads
 
 template <int XDT>
 __global__ __launch_bounds__(kFT) void front_kernel(
-    const void* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
-    int T, int H, int E, int k, int TG, int32_t* __restrict__ ids, float* __restrict__ w,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, uint32_t* __restrict__ flags, int quant, f16* __restrict__ a16,
-    float* __restrict__ ascale) {
-  extern __shared__ double smem[];
-  // 1. routing, 2 TG tokens per pass (the LDS is reused pass to pass)
-  for (int t0 = 0; t0 < T; t0 += TG * rt::kTM) {
-    rt::route_group<XDT, kFT>(x, Wr, bias, T, H, E, k, TG, t0, ids, w, nullptr, smem);
-    __syncthreads();
-  }
+    const double* __restrict__ P, int KB, const void* __restrict__ x,
+    const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* __restrict__ flags, int quant,
+    f16* __restrict__ a16, float* __restrict__ ascale) {
+  extern __shared__ int32_t smem[];
+  // 1. top-k + softmax, one wavefront per token
+  for (int t = threadIdx.x / 64; t < T; t += kFW)
+    rt::topk_token(P, KB, bias, T, E, k, t, ids, w, nullptr);
+  __syncthreads();
   // 2. permutation (its barriers make the ids written above visible)
   const uint32_t bits =
-      pm::permute_block<kFW>(ids, T * k, k, E, counts, offsets, perm, inv, (int32_t*)smem);
+      pm::permute_block<kFW>(ids, T * k, k, E, counts, offsets, perm, inv, smem);
   __syncthreads();
   // 3. gather of the rows the permutation produced
   const int rows_used = offsets[E];
   if (!quant) {
     // every thread moves 8-column chunks of any row; a batch of kU chunks per
     // thread is loaded before any is stored, so one memory round trip covers
-    // kU * 1024 chunks
+    // kU * kFT chunks
     constexpr int kU = 16;
     const int CH = H / 8;
     const int total = rows_used * CH;
@@ -108,29 +108,24 @@ __global__ __launch_bounds__(kFT) void front_kernel(
 
 }  // namespace
 
-// One CU's fp64 router pass must stay short: above ~64K multiply-adds the
-// separate router kernel (one block per token pair) is faster.
-bool front_fits(int T, int H, int E) { return (long)T * E * H <= (1L << 16); }
+// One CU gathers the rows and sums the partial logits: kept to a few
+// hundred KB of each.
+bool front_fits(int T, int H, int E, int k) {
+  return (long)T * k * H * 2 <= (256L << 10) && (long)T * E * route_plan(T, H, E).kb <= 32768;
+}
 
-hipError_t launch_front(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
-                        int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* inv, uint32_t* flags, int quant, f16* a16,
-                        float* ascale, hipStream_t s) {
+hipError_t launch_front(const double* P, int KB, const void* x, int xdt, const float* b, int T,
+                        int H, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags, int quant,
+                        f16* a16, float* ascale, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  // token groups per routing pass: all tokens at once when they fit, with at
-  // least two hidden-dimension slices per (token group, expert group)
-  const int EG = (E + rt::kEM - 1) / rt::kEM;
-  int TG = (T + rt::kTM - 1) / rt::kTM;
-  while (TG > 1 && (TG > 16 || TG * EG > kFT / 2)) TG = (TG + 1) / 2;
-  const size_t r_bytes = sizeof(double) * rt::route_smem_doubles(kFT, TG, E);
-  const size_t p_bytes = sizeof(int32_t) * pm::permute_smem_words(kFW, E);
-  const size_t smem = r_bytes > p_bytes ? r_bytes : p_bytes;
+  const size_t smem = sizeof(int32_t) * pm::permute_smem_words(kFW, E);
   if (xdt == MOE_BF16)
-    hipLaunchKernelGGL(front_kernel<MOE_BF16>, dim3(1), dim3(kFT), smem, s, x, Wr, b, T, H, E, k,
-                       TG, ids, w, counts, offsets, perm, inv, flags, quant, a16, ascale);
+    hipLaunchKernelGGL(front_kernel<MOE_BF16>, dim3(1), dim3(kFT), smem, s, P, KB, x, b, T, H, E,
+                       k, ids, w, counts, offsets, perm, inv, flags, quant, a16, ascale);
   else
-    hipLaunchKernelGGL(front_kernel<MOE_F32>, dim3(1), dim3(kFT), smem, s, x, Wr, b, T, H, E, k,
-                       TG, ids, w, counts, offsets, perm, inv, flags, quant, a16, ascale);
+    hipLaunchKernelGGL(front_kernel<MOE_F32>, dim3(1), dim3(kFT), smem, s, P, KB, x, b, T, H, E,
+                       k, ids, w, counts, offsets, perm, inv, flags, quant, a16, ascale);
   return hipGetLastError();
 }
 

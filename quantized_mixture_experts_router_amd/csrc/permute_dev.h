@@ -51,14 +51,22 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
   const int c0 = wave * chunk;
   const int c1 = min(R, c0 + chunk);
 
-  // 1. histograms
+  // 1. histograms (ids loaded kB per lane at a time, all in flight at once)
+  constexpr int kB = 8;
   uint32_t bad = 0u;
-  for (int a = c0 + lane; a < c1; a += 64) {
-    int e = ids[a];
-    if (e >= 0 && e < E)
-      atomicAdd(&base[wave * E + e], 1);
-    else
-      bad |= e == MOE_ID_NAN ? (uint32_t)MOE_FLAG_NAN_LOGIT : (uint32_t)MOE_FLAG_BAD_EXPERT_ID;
+  for (int a0 = c0; a0 < c1; a0 += 64 * kB) {
+    int ev[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) ev[u] = ids[min(a0 + 64 * u + lane, c1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (a0 + 64 * u + lane >= c1) break;
+      const int e = ev[u];
+      if (e >= 0 && e < E)
+        atomicAdd(&base[wave * E + e], 1);
+      else
+        bad |= e == MOE_ID_NAN ? (uint32_t)MOE_FLAG_NAN_LOGIT : (uint32_t)MOE_FLAG_BAD_EXPERT_ID;
+    }
   }
   if (bad) atomicOr(s_flags, bad);
   __syncthreads();
@@ -105,24 +113,32 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
   // 3. stable scatter
   const int bits = 32 - __clz(E > 1 ? E - 1 : 1);
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int p = c0; p < c1; p += 64) {
-    int a = p + lane;
-    int e = a < c1 ? ids[a] : -1;
-    bool valid = e >= 0 && e < E;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      uint64_t bb = __ballot(valid && ((e >> b) & 1));
-      m &= ((e >> b) & 1) ? bb : ~bb;
-    }
-    if (valid) {
-      int rank = __popcll(m & lt_mask);
-      int pos = base[wave * E + e] + rank;
-      perm[pos] = a / k;
-      inv[a] = pos;
-      bool last = (m >> lane) == 1ull;  // no same-expert lane above this one
-      if (last) base[wave * E + e] += rank + 1;
-    } else if (a < c1) {
-      inv[a] = -1;
+  for (int p0 = c0; p0 < c1; p0 += 64 * kB) {
+    int ev[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) ev[u] = ids[min(p0 + 64 * u + lane, c1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int p = p0 + 64 * u;
+      if (p >= c1) break;  // uniform: p is the same in every lane
+      const int a = p + lane;
+      const int e = a < c1 ? ev[u] : -1;
+      const bool valid = e >= 0 && e < E;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < bits; ++b) {
+        const uint64_t bb = __ballot(valid && ((e >> b) & 1));
+        m &= ((e >> b) & 1) ? bb : ~bb;
+      }
+      if (valid) {
+        const int rank = __popcll(m & lt_mask);
+        const int pos = base[wave * E + e] + rank;
+        perm[pos] = a / k;
+        inv[a] = pos;
+        const bool last = (m >> lane) == 1ull;  // no same-expert lane above this one
+        if (last) base[wave * E + e] += rank + 1;
+      } else if (a < c1) {
+        inv[a] = -1;
+      }
     }
   }
   __syncthreads();

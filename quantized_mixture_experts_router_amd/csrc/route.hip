@@ -1,54 +1,123 @@
-// Router kernel: logits + top-k + softmax over the selected logits for
-// blocks of 2..16 tokens (the arithmetic lives in route_dev.h).
+// Routing kernels: fp64 logits on the matrix cores (one block per 16-token
+// tile x expert group, its wavefronts splitting the hidden dimension), then
+// top-k + softmax with one wavefront per token. The arithmetic lives in
+// route_dev.h; the split plan (route_plan) in common.h.
 #include "route_dev.h"
 
 namespace moeq {
 
 namespace {
 
-constexpr int kThreads = 256;
-
-// Token groups per block (2 tokens each): as few as keep the grid near 1024
-// blocks (small batches spread the hidden dimension over every thread), but
-// enough that re-reading the router weights per block stays under ~256 MB of
-// L2 traffic (large E*H), and at most 8 (kTG * expert groups <= 256 threads).
-__host__ __device__ inline int route_tgroups(int T, int H, int E) {
-  int tg = 1;
-  while (tg < 8 && (T + 2 * tg - 1) / (2 * tg) > 1024) tg *= 2;
-  const double traffic = 2.0 * T * E * H;  // bytes of Wr reads with one group
-  while (tg < 8 && traffic / tg > 256e6) tg *= 2;
-  const int EG = (E + 7) / 8;
-  while (tg > 1 && tg * EG > 256) tg /= 2;
-  return tg;
+// Block = KS wavefronts over one (token tile, expert group, K block). Wave
+// ks accumulates chunks [c0 + ks*CPW, ...) of the block's K range; the KS
+// partial tiles meet in LDS and are added in wave order, and the block
+// stores the sum for its K block kb at P[kb][t][e].
+template <int XDT, int NTW>
+__global__ __launch_bounds__(1024) void route_logits_kernel(const void* __restrict__ x,
+                                                            const float* __restrict__ Wr, int T,
+                                                            int H, int E, int EG, int KS, int CPW,
+                                                            double* __restrict__ P) {
+  extern __shared__ double red[];  // [KS][NTW][4][64]
+  const int TT = (T + rt::kTT - 1) / rt::kTT;
+  const int NC = (H + 15) / 16;
+  const int eg = blockIdx.x % EG;
+  const int tt = (blockIdx.x / EG) % TT;
+  const int kb = blockIdx.x / (EG * TT);
+  const int ks = threadIdx.x / 64, lane = threadIdx.x & 63;
+  const int t0 = tt * rt::kTT, e0 = eg * NTW * 16;
+  const int c0 = (kb * KS + ks) * CPW, c1 = min(c0 + CPW, NC);
+  rt::f64x4 acc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) acc[j] = rt::f64x4{0.0, 0.0, 0.0, 0.0};
+  if (c0 < c1) rt::logits_acc<XDT, NTW>(x, Wr, T, H, E, t0, e0, c0, c1, acc);
+  double* out = P + (size_t)kb * T * E;
+  if (KS == 1) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * i + (lane >> 4), e = e0 + 16 * j + (lane & 15);
+        if (t < T && e < E) out[(size_t)t * E + e] = acc[j][i];
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((ks * NTW + j) * 4 + i) * 64 + lane] = acc[j][i];
+  __syncthreads();
+  for (int v = threadIdx.x; v < NTW * 4 * 64; v += KS * 64) {
+    const int l = v & 63, i = (v >> 6) & 3, j = v >> 8;
+    const int t = t0 + 4 * i + (l >> 4), e = e0 + 16 * j + (l & 15);
+    double sum = 0.0;
+    for (int q = 0; q < KS; ++q) sum += red[((q * NTW + j) * 4 + i) * 64 + l];
+    if (t < T && e < E) out[(size_t)t * E + e] = sum;
+  }
 }
 
+// Top-k + softmax, one wavefront per token.
+constexpr int kTopkThreads = 256;
+
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
+    const double* __restrict__ P, int KB, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ logits) {
+  const int t = blockIdx.x * (kTopkThreads / 64) + threadIdx.x / 64;
+  if (t < T) rt::topk_token(P, KB, bias, T, E, k, t, ids, w, logits);
+}
 
 template <int XDT>
-__global__ __launch_bounds__(kThreads) void route_kernel(
-    const void* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
-    int T, int H, int E, int k, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    float* __restrict__ logits_out) {
-  extern __shared__ double smem[];
-  const int TG = route_tgroups(T, H, E);
-  rt::route_group<XDT, kThreads>(x, Wr, bias, T, H, E, k, TG, blockIdx.x * TG * rt::kTM, ids_out,
-                                 w_out, logits_out, smem);
+hipError_t launch_logits_x(const void* x, const float* Wr, int T, int H, int E,
+                           const RoutePlan& p, double* P, hipStream_t s) {
+  const int TT = (T + rt::kTT - 1) / rt::kTT;
+  dim3 grid(TT * p.eg * p.kb), block(64 * p.ks);
+  const size_t smem = p.ks > 1 ? sizeof(double) * p.ks * p.ntw * 4 * 64 : 0;
+  switch (p.ntw) {
+    case 1:
+      hipLaunchKernelGGL((route_logits_kernel<XDT, 1>), grid, block, smem, s, x, Wr, T, H, E, p.eg,
+                         p.ks, p.cpw, P);
+      break;
+    case 2:
+      hipLaunchKernelGGL((route_logits_kernel<XDT, 2>), grid, block, smem, s, x, Wr, T, H, E, p.eg,
+                         p.ks, p.cpw, P);
+      break;
+    case 3:
+      hipLaunchKernelGGL((route_logits_kernel<XDT, 3>), grid, block, smem, s, x, Wr, T, H, E, p.eg,
+                         p.ks, p.cpw, P);
+      break;
+    default:
+      hipLaunchKernelGGL((route_logits_kernel<XDT, 4>), grid, block, smem, s, x, Wr, T, H, E, p.eg,
+                         p.ks, p.cpw, P);
+      break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
-                        int E, int k, int32_t* ids, float* w, float* logits, hipStream_t s) {
+hipError_t launch_route_logits(const void* x, int xdt, const float* Wr, int T, int H, int E,
+                               double* P, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int TG = route_tgroups(T, H, E), TB = TG * rt::kTM;
-  const size_t smem = sizeof(double) * rt::route_smem_doubles(kThreads, TG, E);
-  dim3 grid((T + TB - 1) / TB);
-  if (xdt == MOE_BF16)
-    hipLaunchKernelGGL(route_kernel<MOE_BF16>, grid, dim3(kThreads), smem, s, x, Wr, b, T, H, E, k,
-                       ids, w, logits);
-  else
-    hipLaunchKernelGGL(route_kernel<MOE_F32>, grid, dim3(kThreads), smem, s, x, Wr, b, T, H, E, k,
-                       ids, w, logits);
+  const RoutePlan p = route_plan(T, H, E);
+  return xdt == MOE_BF16 ? launch_logits_x<MOE_BF16>(x, Wr, T, H, E, p, P, s)
+                         : launch_logits_x<MOE_F32>(x, Wr, T, H, E, p, P, s);
+}
+
+hipError_t launch_route_topk(const double* P, int KB, const float* b, int T, int E, int k,
+                             int32_t* ids, float* w, float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + kTopkThreads / 64 - 1) / (kTopkThreads / 64));
+  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kTopkThreads), 0, s, P, KB, b, T, E, k, ids, w,
+                     logits);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
+                        int E, int k, int32_t* ids, float* w, float* logits, double* P,
+                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipError_t e = launch_route_logits(x, xdt, Wr, T, H, E, P, s);
+  if (e != hipSuccess) return e;
+  return launch_route_topk(P, route_plan(T, H, E).kb, b, T, E, k, ids, w, logits, s);
 }
 
 }  // namespace moeq

@@ -1,5 +1,6 @@
-// Router device code shared by the routing kernel and the fused small-batch
-// front kernel: fp64 logits of a group of tokens, top-k and softmax.
+// Router device code: fp64 logits on the matrix cores, and the per-token
+// top-k + softmax that the routing kernel and the fused small-batch front
+// kernel share.
 //
 // Method: Baidu Cloud article on quantized MoE LLM inference, "expert
 // routing" section (router linear -> top-k -> softmax over the top-k ->
@@ -10,12 +11,17 @@
 // with fp32 weights are exact in fp64 and the sum carries ~1e-16 relative
 // error, far below the 1e-6 gap at which a token counts as a near-tie.
 //
-// A group = TG x 2 tokens x all experts, computed by NT threads. Each thread
-// owns a 2-token x 8-expert register tile and a slice of the hidden
-// dimension: slices are 8 columns wide and interleaved, so neighbouring
-// lanes read neighbouring 16-/32-byte chunks of the same rows. Partial sums
-// meet through wavefront butterflies and LDS, then each wavefront runs the
-// top-k of its tokens with wave-wide (value desc, index asc) argmax rounds.
+// Logits. gfx950's fp64 matrix instruction (16x16x4, D = A B + C) runs the
+// contraction. A wavefront owns 16 tokens x NTW*16 experts over a range of
+// hidden-dimension chunks of 16 columns. In a chunk, lane (r = lane % 16,
+// g = lane / 16) loads columns [4g, 4g+4) of token row r and of expert row r
+// of each 16-expert tile; step s of the chunk then feeds column 4g + s as
+// k-index g of A (token r) and B (expert r). Any bijection between (step,
+// k-index) and columns gives the same dot products, and this one makes every
+// lane's loads contiguous 8/16-byte reads. Output: element i of lane l is
+// D[4i + l/16][l%16] (token 4i + g, expert r). Several waves may split the
+// hidden dimension; each writes its fp64 partial sums and the consumer adds
+// them in split order, so results do not depend on scheduling.
 #pragma once
 
 #include "common.h"
@@ -23,251 +29,198 @@
 namespace moeq {
 namespace rt {
 
-constexpr int kTM = 2;         // tokens per thread
-constexpr int kEM = 8;         // experts per thread
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTT = 16;  // tokens per wavefront tile
 constexpr int kInvalid = 0x7fffffff;
 
-// Raw operands of one 8-column slice: x of kTM tokens (bf16 pairs or fp32)
-// and Wr of kEM experts. Loaded for a whole batch of slices before any use,
-// so that a thread waits for memory once per batch.
-template <int XDT>
-struct Slice {
-  static constexpr int XW = XDT == MOE_BF16 ? 4 : 8;  // 32-bit words of x per token
-  uint32_t x[kTM][XW];
-  f32x4 w[kEM][2];
+// raw operands of one 16-column chunk for one lane
+template <int XDT, int NTW>
+struct Chunk {
+  static constexpr int XW = XDT == MOE_BF16 ? 2 : 4;  // 32-bit words of x (4 columns)
+  uint32_t x[XW];
+  f32x4 w[NTW];
 };
 
-template <int XDT>
-__device__ inline void load_slice(const void* x, const float* Wr, const int* trow, const int* erow,
-                                  int H, int h, Slice<XDT>& o) {
+template <int XDT, int NTW>
+__device__ inline void load_chunk(const void* x, const float* Wr, size_t xoff,
+                                  const size_t (&woff)[NTW], int col, Chunk<XDT, NTW>& o) {
+  if (XDT == MOE_BF16) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>((const uint16_t*)x + xoff + col);
+    o.x[0] = v[0];
+    o.x[1] = v[1];
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>((const float*)x + xoff + col);
 #pragma unroll
-  for (int i = 0; i < kTM; ++i) {
-    if (XDT == MOE_BF16) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)x + (size_t)trow[i] * H + h);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o.x[i][q] = v[q];
-    } else {
-      const u32x4* p = reinterpret_cast<const u32x4*>((const float*)x + (size_t)trow[i] * H + h);
-      const u32x4 a = p[0], b = p[1];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        o.x[i][q] = a[q];
-        o.x[i][4 + q] = b[q];
-      }
-    }
+    for (int q = 0; q < 4; ++q) o.x[q] = v[q];
   }
 #pragma unroll
-  for (int j = 0; j < kEM; ++j) {
-    const f32x4* wp = reinterpret_cast<const f32x4*>(Wr + (size_t)erow[j] * H + h);
-    o.w[j][0] = wp[0];
-    o.w[j][1] = wp[1];
-  }
+  for (int j = 0; j < NTW; ++j) o.w[j] = *reinterpret_cast<const f32x4*>(Wr + woff[j] + col);
 }
 
 template <int XDT>
-__device__ inline void fma_slice(const Slice<XDT>& o, double (&acc)[kTM][kEM]) {
-  double xv[kTM][8];
+__device__ inline float x_val(const uint32_t* xw, int s) {
+  if (XDT == MOE_BF16) return __uint_as_float(s & 1 ? (xw[s >> 1] & 0xffff0000u) : (xw[s >> 1] << 16));
+  return __uint_as_float(xw[s]);
+}
+
+template <int XDT, int NTW>
+__device__ inline void mma_chunk(const Chunk<XDT, NTW>& c, bool valid, f64x4 (&acc)[NTW]) {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int s = 0; s < 4; ++s) {
+    const double a = valid ? (double)x_val<XDT>(c.x, s) : 0.0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (XDT == MOE_BF16) {
-        xv[i][2 * q] = (double)__uint_as_float(o.x[i][q] << 16);
-        xv[i][2 * q + 1] = (double)__uint_as_float(o.x[i][q] & 0xffff0000u);
-      } else {
-        xv[i][q] = (double)__uint_as_float(o.x[i][q]);
-        xv[i][4 + q] = (double)__uint_as_float(o.x[i][4 + q]);
-      }
+    for (int j = 0; j < NTW; ++j) {
+      const double b = valid ? (double)c.w[j][s] : 0.0;
+      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[j], 0, 0, 0);
     }
-#pragma unroll
-  for (int j = 0; j < kEM; ++j) {
-    double wv[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wv[q] = (double)o.w[j][0][q];
-      wv[4 + q] = (double)o.w[j][1][q];
-    }
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[i][j] = fma(xv[i][q], wv[q], acc[i][j]);
   }
 }
 
-// hidden-dimension slices per (token group, expert group): the largest
-// power of two with KS * TG * EG <= NT
-__host__ __device__ inline int route_slices(int NT, int TG, int EG) {
-  int ks = 1;
-  while (2 * ks * TG * EG <= NT) ks *= 2;
-  return ks;
+// Adds to acc the products of tokens [t0, t0+16) x experts [e0, e0 + 16 NTW)
+// over the chunks [c0, c1) (c0 < c1); rows past T or E repeat the last row
+// (their sums are never stored).
+template <int XDT, int NTW>
+__device__ inline void logits_acc(const void* __restrict__ x, const float* __restrict__ Wr, int T,
+                                  int H, int E, int t0, int e0, int c0, int c1,
+                                  f64x4 (&acc)[NTW]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const size_t xoff = (size_t)min(t0 + r, T - 1) * H + 4 * g;
+  size_t woff[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) woff[j] = (size_t)min(e0 + 16 * j + r, E - 1) * H + 4 * g;
+  // a lane's columns 16c + 4g + [0,4) lie inside the row iff 16c + 4g < H
+  // (H is a multiple of 8); past the end the load is clamped and the
+  // operands are zeroed. Two chunks in flight: the loads of the next chunk
+  // go out before the current one is multiplied; an odd count ends with a
+  // zeroed chunk.
+  auto col_of = [&](int c) { return min(16 * min(c, c1 - 1), H - 4 - 4 * g); };
+  Chunk<XDT, NTW> ca, cb;
+  load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c0), ca);
+  for (int c = c0; c < c1; c += 2) {
+    load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c + 1), cb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiplies
+    mma_chunk<XDT, NTW>(ca, 16 * c + 4 * g < H, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c + 2), ca);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_chunk<XDT, NTW>(cb, c + 1 < c1 && 16 * (c + 1) + 4 * g < H, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// doubles of dynamic LDS that route_group needs
-__host__ __device__ inline int route_smem_doubles(int NT, int TG, int E) {
-  const int EG = (E + kEM - 1) / kEM;
-  const int KS = route_slices(NT, TG, EG);
-  const int NW = KS > 64 ? KS / 64 : 1;
-  return (NW > 1 ? NW * TG * EG * kTM * kEM : 0) + TG * kTM * (E + 1);
+// Order key of a candidate: the fp64 value's bits made monotone as an
+// unsigned integer, the low 8 bits replaced by 255 - e so that the maximum
+// key is the largest value and, among equal values, the lowest expert index.
+// Keys drop 8 of the 52 mantissa bits, so two values within ~2^-44 of each
+// other (relative) may be ordered by index rather than by value; such a pair
+// is a near-tie by orders of magnitude (gap < 1e-6) and never decides an id
+// that is compared exactly.
+__device__ inline uint64_t order_key(double v, int e) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  u = (u >> 63) ? ~u : (u | (1ull << 63));
+  return (u & ~0xFFull) | (uint64_t)(255 - e);
 }
 
-// Logits, top-k ids and softmax weights of tokens [t0, t0 + 2 TG) (those
-// below T), computed by the NT threads of the block. A token whose logits
-// include a NaN gets MOE_ID_NAN in every slot and weight 0. Ends with the
-// outputs written by the threads that own them (no trailing barrier).
-template <int XDT, int NT>
-__device__ void route_group(const void* __restrict__ x, const float* __restrict__ Wr,
-                            const float* __restrict__ bias, int T, int H, int E, int k, int TG,
-                            int t0, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                            float* __restrict__ logits_out, double* smem) {
-  const int tid = threadIdx.x;
-  const int TB = TG * kTM;
-  const int EG = (E + kEM - 1) / kEM;             // expert groups
-  const int KS = route_slices(NT, TG, EG);        // hidden-dimension slices
-  const int active = KS * TG * EG;                // threads with work (<= NT)
-  // lane -> (slice, token group, expert group); slice varies fastest
-  const int ks = tid % KS;
-  const int tg = (tid / KS) % TG;
-  const int eg = tid / (KS * TG);
-  const bool on = tid < active;
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  double acc[kTM][kEM];
-#pragma unroll
-  for (int i = 0; i < kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kEM; ++j) acc[i][j] = 0.0;
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-  if (on) {
-    int trow[kTM];
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const int t = t0 + tg * kTM + i;
-      trow[i] = t < T ? t : 0;
-    }
-    int erow[kEM];
-#pragma unroll
-    for (int j = 0; j < kEM; ++j) erow[j] = min(eg * kEM + j, E - 1);
-    // slices h = 8 ks + 8 KS i, i < ns, in pairs whose loads are all issued
-    // before either slice is used; an odd last slice on its own
-    const int ns = 8 * ks < H ? (H - 8 * ks + 8 * KS - 1) / (8 * KS) : 0;
-    int i = 0;
-    for (; i + 1 < ns; i += 2) {
-      Slice<XDT> s0, s1;
-      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * i, s0);
-      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * (i + 1), s1);
-      __builtin_amdgcn_sched_barrier(0);  // keep every load of the pair ahead of the FMAs
-      fma_slice<XDT>(s0, acc);
-      fma_slice<XDT>(s1, acc);
-    }
-    if (i < ns) {
-      Slice<XDT> s0;
-      load_slice<XDT>(x, Wr, trow, erow, H, 8 * ks + 8 * KS * i, s0);
-      fma_slice<XDT>(s0, acc);
-    }
-  }
+// Maximum of a key over the 64 lanes, returned to every lane (all lanes
+// active): DPP swaps within each 16-lane row (lane ^ 1, lane ^ 2, rotate by
+// 4 and 8), then lane ^ 16 and lane ^ 32.
+__device__ inline uint64_t wave_max_u64(uint64_t k) {
+  k = umax64(k, dpp_u64<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = umax64(k, dpp_u64<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = umax64(k, dpp_u64<0x124>(k));  // row_ror:4
+  k = umax64(k, dpp_u64<0x128>(k));  // row_ror:8
+  k = umax64(k, (uint64_t)__shfl_xor((unsigned long long)k, 16));
+  k = umax64(k, (uint64_t)__shfl_xor((unsigned long long)k, 32));
+  return k;
+}
 
-  // reduce the hidden slices. Slices of one (token group, expert group) are
-  // adjacent lanes (KS is a power of two): butterfly within the wavefront,
-  // then across wavefronts through LDS when KS > 64.
-  const int KW = KS < 64 ? KS : 64;  // slices per wavefront
-  if (KS > 1) {
+// Routing of token t by one wavefront (all 64 lanes active): lane l holds
+// the logits of experts l, l + 64, l + 128, l + 192 (those below E), each
+// the KB partial sums P[kb][t][e] added in kb order plus the bias, all
+// loaded up front. Then k rounds of a wave-wide argmax over the untaken
+// candidates; the softmax over the k winners' exact fp64 logits. A NaN
+// among the token's logits makes its routing undefined: every slot gets
+// MOE_ID_NAN and weight 0. logits_out (optional) receives the fp32 logits.
+__device__ inline void topk_token(const double* __restrict__ P, int KB, const float* __restrict__ bias,
+                                  int T, int E, int k, int t, int32_t* __restrict__ ids_out,
+                                  float* __restrict__ w_out, float* __restrict__ logits_out) {
+  const int lane = threadIdx.x & 63;
+  const size_t stride = (size_t)T * E;
+  const double* row = P + (size_t)t * E;
+  int ec[4];
+  double cand[4];
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kEM; ++j)
-        for (int off = 1; off < KW; off <<= 1) acc[i][j] += __shfl_xor(acc[i][j], off);
+  for (int j = 0; j < 4; ++j) {
+    ec[j] = min(lane + 64 * j, E - 1);
+    cand[j] = 0.0;
   }
-  const int NW = KS / KW;  // wavefronts per (token group, expert group)
-  double* part = smem;     // [group][i][j][NW]
-  if (NW > 1 && on && (ks % KW) == 0) {
+  // partials in batches of 4 (16 loads in flight), added in kb order
+  for (int q0 = 0; q0 < KB; q0 += 4) {
+    double pv[4][4];
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int j = 0; j < kEM; ++j)
-        part[(((size_t)(eg * TG + tg) * kTM + i) * kEM + j) * NW + ks / KW] = acc[i][j];
+      for (int j = 0; j < 4; ++j) pv[u][j] = row[(size_t)min(q0 + u, KB - 1) * stride + ec[j]];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (q0 + u < KB) cand[j] += pv[u][j];
   }
-  __syncthreads();
-  double* lg = smem + (NW > 1 ? (size_t)NW * TG * EG * kTM * kEM : 0);  // [TB][E+1]
-  if (NW > 1) {
-    const int nslots = TG * EG * kTM * kEM;
-    for (int slot = tid; slot < nslots; slot += NT) {
-      double v = 0.0;
-      for (int q = 0; q < NW; ++q) v += part[(size_t)slot * NW + q];
-      const int j = slot % kEM, i = (slot / kEM) % kTM, g = slot / (kEM * kTM);
-      const int tgi = g % TG, egi = g / TG;
-      const int e = egi * kEM + j, tt = tgi * kTM + i;
-      if (e < E) lg[tt * (E + 1) + e] = v;
+  bool nan_seen = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (bias) cand[j] += (double)bias[ec[j]];
+    const int e = lane + 64 * j;
+    if (e < E) {
+      nan_seen |= cand[j] != cand[j];
+      if (logits_out) logits_out[(size_t)t * E + e] = (float)cand[j];
     }
-  } else if (on && ks == 0) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kEM; ++j) {
-        const int e = eg * kEM + j;
-        if (e < E) lg[(tg * kTM + i) * (E + 1) + e] = acc[i][j];
-      }
   }
-  __syncthreads();
-  // bias; optional fp32 logits
-  for (int i = tid; i < TB * E; i += NT) {
-    const int tt = i / E, e = i % E;
-    double v = lg[tt * (E + 1) + e] + (bias ? (double)bias[e] : 0.0);
-    lg[tt * (E + 1) + e] = v;
-    if (logits_out && t0 + tt < T) logits_out[(size_t)(t0 + tt) * E + e] = (float)v;
+  uint32_t taken = 0;
+  double my_v = 0.0, top_v = 0.0;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+    double best_v = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      const uint64_t key = (e < E && !((taken >> j) & 1u)) ? order_key(cand[j], e) : 0ull;
+      if (key > best) {
+        best = key;
+        best_v = cand[j];
+      }
+    }
+    const uint64_t win = wave_max_u64(best);
+    const int wi = 255 - (int)(win & 0xFF);
+    const double wv = __shfl(best_v, wi & 63);  // the owner's exact logit
+    if (r == 0) top_v = wv;
+    if (lane == r) {
+      my_v = wv;
+      my_i = wi;
+    }
+    if ((wi & 63) == lane) taken |= 1u << (wi >> 6);
   }
-  __syncthreads();
-
-  // top-k: wavefront w handles tokens w, w + NT/64, ...
-  const int wave = tid / 64, lane = tid % 64;
-  const int EPL = (E + 63) / 64;  // candidates per lane (<= 4)
-  for (int tt = wave; tt < TB; tt += NT / 64) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    const double* row = lg + tt * (E + 1);
-    uint32_t taken = 0;
-    bool nan_seen = false;
-    double my_v = 0.0, top_v = 0.0;
-    int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-      double bv = 0.0;
-      int bi = kInvalid;
-      for (int j = 0; j < EPL; ++j) {
-        int e = lane + 64 * j;
-        if (e < E && !((taken >> j) & 1u)) {
-          double v = row[e];
-          if (v != v) nan_seen = true;
-          if (bi == kInvalid || v > bv) {  // increasing e: ties keep the lower index
-            bv = v;
-            bi = e;
-          }
-        }
-      }
+  const bool nan_row = __any(nan_seen);
+  const double ex = lane < k ? exp(my_v - top_v) : 0.0;
+  double den = ex;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        double ov = __shfl_xor(bv, off);
-        int oi = __shfl_xor(bi, off);
-        bool better = oi != kInvalid && (bi == kInvalid || ov > bv || (ov == bv && oi < bi));
-        if (better) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (r == 0) top_v = bv;
-      if (lane == r) {
-        my_v = bv;
-        my_i = bi;
-      }
-      if (bi != kInvalid && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    }
-    // a NaN anywhere in the row makes the whole routing of the token undefined
-    const bool nan_row = __any(nan_seen);
-    double ex = lane < k ? exp(my_v - top_v) : 0.0;
-    double den = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-    if (lane < k) {
-      ids_out[(size_t)t * k + lane] = nan_row ? MOE_ID_NAN : my_i;
-      w_out[(size_t)t * k + lane] = nan_row ? 0.f : (float)(ex / den);
-    }
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+  if (lane < k) {
+    ids_out[(size_t)t * k + lane] = nan_row ? MOE_ID_NAN : my_i;
+    w_out[(size_t)t * k + lane] = nan_row ? 0.f : (float)(ex / den);
   }
 }
 

@@ -49,24 +49,39 @@ def test_workspace_size_monotone():
 
 
 def _route(**kw):
-    a = dict(x=16, xdt=1, Wr=16, b=None, T=4, H=64, E=8, k=2, ids=16, w=16, logits=None)
+    a = dict(x=16, xdt=1, Wr=16, b=None, T=4, H=64, E=8, k=2, ids=16, w=16, logits=None,
+             ws=256, ws_bytes=1 << 20)
     a.update(kw)
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     return _lib.LIB.moe_route(p(a["x"]), a["xdt"], p(a["Wr"]), p(a["b"]), a["T"], a["H"], a["E"],
-                              a["k"], p(a["ids"]), p(a["w"]), p(a["logits"]), None)
+                              a["k"], p(a["ids"]), p(a["w"]), p(a["logits"]), p(a["ws"]),
+                              a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), -1), (dict(k=9), -1), (dict(E=0), -1), (dict(E=257, k=2), -1),
     (dict(H=60), -1), (dict(xdt=7), -1), (dict(x=None), -1), (dict(ids=None), -1),
-    (dict(x=17), -3), (dict(T=-1), -1), (dict(k=33, E=64), -1),
+    (dict(x=17), -3), (dict(T=-1), -1), (dict(k=33, E=64), -1), (dict(ws=None), -1),
+    (dict(ws=272), -3), (dict(ws_bytes=0), -4),
 ])
 def test_route_rejects(kw, status):
     assert _route(**kw) == status
 
 
 def test_route_empty_is_noop():
-    assert _route(T=0, x=None, ids=None, w=None) == 0
+    assert _route(T=0, x=None, ids=None, w=None, ws=None) == 0
+
+
+def test_route_workspace_size():
+    L = _lib.LIB
+    assert L.moe_route_workspace_size(0, 2048, 256) == 0
+    for T, H, E in ((1, 4096, 8), (64, 2048, 256), (4096, 2048, 256), (16, 8192, 64), (5, 136, 20)):
+        n = L.moe_route_workspace_size(T, H, E)
+        # at least the fp64 logits themselves, 256-byte granular
+        assert n >= T * E * 8 and n % 256 == 0
+        # the layer workspace holds the router's partial logits too
+        if H % 128 == 0:
+            assert moeq.workspace_size(T, H, 512, E, 2) >= n
 
 
 def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bits=None):

@@ -60,6 +60,51 @@ def test_route_parity(moeq, name, T, _):
     assert np.all(np.abs(logits - L) <= 1e-6 * np.maximum(1.0, np.abs(L)))
 
 
+# shapes chosen to reach every branch of the router's split plan: expert
+# tiles per wave 1..4, one or several waves per block (in-block K split),
+# several K blocks (partials summed by the top-k), H % 16 == 8 (half chunk),
+# T and E off the 16-row tiles
+PLAN_CASES = [
+    # T, H, E, k, x dtype, bias
+    (1, 4096, 8, 2, "bf16", False),      # 1 tile/wave, 16 waves/block, 4 K blocks
+    (5, 136, 20, 3, "f32", True),        # half last chunk, ragged T and E
+    (33, 264, 40, 4, "bf16", True),      # 3 expert groups, ragged everything
+    (16, 8192, 64, 2, "bf16", False),    # 8 K blocks
+    (2100, 1024, 256, 8, "bf16", True),  # 4 tiles/wave, in-block split of 4
+    (2048, 256, 48, 4, "f32", False),    # 3 tiles/wave
+    (2048, 128, 32, 2, "bf16", True),    # 2 tiles/wave
+    (4096, 64, 256, 6, "bf16", False),   # one wave per block, no split at all
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,xdt,with_bias", PLAN_CASES)
+def test_route_plan_shapes(moeq, T, H, E, k, xdt, with_bias):
+    _say(f"[route-plan] T={T} H={H} E={E} k={k} {xdt} bias={with_bias}")
+    rng = np.random.default_rng(T * 7 + H + E)
+    x = rng.standard_normal((T, H), dtype=np.float32)
+    Wr = (rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
+    b = (rng.standard_normal(E).astype(np.float32) * np.float32(0.5)) if with_bias else None
+    if xdt == "bf16":
+        bits = synth.f32_to_bf16_bits(x)
+        xt = x_to_torch(bits, "bf16")
+        x64 = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    else:
+        xt = torch.from_numpy(x).cuda()
+        x64 = x.astype(np.float64)
+    bt = torch.from_numpy(b).cuda() if b is not None else None
+    ids, w, logits = moeq.route(xt, torch.from_numpy(Wr).cuda(), bt, k, want_logits=True)
+    torch.cuda.synchronize()
+    L = oracle.router_logits(x64, Wr, b)
+    rids, rw, gap, flagged = oracle.topk_softmax(L, k)
+    ids, w, logits = ids.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy()
+    ok = ~flagged
+    assert ok.sum() >= 0.9 * T
+    np.testing.assert_array_equal(ids[ok], rids[ok])
+    assert np.max(np.abs(w[ok] - rw[ok])) <= 1e-6
+    # fp32 logits are the fp64 sums rounded once (to within an fp32 ulp)
+    assert np.all(np.abs(logits - L) <= 2.0 ** -23 * np.abs(L) + 1e-30)
+
+
 def test_route_ties_and_bias_closed_form(moeq):
     """Zero router weights: all logits tie -> ids 0..k-1, w = 1/k; a ramp bias
     -> ids E-1, E-2, ... with the closed-form softmax."""
