@@ -173,15 +173,21 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
                      int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
                      float* logits, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes moe_permute needs: the 256-byte flag block, plus, for
+ * more than 8192 assignments, per-block expert counts of the multi-block
+ * sort (0 on invalid sizes). Host only. */
+size_t moe_permute_workspace_size(int T, int k, int E);
+
 /* Stable counting sort of the T*k assignments a = t*k + j by expert.
  * topk_ids (device) int32 [T,k]. Outputs (device, int32): counts [E],
  * offsets [E+1] (exclusive prefix sum, offsets[E] = T*k), perm_token [T*k]
  * (token of the r-th sorted assignment; ascending token inside each
- * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: at least 256
- * bytes, 256-byte aligned (its first word is the flag word).
+ * expert's segment), inv [T*k] (inv[a] = r). ws/ws_bytes: at least
+ * moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned; its first
+ * word is the flag word, the rest scratch.
  * Ids outside [0,E) are dropped (inv = -1): MOE_ID_NAN raises
  * MOE_FLAG_NAN_LOGIT, any other MOE_FLAG_BAD_EXPERT_ID. The flag word is
- * written with exactly the bits this call found. */
+ * written with exactly the bits this call found. T*k <= 2^30. */
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
                        size_t ws_bytes, void* stream);

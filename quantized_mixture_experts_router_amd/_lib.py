@@ -59,6 +59,7 @@ _SIGS = {
     "moe_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
     "moe_route_workspace_size": ([_i, _i, _i], _sz),
     "moe_route": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_permute_workspace_size": ([_i, _i, _i], _sz),
     "moe_permute": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_format_mask": ([ctypes.POINTER(PackedExpertC), _i], ctypes.c_uint32),
     "moe_grouped_ffn_q": ([_vp, _i, _vp, ctypes.c_uint32, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
@@ -245,7 +246,8 @@ def permute(ids, E, ws=None):
     perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
     inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
     if ws is None:
-        ws = torch.empty(256, dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, int(LIB.moe_permute_workspace_size(T, k, E))), dtype=torch.uint8,
+                         device=dev)
     _check(LIB.moe_permute(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
                            _ptr(ws), ws.numel(), _stream()), "moe_permute")
     return counts, offsets, perm[:T * k], inv[:T * k], ws

@@ -217,17 +217,24 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
                                  (double*)ws, (hipStream_t)stream));
 }
 
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (T < 0 || k < 1 || E <= 0 || (long)T * k > (1L << 30)) return 0;
+  return 256 + permute_plan(T * k, E).scratch_bytes;
+}
+
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv, void* ws,
                        size_t ws_bytes, void* stream) {
   if (T < 0 || E <= 0 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if ((long)T * k > (1L << 30)) return MOE_ERR_INVALID_ARG;
   if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !perm_token || !inv)) return MOE_ERR_INVALID_ARG;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (ws_bytes < 256) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_permute_workspace_size(T, k, E)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* flags = (uint32_t*)ws;
-  MOE_TRY(launch_permute(topk_ids, T, k, E, counts, offsets, perm_token, inv, flags, s));
+  MOE_TRY(launch_permute(topk_ids, T, k, E, counts, offsets, perm_token, inv, flags,
+                         (char*)ws + 256, s));
   return MOE_OK;
 }
 
@@ -338,7 +345,8 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
                          (float*)ws_at(ws, L.ascale), s));
   } else {
     MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
-    MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags, s));
+    MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags,
+                           ws_at(ws, L.pscratch), s));
     st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
     if (st != MOE_OK) return st;
   }

@@ -99,6 +99,8 @@ struct WsLayout {
   size_t yp;       // f32 [splits, T*k, H] down-projection (partial) sums
   size_t rpart;    // f64 [kb, T, E] router partial logits; aliases yp (routing ends
                    // before the down projection writes it)
+  size_t pscratch; // permutation scratch; aliases yp too (the top-k has read the
+                   // partial logits before the permutation runs)
   size_t total;
   int splits;
   bool decode;
@@ -157,6 +159,16 @@ inline RoutePlan route_plan(int T, int H, int E) {
   return p;
 }
 
+// permutation: one block up to kPermuteSingleMax assignments, else
+// histogram / scan / scatter kernels over `blocks` blocks of `chunk`
+// assignments with scratch_bytes of device scratch (256-aligned)
+constexpr int kPermuteSingleMax = 8192;
+struct PermutePlan {
+  int blocks, chunk;
+  size_t scratch_bytes;
+};
+PermutePlan permute_plan(int R, int E);
+
 inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   WsLayout L;
   size_t R = (size_t)T * k;
@@ -178,8 +190,12 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   L.decode = use_decode_path(T, k, E);
   const size_t yp_bytes = (size_t)L.splits * R * H * 4;
   const size_t rp_bytes = route_plan(T, H, E).part_bytes;
-  L.yp = take(yp_bytes > rp_bytes ? yp_bytes : rp_bytes);
+  const size_t ps_bytes = permute_plan((int)R, E).scratch_bytes;
+  size_t big = yp_bytes > rp_bytes ? yp_bytes : rp_bytes;
+  big = big > ps_bytes ? big : ps_bytes;
+  L.yp = take(big);
   L.rpart = L.yp;
+  L.pscratch = L.yp;
   L.total = o;
   return L;
 }
@@ -206,7 +222,7 @@ hipError_t launch_front(const double* P, int KB, const void* x, int xdt, const f
                         f16* a16, float* ascale, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
-                          hipStream_t s);
+                          void* scratch, hipStream_t s);
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
                            int quant, f16* a16, float* ascale, hipStream_t s);
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,

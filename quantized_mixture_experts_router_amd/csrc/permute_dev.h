@@ -7,13 +7,15 @@
 // library's choice: ascending token inside each expert, which makes the
 // permutation unique and reproducible run to run.
 //
-// One block of 16 waves (permute_block): wave w owns a contiguous chunk of
-// assignments.
-//  1. per-wave expert histograms (LDS);
-//  2. counts, offsets and per-(wave, expert) bases by prefix sums;
-//  3. each wave walks its chunk 64 assignments at a time; a lane's rank among
-//     earlier lanes with the same expert comes from ballots over the expert
-//     id bits, so equal experts keep their assignment order.
+// Building blocks, each run by one wavefront over a contiguous slice of
+// assignments (ids loaded kB per lane at a time, all in flight at once):
+//  - wave_hist: per-expert counts of the slice into an LDS histogram;
+//  - wave_scatter: walks the slice 64 assignments at a time; a lane's rank
+//    among earlier lanes with the same expert comes from ballots over the
+//    expert id bits, so equal experts keep their assignment order, and the
+//    per-expert running bases (LDS) advance by the counts.
+// permute_block sorts everything with one block; the multi-block kernels in
+// permute.hip split the assignments over blocks with the same pieces.
 #pragma once
 
 #include "common.h"
@@ -21,38 +23,20 @@
 namespace moeq {
 namespace pm {
 
-constexpr int kWaves = 16;  // the permutation kernel's block
+constexpr int kWaves = 16;  // the single-block permutation kernel's block
 constexpr int kThreads = kWaves * 64;
+constexpr int kB = 8;       // ids per lane in flight
 
-// int32 words of dynamic LDS that permute_block<W> needs
-__host__ __device__ inline int permute_smem_words(int W, int E) { return W * E + W * 64 + 1; }
+// flag bits of an id outside [0, E)
+__device__ inline uint32_t bad_bits(int e) {
+  return e == MOE_ID_NAN ? (uint32_t)MOE_FLAG_NAN_LOGIT : (uint32_t)MOE_FLAG_BAD_EXPERT_ID;
+}
 
-// Stable counting sort of the R = T*k assignments by the W * 64 threads of
-// the block. Returns (to every thread) the flag bits found: ids equal to
-// MOE_ID_NAN raise MOE_FLAG_NAN_LOGIT, any other id outside [0,E)
-// MOE_FLAG_BAD_EXPERT_ID; such assignments get inv = -1 and no row.
-template <int W>
-__device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R, int k, int E,
-                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                  int32_t* sm) {
-  constexpr int NTH = W * 64;
-  int32_t* base = sm;                       // [W][E]
-  int32_t* scan = sm + W * E;          // [NTH] scan scratch
-  uint32_t* s_flags = (uint32_t*)(scan + NTH);
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-
-  if (tid == 0) *s_flags = 0u;
-  for (int i = tid; i < W * E; i += NTH) base[i] = 0;
-  __syncthreads();
-
-  const int chunk = ((R + W - 1) / W + 63) / 64 * 64;
-  const int c0 = wave * chunk;
-  const int c1 = min(R, c0 + chunk);
-
-  // 1. histograms (ids loaded kB per lane at a time, all in flight at once)
-  constexpr int kB = 8;
+// Adds the expert counts of assignments [c0, c1) to hist[E] (LDS); returns
+// (per lane) the flag bits of the ids outside [0, E).
+__device__ inline uint32_t wave_hist(const int32_t* __restrict__ ids, int c0, int c1, int E,
+                                     int32_t* hist) {
+  const int lane = threadIdx.x & 63;
   uint32_t bad = 0u;
   for (int a0 = c0; a0 < c1; a0 += 64 * kB) {
     int ev[kB];
@@ -63,54 +47,21 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
       if (a0 + 64 * u + lane >= c1) break;
       const int e = ev[u];
       if (e >= 0 && e < E)
-        atomicAdd(&base[wave * E + e], 1);
+        atomicAdd(&hist[e], 1);
       else
-        bad |= e == MOE_ID_NAN ? (uint32_t)MOE_FLAG_NAN_LOGIT : (uint32_t)MOE_FLAG_BAD_EXPERT_ID;
+        bad |= bad_bits(e);
     }
   }
-  if (bad) atomicOr(s_flags, bad);
-  __syncthreads();
+  return bad;
+}
 
-  // 2. per-expert totals (thread e loops over waves), then exclusive scan
-  const int EPT = (E + NTH - 1) / NTH;  // experts per thread (1 for E <= 1024)
-  int local_total = 0;
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    if (e < E) {
-      int run = 0;
-      for (int w = 0; w < W; ++w) {
-        int c = base[w * E + e];
-        base[w * E + e] = run;
-        run += c;
-      }
-      counts[e] = run;
-      local_total += run;
-    }
-  }
-  scan[tid] = local_total;
-  __syncthreads();
-  for (int off = 1; off < NTH; off <<= 1) {
-    int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int excl = scan[tid] - local_total;
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    if (e < E) {
-      int c = 0;
-      for (int w = 0; w < W; ++w) base[w * E + e] += excl;
-      offsets[e] = excl;
-      // counts[e] was written above; recompute the running prefix
-      c = counts[e];
-      excl += c;
-    }
-  }
-  if (tid == NTH - 1) offsets[E] = scan[NTH - 1];
-  __syncthreads();
-
-  // 3. stable scatter
+// Stable scatter of assignments [c0, c1): row base[e] + rank for the r-th
+// assignment of expert e in the slice (base[] in LDS, advanced as it goes).
+// Assignment a belongs to token a / k. Ids outside [0, E) get inv = -1.
+__device__ inline void wave_scatter(const int32_t* __restrict__ ids, int c0, int c1, int E, int k,
+                                    int32_t* base, int32_t* __restrict__ perm,
+                                    int32_t* __restrict__ inv) {
+  const int lane = threadIdx.x & 63;
   const int bits = 32 - __clz(E > 1 ? E - 1 : 1);
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int p0 = c0; p0 < c1; p0 += 64 * kB) {
@@ -131,16 +82,101 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
       }
       if (valid) {
         const int rank = __popcll(m & lt_mask);
-        const int pos = base[wave * E + e] + rank;
+        const int pos = base[e] + rank;
         perm[pos] = a / k;
         inv[a] = pos;
         const bool last = (m >> lane) == 1ull;  // no same-expert lane above this one
-        if (last) base[wave * E + e] += rank + 1;
+        if (last) base[e] += rank + 1;
       } else if (a < c1) {
         inv[a] = -1;
       }
     }
   }
+}
+
+// In-block exclusive scan of one int per thread (NTH threads, scan[NTH] in
+// LDS); returns the thread's exclusive prefix, and the total in *total.
+template <int NTH>
+__device__ inline int block_excl_scan(int v, int* scan, int* total) {
+  const int tid = threadIdx.x;
+  scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < NTH; off <<= 1) {
+    const int o = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += o;
+    __syncthreads();
+  }
+  const int incl = scan[tid];
+  *total = scan[NTH - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// int32 words of dynamic LDS that permute_block<W> needs
+__host__ __device__ inline int permute_smem_words(int W, int E) { return W * E + W * 64 + 1; }
+
+// Stable counting sort of the R = T*k assignments by the W * 64 threads of
+// the block. Returns (to every thread) the flag bits found: ids equal to
+// MOE_ID_NAN raise MOE_FLAG_NAN_LOGIT, any other id outside [0,E)
+// MOE_FLAG_BAD_EXPERT_ID; such assignments get inv = -1 and no row.
+template <int W>
+__device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R, int k, int E,
+                                         int32_t* __restrict__ counts,
+                                         int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                         int32_t* __restrict__ inv, int32_t* sm) {
+  constexpr int NTH = W * 64;
+  int32_t* base = sm;              // [W][E]
+  int32_t* scan = sm + W * E;      // [NTH] scan scratch
+  uint32_t* s_flags = (uint32_t*)(scan + NTH);
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+
+  if (tid == 0) *s_flags = 0u;
+  for (int i = tid; i < W * E; i += NTH) base[i] = 0;
+  __syncthreads();
+
+  const int chunk = ((R + W - 1) / W + 63) / 64 * 64;
+  const int c0 = wave * chunk;
+  const int c1 = min(R, c0 + chunk);
+
+  // 1. per-wave histograms
+  const uint32_t bad = wave_hist(ids, c0, c1, E, base + wave * E);
+  if (bad) atomicOr(s_flags, bad);
+  __syncthreads();
+
+  // 2. per-expert totals (thread e loops over waves; the wave bases become
+  //    prefixes over the waves), then the exclusive scan over experts
+  const int EPT = (E + NTH - 1) / NTH;  // experts per thread (1 for E <= 1024)
+  int local_total = 0;
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid * EPT + q;
+    if (e < E) {
+      int run = 0;
+      for (int w = 0; w < W; ++w) {
+        const int c = base[w * E + e];
+        base[w * E + e] = run;
+        run += c;
+      }
+      counts[e] = run;
+      local_total += run;
+    }
+  }
+  int total;
+  int excl = block_excl_scan<NTH>(local_total, scan, &total);
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid * EPT + q;
+    if (e < E) {
+      for (int w = 0; w < W; ++w) base[w * E + e] += excl;
+      offsets[e] = excl;
+      excl += counts[e];
+    }
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+
+  // 3. stable scatter
+  wave_scatter(ids, c0, c1, E, k, base + wave * E, perm, inv);
   __syncthreads();
   return *s_flags;
 }

@@ -84,6 +84,23 @@ def test_route_workspace_size():
             assert moeq.workspace_size(T, H, 512, E, 2) >= n
 
 
+def test_permute_workspace_size():
+    L = _lib.LIB
+    # one block (the flag block only) up to 8192 assignments, then per-block counts
+    assert L.moe_permute_workspace_size(4096, 2, 8) == 256
+    assert L.moe_permute_workspace_size(8192, 1, 256) == 256
+    assert L.moe_permute_workspace_size(8193, 1, 256) > 256
+    big = L.moe_permute_workspace_size(4096, 8, 256)
+    assert big >= 256 + 16 * 256 * 4
+    assert L.moe_permute_workspace_size(-1, 2, 8) == 0
+    # the layer workspace holds it (the layer may be driven through the split calls)
+    assert moeq.workspace_size(4096, 2048, 512, 256, 8) >= big
+    # a workspace big enough for the flag word only is refused above one block
+    p = ctypes.c_void_p(256)
+    assert L.moe_permute(p, 4096, 8, 256, p, p, p, p, p, 256, None) == -4
+    assert L.moe_permute(p, 1 << 20, 1 << 11, 256, p, p, p, p, p, 1 << 30, None) == -1
+
+
 def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bits=None):
     q = lambda r, c, b: _lib.QMatC(fmt, b, group, r, c, codes, params)
     return _lib.ExpertCanonC(q(I, H, bits), q(I, H, bits), q(H, I, down_bits or bits))

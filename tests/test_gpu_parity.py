@@ -126,6 +126,7 @@ PERM_CASES = [
     (1, 2, 8, "random"), (0, 2, 8, "random"), (33, 2, 8, "random"), (1000, 6, 256, "random"),
     (4096, 8, 256, "random"), (2048, 2, 8, "one_expert"), (5000, 8, 64, "skewed"),
     (16384, 2, 64, "random"), (300, 1, 1, "random"), (777, 32, 256, "random"),
+    (8192, 1, 8, "random"), (4097, 2, 8, "one_expert"), (100000, 8, 256, "skewed"),
 ]
 
 
@@ -157,6 +158,31 @@ def test_permute_flags_bad_ids(moeq):
     torch.cuda.synchronize()
     assert moeq.read_flags(ws) & moeq.FLAG_BAD_EXPERT_ID
     assert counts.sum().item() == 4
+
+
+@pytest.mark.parametrize("T,k", [(8193, 1), (3000, 8)])
+def test_permute_multiblock_flags_and_drops(moeq, T, k):
+    """Above one block's share: bad and NaN ids in different blocks are
+    dropped (inv = -1), both flags are raised, the rest sorts as the oracle."""
+    E = 64
+    rng = np.random.default_rng(T + k)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[5, 0] = E + 3                # bad id in the first block
+    ids[T - 2, k - 1] = moeq.ID_NAN  # NaN sentinel in the last block
+    counts, offsets, perm, inv, ws = moeq.permute(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    flags = moeq.read_flags(ws)
+    assert flags & moeq.FLAG_BAD_EXPERT_ID and flags & moeq.FLAG_NAN_LOGIT
+    # dropping an assignment = sorting it into an extra trailing expert E and
+    # cutting that segment off: rows of the real experts are unchanged
+    bad = (ids < 0) | (ids >= E)
+    rc, ro, rp, ri = oracle.canonical_permute(np.where(bad, E, ids), E + 1)
+    n = int(ro[E])
+    ri = np.where(bad.reshape(-1), -1, ri)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc[:E])
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro[:E + 1])
+    np.testing.assert_array_equal(perm.cpu().numpy()[:n], rp[:n])
+    np.testing.assert_array_equal(inv.cpu().numpy(), ri)
 
 
 # --------------------------------------------------------------------------- int8
