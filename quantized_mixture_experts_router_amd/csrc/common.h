@@ -130,11 +130,11 @@ inline int down_splits(int T, int H, int I, int E, int k) {
 // block per (16-token tile, group of ntw 16-expert tiles, K block); the
 // block's ks wavefronts split the K block's 16-column chunks, cpw chunks
 // each. K is split ks * kb ways in all, as few as give about
-// MOEQ_ROUTE_WAVES wavefronts (two per SIMD) with >= 4 chunks per wave;
+// MOEQ_ROUTE_WAVES wavefronts (four per SIMD) with >= 4 chunks per wave;
 // expert tiles per wave drop below 4 first when the batch is too small for
 // that. kb > 1 leaves kb fp64 partial logits [kb][T][E] for the top-k to add.
 #ifndef MOEQ_ROUTE_WAVES
-#define MOEQ_ROUTE_WAVES 2048
+#define MOEQ_ROUTE_WAVES 4096
 #endif
 struct RoutePlan {
   int ntw, eg, ks, kb, cpw;

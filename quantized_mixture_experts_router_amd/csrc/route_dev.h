@@ -34,7 +34,8 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kTT = 16;  // tokens per wavefront tile
 constexpr int kInvalid = 0x7fffffff;
 
-// raw operands of one 16-column chunk for one lane
+// raw operands of one 16-column chunk for one lane: a token row, NTW
+// expert rows
 template <int XDT, int NTW>
 struct Chunk {
   static constexpr int XW = XDT == MOE_BF16 ? 2 : 4;  // 32-bit words of x (4 columns)
@@ -64,22 +65,26 @@ __device__ inline float x_val(const uint32_t* xw, int s) {
   return __uint_as_float(xw[s]);
 }
 
-template <int XDT, int NTW>
+// the four k-steps of one chunk; CHECK: zero the operands of a lane whose
+// columns lie past the row end (or of a chunk past the range)
+template <int XDT, int NTW, bool CHECK>
 __device__ inline void mma_chunk(const Chunk<XDT, NTW>& c, bool valid, f64x4 (&acc)[NTW]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const double a = valid ? (double)x_val<XDT>(c.x, s) : 0.0;
+    double a = (double)x_val<XDT>(c.x, s);
+    if (CHECK && !valid) a = 0.0;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const double b = valid ? (double)c.w[j][s] : 0.0;
+      double b = (double)c.w[j][s];
+      if (CHECK && !valid) b = 0.0;
       acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[j], 0, 0, 0);
     }
   }
 }
 
-// Adds to acc the products of tokens [t0, t0+16) x experts [e0, e0 + 16 NTW)
-// over the chunks [c0, c1) (c0 < c1); rows past T or E repeat the last row
-// (their sums are never stored).
+// Adds to acc the products of tokens [t0, t0 + 16) x experts
+// [e0, e0 + 16 NTW) over the chunks [c0, c1) (c0 < c1); rows past T or E
+// repeat the last row (their sums are never stored).
 template <int XDT, int NTW>
 __device__ inline void logits_acc(const void* __restrict__ x, const float* __restrict__ Wr, int T,
                                   int H, int E, int t0, int e0, int c0, int c1,
@@ -89,23 +94,30 @@ __device__ inline void logits_acc(const void* __restrict__ x, const float* __res
   size_t woff[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) woff[j] = (size_t)min(e0 + 16 * j + r, E - 1) * H + 4 * g;
-  // a lane's columns 16c + 4g + [0,4) lie inside the row iff 16c + 4g < H
-  // (H is a multiple of 8); past the end the load is clamped and the
-  // operands are zeroed. Two chunks in flight: the loads of the next chunk
-  // go out before the current one is multiplied; an odd count ends with a
-  // zeroed chunk.
+  // A lane's columns 16c + 4g + [0,4) lie inside the row iff 16c + 4g < H
+  // (H is a multiple of 8): every chunk below H / 16 is whole. Pairs of
+  // whole chunks run without checks, two in flight (the loads of the next
+  // go out before the current one is multiplied); what is left (a half
+  // chunk, an odd chunk) runs with them.
   auto col_of = [&](int c) { return min(16 * min(c, c1 - 1), H - 4 - 4 * g); };
+  const int cw = min(c1, H / 16);  // end of the whole chunks
   Chunk<XDT, NTW> ca, cb;
   load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c0), ca);
-  for (int c = c0; c < c1; c += 2) {
+  int c = c0;
+  for (; c + 1 < cw; c += 2) {
     load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c + 1), cb);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiplies
-    mma_chunk<XDT, NTW>(ca, 16 * c + 4 * g < H, acc);
+    mma_chunk<XDT, NTW, false>(ca, true, acc);
     __builtin_amdgcn_sched_barrier(0);
     load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c + 2), ca);
     __builtin_amdgcn_sched_barrier(0);
-    mma_chunk<XDT, NTW>(cb, c + 1 < c1 && 16 * (c + 1) + 4 * g < H, acc);
+    mma_chunk<XDT, NTW, false>(cb, true, acc);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // ca holds chunk c (clamped) here
+  for (; c < c1; ++c) {
+    mma_chunk<XDT, NTW, true>(ca, 16 * c + 4 * g < H, acc);
+    if (c + 1 < c1) load_chunk<XDT, NTW>(x, Wr, xoff, woff, col_of(c + 1), ca);
   }
 }
 
