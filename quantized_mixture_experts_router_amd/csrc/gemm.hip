@@ -22,7 +22,10 @@
 //    swizzled for the 64-bank LDS, three buffers for 4-bit tiles) and is
 //    shared by the 4 wavefronts, each of which streams its own weight rows
 //    into registers and decodes step s+1 while the MFMAs of step s run; two
-//    blocks share a CU so one block's decode overlaps the other's MFMAs.
+//    blocks share a CU so one block's decode overlaps the other's MFMAs. The
+//    pipeline is specialised on the number of 32-row sub-tiles holding rows,
+//    so a partial last m-tile costs only its own MFMAs, and each XCD runs
+//    its full m-tiles before its partial ones (longest first).
 // Every kernel is instantiated per block format; a launch handles the experts
 // of its format. Tasks are (expert, n-tile, m-tile), expert-major, so blocks
 // that share weight tiles run together; each block derives its task from the
@@ -35,6 +38,11 @@ namespace moeq {
 namespace {
 
 constexpr int kThreads = 256;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 template <int FID>
 struct FmtOf;
@@ -87,8 +95,8 @@ __device__ inline int expert_fid(const moe_packed_expert* experts, int e) {
   return fmt_id(w & 0xff, (w >> 8) & 0xff, w >> 16);
 }
 
-// Task lookup over the experts of format `fid`: tasks of expert e =
-// ceil(count_e / BM) * NB, expert-major, then n-tile, then m-tile.
+// Task lookup over the experts of format `fid` (decode): tasks of expert e
+// = ceil(count_e / BM) * NB, expert-major, then n-tile, then m-tile.
 // The first block also flags experts with rows whose format is not in the
 // launch mask (their rows would otherwise be left uncomputed).
 template <bool GU>
@@ -138,6 +146,103 @@ __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task
       s_res[3] = rel / mt;
     }
     start += ntk[q];
+  }
+  __syncthreads();
+  task.e = s_res[0];
+  task.row0 = s_res[1];
+  task.mcount = s_res[2];
+  task.nt = s_res[3];
+  return task.e >= 0;
+}
+
+// Task lookup of the prefill kernel for block b, longest tasks first on each
+// XCD. Tasks are split into full m-tiles (count_e / BM per expert and
+// n-tile) and partial last m-tiles (one per expert and n-tile when count_e
+// is not a multiple of BM), each list expert-major, then n-tile, then m-tile.
+// Blocks are dealt round-robin to the 8 XCDs; XCD x takes a contiguous
+// share of the full list, then a contiguous share of the partial list, in
+// slot order, so blocks sharing weight tiles share an L2 and the short
+// partial tiles run last, filling the tail of the launch. The grid needs 16
+// blocks more than there are tasks (spare blocks find nothing and exit).
+template <bool GU>
+__device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, Task& task) {
+  __shared__ int s_wsum[2][16];  // up to 1024 threads
+  __shared__ int s_res[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  if (tid == 0) s_res[0] = -1;
+  int cnt[2], nfu[2], npa[2];
+  int lf = 0, lp = 0;
+  bool missing = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    int c = 0, f = -1;
+    if (e < a.E) {
+      c = a.offsets[e + 1] - a.offsets[e];
+      f = expert_fid<GU>(a.experts, e);
+      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
+    }
+    cnt[q] = c;
+    nfu[q] = f == fid ? (c / BM) * NB : 0;
+    npa[q] = f == fid && c % BM ? NB : 0;
+    lf += nfu[q];
+    lp += npa[q];
+  }
+  if (missing && blockIdx.x == 0 && a.flags)
+    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  int incf = lf, incp = lp;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int vf = __shfl_up(incf, off), vp = __shfl_up(incp, off);
+    if (lane >= off) {
+      incf += vf;
+      incp += vp;
+    }
+  }
+  if (lane == 63) {
+    s_wsum[0][wave] = incf;
+    s_wsum[1][wave] = incp;
+  }
+  __syncthreads();
+  int sf = incf - lf, sp = incp - lp, F = 0, P = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    if (w < wave) {
+      sf += s_wsum[0][w];
+      sp += s_wsum[1][w];
+    }
+    F += s_wsum[0][w];
+    P += s_wsum[1][w];
+  }
+  // this block's place: XCD x, slot s; the XCD's shares of the two lists
+  const int x = b & 7, slot = b >> 3;
+  const int qf = F >> 3, rf = F & 7, qp = P >> 3, rp = P & 7;
+  const int nf = qf + (x < rf ? 1 : 0);
+  const int bf = x * qf + min(x, rf);
+  // the partial list's extras go to the last XCDs (the full list's to the
+  // first), so no XCD takes two
+  const int np = qp + (x >= 8 - rp ? 1 : 0);
+  const int bp = x * qp + max(0, x - (8 - rp));
+  const bool full = slot < nf;
+  const int L = full ? bf + slot : bp + (slot - nf);
+  if (full || slot - nf < np) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      const int st = full ? sf : sp;
+      const int n = full ? nfu[q] : npa[q];
+      if (L >= st && L < st + n) {
+        const int rel = L - st;
+        const int mf = cnt[q] / BM;  // full m-tiles of the expert
+        const int mi = full ? rel % mf : mf;
+        s_res[0] = e;
+        s_res[1] = a.offsets[e] + mi * BM;
+        s_res[2] = min(BM, cnt[q] - mi * BM);
+        s_res[3] = full ? rel / mf : rel;
+      }
+      sf += nfu[q];
+      sp += npa[q];
+    }
   }
   __syncthreads();
   task.e = s_res[0];
@@ -335,14 +440,6 @@ constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 // streaming its own 64 weight rows (one block per CU at 8)
 constexpr int kPW = MOEQ_PF_WAVES;
 
-__device__ inline int xcd_remap(int b, int nblk) {
-  // blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous
-  // range of tasks so that blocks sharing weight tiles share an L2
-  const int xcd = b & 7, slot = b >> 3;
-  const int q = nblk >> 3, r = nblk & 7;
-  return xcd * q + min(xcd, r) + slot;
-}
-
 template <class F, bool GU>
 __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs a) {
   // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
@@ -365,7 +462,7 @@ __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs 
   const int NU = a.N / (GU ? 32 : 64);
   const int NB = (NU + kPW - 1) / kPW;
   Task t;
-  if (!find_task<GU>(a, F::ID, kBM, NB, xcd_remap(blockIdx.x, gridDim.x), t)) return;
+  if (!find_task_lpt<GU>(a, F::ID, kBM, NB, blockIdx.x, t)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, kh = lane >> 5;
@@ -417,139 +514,155 @@ __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs 
     b.q0.template load<kPrefillNT>(p0 + (size_t)ei * 32 * F::EB);
     b.q1.template load<kPrefillNT>(p1 + (size_t)ei * 32 * F::EB);
   };
-  f32x16 acc[kMT][2];
+  // The block's pipeline, specialised on the number of 32-row sub-tiles
+  // that hold rows (the last m-tile of an expert is usually partial): empty
+  // sub-tiles cost no MFMAs and no LDS reads. amt is block-uniform, taken
+  // through a scalar register so every wavefront branches the same way.
+  const int amt = __builtin_amdgcn_readfirstlane((t.mcount + 31) / 32);
+  auto run = [&](auto amt_c) {
+    constexpr int AMT = decltype(amt_c)::value;
+    f32x16 acc[AMT][2];
 #pragma unroll
-  for (int mi = 0; mi < kMT; ++mi) {
-    acc[mi][0] = f32x16{};
-    acc[mi][1] = f32x16{};
-  }
-  // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
-  // kh*SPAN/8 + s; swz(mi*32 + n) == swz(n)
-  auto afrag = [&](const uint8_t* buf, int mi, int s) {
-    const int c = (kh * (F::SPAN / 8) + s) ^ swz(n);
-    return *reinterpret_cast<const f16x8*>(buf + (mi * 32 + n) * ROWB + c * 16);
-  };
-
-  // Pipeline, one barrier per K tile. At the start of tile kt the wavefront
-  // waits for its own DMA of token tile kt and its weight codes of tile kt
-  // (everything but the 4 weight loads of tile kt+1 issued at the end of
-  // tile kt-1), then the barrier makes every wavefront's DMA visible and
-  // frees the other buffer; the DMA of tile kt+1 goes out, tile kt is
-  // computed (codes of MFMA step s+1 decoded while the MFMAs of step s run),
-  // and the weight codes of tile kt+2 are fetched into the slot just used.
-  // Prefetches past the last tile re-read the last tile (unused).
-  BTile<F> R0, R1;  // raw weight codes (tile parity)
-  auto mma_jit = [&](const uint8_t* buf, const BTile<F>& raw) {
-    f16x8 av[kMT];
-#pragma unroll
-    for (int mi = 0; mi < kMT; ++mi) av[mi] = afrag(buf, mi, 0);
-    f16x8 d0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
-    f16x8 d1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
-#pragma unroll
-    for (int s = 0; s < F::STEPS; ++s) {
-      f16x8 an[kMT];
-      f16x8 n0 = d0, n1 = d1;
-      if (s + 1 < F::STEPS) {
-#pragma unroll
-        for (int mi = 0; mi < kMT; ++mi) an[mi] = afrag(buf, mi, s + 1);
-        n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
-        n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
-      }
-      // LDS reads of step s+1 stay above the MFMAs of step s (vector and
-      // scalar ALU work may still move across)
-      __builtin_amdgcn_sched_barrier(0x0006);
-      // (a wavefront with no row tile of its own computes on the clamped
-      // tile and stores nothing: no branch around the matrix-core chain)
-#pragma unroll
-      for (int mi = 0; mi < kMT; ++mi) {
-        acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
-        acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
-      }
-      if (s + 1 < F::STEPS) {
-#pragma unroll
-        for (int mi = 0; mi < kMT; ++mi) av[mi] = an[mi];
-      }
-      d0 = n0;
-      d1 = n1;
+    for (int mi = 0; mi < AMT; ++mi) {
+      acc[mi][0] = f32x16{};
+      acc[mi][1] = f32x16{};
     }
-  };
-  if constexpr (DEEP) {
-    // Three token buffers, three weight slots: the DMA of token tile kt+2
-    // goes out at the start of tile kt (into the buffer tile kt-1 used) and
-    // the weight codes of tile kt+3 at its end, so both are fetched two full
-    // tiles ahead. At the start of tile kt everything but the last 8 + NI
-    // memory operations (weights kt+1, DMA kt+1, weights kt+2) has landed.
-    BTile<F> R2;
-    constexpr int VM = 8 + NI;
-    auto tile = [&](int kt, uint8_t* cur, uint8_t* next2, BTile<F>& slot) {
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      dma_a(min(kt + 2, KTn - 1), next2);
-      mma_jit(cur, slot);
-      load_b(min(kt + 3, KTn - 1), slot);
+    // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
+    // kh*SPAN/8 + s; swz(mi*32 + n) == swz(n)
+    auto afrag = [&](const uint8_t* buf, int mi, int s) {
+      const int c = (kh * (F::SPAN / 8) + s) ^ swz(n);
+      return *reinterpret_cast<const f16x8*>(buf + (mi * 32 + n) * ROWB + c * 16);
     };
-    load_b(0, R0);
-    dma_a(0, lds0);
-    load_b(min(1, KTn - 1), R1);
-    dma_a(min(1, KTn - 1), lds1);
-    load_b(min(2, KTn - 1), R2);
-    int kt = 0;
-    for (; kt + 2 < KTn; kt += 3) {
-      tile(kt, lds0, lds2, R0);
-      tile(kt + 1, lds1, lds0, R1);
-      tile(kt + 2, lds2, lds1, R2);
-    }
-    if (kt < KTn) tile(kt, lds0, lds2, R0);
-    if (kt + 1 < KTn) tile(kt + 1, lds1, lds0, R1);
-  } else {
-    // Two token buffers: the DMA of token tile kt+1 goes out at the start of
-    // tile kt, the weight codes of tile kt+2 at its end.
-    auto tile_start = [&](int kt, uint8_t* next) {
-      // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
-      __builtin_amdgcn_s_waitcnt(0x0F74);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // past the last tile this re-fills the idle buffer (no branch in the loop)
-      dma_a(min(kt + 1, KTn - 1), next);
-    };
-    dma_a(0, lds0);
-    load_b(0, R0);
-    load_b(min(1, KTn - 1), R1);
-    int kt = 0;
-    for (; kt + 1 < KTn; kt += 2) {
-      tile_start(kt, lds1);
-      mma_jit(lds0, R0);
-      load_b(min(kt + 2, KTn - 1), R0);
-      tile_start(kt + 1, lds0);
-      mma_jit(lds1, R1);
-      load_b(min(kt + 3, KTn - 1), R1);
-    }
-    if (kt < KTn) {
-      tile_start(kt, lds1);
-      mma_jit(lds0, R0);
-    }
-  }
-  // no LDS DMA may still be in flight when the block's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  if (!on) return;
+    // Pipeline, one barrier per K tile. At the start of tile kt the wavefront
+    // waits for its own DMA of token tile kt and its weight codes of tile kt
+    // (everything but the 4 weight loads of tile kt+1 issued at the end of
+    // tile kt-1), then the barrier makes every wavefront's DMA visible and
+    // frees the other buffer; the DMA of tile kt+1 goes out, tile kt is
+    // computed (codes of MFMA step s+1 decoded while the MFMAs of step s run),
+    // and the weight codes of tile kt+2 are fetched into the slot just used.
+    // Prefetches past the last tile re-read the last tile (unused).
+    BTile<F> R0, R1;  // raw weight codes (tile parity)
+    auto mma_jit = [&](const uint8_t* buf, const BTile<F>& raw) {
+      f16x8 av[AMT];
 #pragma unroll
-  for (int mi = 0; mi < kMT; ++mi) {
+      for (int mi = 0; mi < AMT; ++mi) av[mi] = afrag(buf, mi, 0);
+      f16x8 d0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
+      f16x8 d1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = mi * 32 + acc_row(r, lane);
-      if (i < t.mcount) {
-        const int row = t.row0 + i;
-        if (GU) {
-          store_gu(a, row, 32 * unit + n, acc[mi][0][r], acc[mi][1][r]);
-        } else {
-          store_dn(a, 0, row, 32 * rt0 + n, acc[mi][0][r]);
-          store_dn(a, 0, row, 32 * (rt0 + 1) + n, acc[mi][1][r]);
+      for (int s = 0; s < F::STEPS; ++s) {
+        f16x8 an[AMT];
+        f16x8 n0 = d0, n1 = d1;
+        if (s + 1 < F::STEPS) {
+#pragma unroll
+          for (int mi = 0; mi < AMT; ++mi) an[mi] = afrag(buf, mi, s + 1);
+          n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
+          n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
+        }
+        // LDS reads of step s+1 stay above the MFMAs of step s (vector and
+        // scalar ALU work may still move across)
+        __builtin_amdgcn_sched_barrier(0x0006);
+        // (a wavefront with no row tile of its own computes on the clamped
+        // tile and stores nothing: no branch around the matrix-core chain)
+#pragma unroll
+        for (int mi = 0; mi < AMT; ++mi) {
+          acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
+          acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
+        }
+        if (s + 1 < F::STEPS) {
+#pragma unroll
+          for (int mi = 0; mi < AMT; ++mi) av[mi] = an[mi];
+        }
+        d0 = n0;
+        d1 = n1;
+      }
+    };
+    if constexpr (DEEP) {
+      // Three token buffers, three weight slots: the DMA of token tile kt+2
+      // goes out at the start of tile kt (into the buffer tile kt-1 used) and
+      // the weight codes of tile kt+3 at its end, so both are fetched two full
+      // tiles ahead. At the start of tile kt everything but the last 8 + NI
+      // memory operations (weights kt+1, DMA kt+1, weights kt+2) has landed.
+      BTile<F> R2;
+      constexpr int VM = 8 + NI;
+      auto tile = [&](int kt, uint8_t* cur, uint8_t* next2, BTile<F>& slot) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        dma_a(min(kt + 2, KTn - 1), next2);
+        mma_jit(cur, slot);
+        load_b(min(kt + 3, KTn - 1), slot);
+      };
+      load_b(0, R0);
+      dma_a(0, lds0);
+      load_b(min(1, KTn - 1), R1);
+      dma_a(min(1, KTn - 1), lds1);
+      load_b(min(2, KTn - 1), R2);
+      int kt = 0;
+      for (; kt + 2 < KTn; kt += 3) {
+        tile(kt, lds0, lds2, R0);
+        tile(kt + 1, lds1, lds0, R1);
+        tile(kt + 2, lds2, lds1, R2);
+      }
+      if (kt < KTn) tile(kt, lds0, lds2, R0);
+      if (kt + 1 < KTn) tile(kt + 1, lds1, lds0, R1);
+    } else {
+      // Two token buffers: the DMA of token tile kt+1 goes out at the start of
+      // tile kt, the weight codes of tile kt+2 at its end.
+      auto tile_start = [&](int kt, uint8_t* next) {
+        // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
+        __builtin_amdgcn_s_waitcnt(0x0F74);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // past the last tile this re-fills the idle buffer (no branch in the loop)
+        dma_a(min(kt + 1, KTn - 1), next);
+      };
+      dma_a(0, lds0);
+      load_b(0, R0);
+      load_b(min(1, KTn - 1), R1);
+      int kt = 0;
+      for (; kt + 1 < KTn; kt += 2) {
+        tile_start(kt, lds1);
+        mma_jit(lds0, R0);
+        load_b(min(kt + 2, KTn - 1), R0);
+        tile_start(kt + 1, lds0);
+        mma_jit(lds1, R1);
+        load_b(min(kt + 3, KTn - 1), R1);
+      }
+      if (kt < KTn) {
+        tile_start(kt, lds1);
+        mma_jit(lds0, R0);
+      }
+    }
+    // no LDS DMA may still be in flight when the block's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    if (!on) return;
+#pragma unroll
+    for (int mi = 0; mi < AMT; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = mi * 32 + acc_row(r, lane);
+        if (i < t.mcount) {
+          const int row = t.row0 + i;
+          if (GU) {
+            store_gu(a, row, 32 * unit + n, acc[mi][0][r], acc[mi][1][r]);
+          } else {
+            store_dn(a, 0, row, 32 * rt0 + n, acc[mi][0][r]);
+            store_dn(a, 0, row, 32 * (rt0 + 1) + n, acc[mi][1][r]);
+          }
         }
       }
     }
-  }
+  };
+  if (amt >= kMT)
+    run(IntC<kMT>{});
+  else if (amt == 3)
+    run(IntC<3>{});
+  else if (amt == 2)
+    run(IntC<2>{});
+  else
+    run(IntC<1>{});
 }
 
 inline int max_tiles(int R, int E, int BM) { return (R + BM - 1) / BM + (R < E ? R : E); }
@@ -569,7 +682,8 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   } else {
     const int NU = a.N / (GU ? 32 : 64);
     const int NB = (NU + kPW - 1) / kPW;
-    dim3 grid(max_tiles(a.R, a.E, kBM) * NB);
+    // 16 spare blocks: the per-XCD task shares may round up (find_task_lpt)
+    dim3 grid(max_tiles(a.R, a.E, kBM) * NB + 16);
     hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(64 * kPW), 0, s, a);
   }
   return hipGetLastError();
