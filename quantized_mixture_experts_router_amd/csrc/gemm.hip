@@ -63,7 +63,11 @@ __device__ inline f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c)
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u; the reciprocal is the hardware one (~1 ulp in fp32), far
+// below the fp16 rounding of h that follows
+__device__ inline float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // Row of accumulator register r for lane `lane` in a 32x32 MFMA output tile.
 __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -275,11 +279,6 @@ struct BTile {
 // ===========================================================================
 // Decode family
 // ===========================================================================
-// Weight-code register slots of the decode loop: 3 (two tiles of prefetch,
-// occupancy 3) measures best; 2 (one tile, occupancy 4) is the alternative.
-#ifndef MOEQ_DEC_BSLOTS
-#define MOEQ_DEC_BSLOTS 3
-#endif
 template <class F, bool GU>
 __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
   // The 4 wavefronts of a block form 4/ksw row groups of ksw wavefronts; the
@@ -335,13 +334,10 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   };
   auto load_a = [&](int i, AFrag& af) {
     const int kt = tile_of(i);
+    // every lane loads: rows past the tile read the tile's first row, and
+    // their outputs (MFMA rows of their own) are never stored
 #pragma unroll
-    for (int s = 0; s < F::STEPS; ++s) {
-      // every lane loads (rows past the tile read the tile's first row) and
-      // padding lanes select zero: no divergent branch around the load
-      const f16x8 v = *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s);
-      af.v[s] = arow ? v : f16x8{};
-    }
+    for (int s = 0; s < F::STEPS; ++s) af.v[s] = *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s);
   };
   f32x16 acc0 = {}, acc1 = {};
   auto compute = [&](const BTile<F>& b, const AFrag& af) {
@@ -353,38 +349,30 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
       acc1 = mfma32(af.v[s], b1, acc1);
     }
   };
-  if (MOEQ_DEC_BSLOTS == 3) {
-  // weights two tiles ahead (three slots), token fragments one tile ahead
+  // weights and token fragments two tiles ahead (three slots each)
   BTile<F> B0, B1, B2;
-  AFrag A0, A1;
+  AFrag A0, A1, A2;
   load_b(0, B0);
   load_a(0, A0);
   load_b(1, B1);
-  for (int i = 0; i < nt; i += 6) {
-    // slot pattern repeats every 6 tiles (lcm of 3 weight and 2 token slots)
-    load_a(i + 1, A1); load_b(i + 2, B2); if (i < nt) compute(B0, A0);
-    load_a(i + 2, A0); load_b(i + 3, B0); if (i + 1 < nt) compute(B1, A1);
-    load_a(i + 3, A1); load_b(i + 4, B1); if (i + 2 < nt) compute(B2, A0);
-    load_a(i + 4, A0); load_b(i + 5, B2); if (i + 3 < nt) compute(B0, A1);
-    load_a(i + 5, A1); load_b(i + 6, B0); if (i + 4 < nt) compute(B1, A0);
-    load_a(i + 6, A0); load_b(i + 7, B1); if (i + 5 < nt) compute(B2, A1);
-  }
-  } else {
-  BTile<F> B0, B1;
-  AFrag A0, A1;
-  load_b(0, B0);
-  load_a(0, A0);
-  for (int i = 0; i < nt; i += 2) {
-    load_a(i + 1, A1); load_b(i + 1, B1); if (i < nt) compute(B0, A0);
-    load_a(i + 2, A0); load_b(i + 2, B0); if (i + 1 < nt) compute(B1, A1);
-  }
+  load_a(1, A1);
+  for (int i = 0; i < nt; i += 3) {
+    load_b(i + 2, B2); load_a(i + 2, A2); compute(B0, A0);
+    load_b(i + 3, B0); load_a(i + 3, A0); if (i + 1 < nt) compute(B1, A1);
+    load_b(i + 4, B1); load_a(i + 4, A1); if (i + 2 < nt) compute(B2, A2);
   }
 
   // reduce the ksw partial sums of each row group: red[w][m][r][lane];
-  // wavefront ks of a group finalises registers r = (16/ksw) ks .. +16/ksw
+  // wavefront ks of a group finalises registers r = (16/ksw) ks .. +16/ksw.
+  // Register r holds token rows 8(r/4) + (r%4) and that + 4 of the tile:
+  // registers whose rows all lie past the segment are neither reduced nor
+  // stored (at one token per expert only register 0 carries a row).
+  const int mrows = __builtin_amdgcn_readfirstlane(t.mcount);
+  auto live = [&](int r) { return 8 * (r >> 2) + (r & 3) < mrows; };
   if (ksw > 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      if (!live(r)) continue;
       red[((wave * 2 + 0) * 16 + r) * 64 + lane] = acc0[r];
       red[((wave * 2 + 1) * 16 + r) * 64 + lane] = acc1[r];
     }
@@ -395,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const int w0 = grp * ksw;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (r / RPW != ks) continue;
+    if (r / RPW != ks || !live(r)) continue;
     float v0 = acc0[r], v1 = acc1[r];
     if (ksw > 1) {
       v0 = 0.f;
@@ -433,15 +421,21 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
 #ifndef MOEQ_PF_WAVES
 #define MOEQ_PF_WAVES 4
 #endif
-constexpr int kBM = 128;
+// MOEQ_PF_BM: token rows per block (256 puts one wavefront on each SIMD and
+// measured ~20% slower; 64 spills at four blocks per CU)
+#ifndef MOEQ_PF_BM
+#define MOEQ_PF_BM 128
+#endif
+constexpr int kBM = MOEQ_PF_BM;
 constexpr bool kPrefillNT = MOEQ_PF_NT;  // weight tiles: non-temporal loads
 constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 // wavefronts per prefill block: they share one token tile in LDS, each
 // streaming its own 64 weight rows (one block per CU at 8)
 constexpr int kPW = MOEQ_PF_WAVES;
+constexpr int kBPC = (8 / kPW) * 128 / kBM;  // blocks per CU
 
 template <class F, bool GU>
-__global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs a) {
+__global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) {
   // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
   // 16-byte chunks of row r stored at chunk ^ swz(r). The LDS serves a 16-byte
   // read of 16 lanes (16 consecutive rows, one logical chunk) per cycle from
@@ -453,7 +447,7 @@ __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs 
   // two separate arrays: the compiler can then tell that a DMA into one
   // buffer does not feed reads of the other, and waits only where needed
   // 16 KiB tiles (4-bit) get three buffers and a deeper pipeline
-  constexpr bool DEEP = MOEQ_PF_DEEP && TILEB <= 16384;
+  constexpr bool DEEP = MOEQ_PF_DEEP && 3 * TILEB * kBPC <= 160 * 1024;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[DEEP ? TILEB : 16];
@@ -655,14 +649,14 @@ __global__ __launch_bounds__(64 * kPW, 8 / kPW) void ffn_prefill_kernel(FfnArgs 
       }
     }
   };
-  if (amt >= kMT)
+  if (amt > 3 * kMT / 4)
     run(IntC<kMT>{});
-  else if (amt == 3)
-    run(IntC<3>{});
-  else if (amt == 2)
-    run(IntC<2>{});
+  else if (amt > kMT / 2)
+    run(IntC<(3 * kMT / 4 > 1 ? 3 * kMT / 4 : 1)>{});
+  else if (amt > kMT / 4)
+    run(IntC<(kMT / 2 > 1 ? kMT / 2 : 1)>{});
   else
-    run(IntC<1>{});
+    run(IntC<(kMT / 4 > 1 ? kMT / 4 : 1)>{});
 }
 
 inline int max_tiles(int R, int E, int BM) { return (R + BM - 1) / BM + (R < E ? R : E); }
