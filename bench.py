@@ -254,6 +254,32 @@ def main():
                     lay.append(e0.elapsed_time(e1))
                     gu.append(g0.elapsed_time(g1))
                     dn.append(g1.elapsed_time(g2))
+            # the same layer call captured once in a HIP graph and replayed
+            # (one submission instead of 5-9 launches); the flush stays outside
+            out_g = torch.empty((Td, H), dtype=torch.float32, device=dev)
+            ids_g = torch.empty((Td, k), dtype=torch.int32, device=dev)
+            w_g = torch.empty((Td, k), dtype=torch.float32, device=dev)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                moeq.layer_forward(x_d, wl.Wr, wl.b, wl.packed, k, act=act, ws=ws_d, out=out_g,
+                                   ids=ids_g, w=w_g)
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                moeq.layer_forward(x_d, wl.Wr, wl.b, wl.packed, k, act=act, ws=ws_d, out=out_g,
+                                   ids=ids_g, w=w_g)
+            lay_g = []
+            for r in range(args.decode_warmup + args.decode_reps):
+                flush.zero_()
+                e0, e1 = event(), event()
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= args.decode_warmup:
+                    lay_g.append(e0.elapsed_time(e1))
+            del graph
             touched = np.nonzero(counts_d.cpu().numpy())[0]
             tot_b = sum(payload_bytes(cfg, int(e))[0] for e in touched)
             gu_b = sum(payload_bytes(cfg, int(e))[1] for e in touched)
@@ -263,17 +289,37 @@ def main():
                  "layer_ms": lay_ms,
                  "layer_ms_p10_p90": [float(np.percentile(lay, 10)), float(np.percentile(lay, 90))],
                  "layer_tokens_per_s": Td / (lay_ms * 1e-3),
+                 "layer_ms_graph": float(np.median(lay_g)),
                  "layer_weight_GBps": tot_b / (lay_ms * 1e-3) / 1e9,
                  "ffn_ms": ffn_ms, "ffn_weight_GBps": tot_b / (ffn_ms * 1e-3) / 1e9,
                  "ffn_frac_hbm": tot_b / (ffn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                  "gate_up_ms": gu_ms_d, "gate_up_weight_GBps": gu_b / (gu_ms_d * 1e-3) / 1e9,
                  "gate_up_frac_hbm": gu_b / (gu_ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS,
                  "weight_bytes_touched": tot_b}
-            log(f"[bench] decode T={Td}: layer {lay_ms * 1e3:.1f} us ({d['layer_weight_GBps']:.0f} GB/s), "
+            log(f"[bench] decode T={Td}: layer {lay_ms * 1e3:.1f} us ({d['layer_weight_GBps']:.0f} GB/s; "
+                f"graph replay {d['layer_ms_graph'] * 1e3:.1f} us), "
                 f"gate_up {gu_ms_d * 1e3:.1f} us ({d['gate_up_weight_GBps']:.0f} GB/s), "
                 f"down {dn_ms_d * 1e3:.1f} us, ffn {d['ffn_weight_GBps']:.0f} GB/s")
             dec.append(d)
         result["decode"] = dec
+        # context: what a plain streaming read of the 1 GiB flush buffer
+        # reaches on this machine (median of 5, cached and non-temporal loads)
+        ctx = {"buffer_bytes": flush.numel()}
+        for nt in (False, True):
+            moeq.stream_read(flush, nontemporal=nt)
+            st = []
+            for _ in range(5):
+                e0, e1 = event(), event()
+                e0.record()
+                moeq.stream_read(flush, nontemporal=nt)
+                e1.record()
+                torch.cuda.synchronize()
+                st.append(e0.elapsed_time(e1))
+            ctx["hbm_read_GBps_" + ("nontemporal" if nt else "cached")] = \
+                flush.numel() / (float(np.median(st)) * 1e-3) / 1e9
+        result["context"] = ctx
+        log(f"[bench] streaming read of 1 GiB: {ctx['hbm_read_GBps_cached']:.0f} GB/s cached, "
+            f"{ctx['hbm_read_GBps_nontemporal']:.0f} GB/s non-temporal")
         del flush
 
     # ------------------------------------------------------------------ CPU oracle

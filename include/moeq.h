@@ -253,6 +253,18 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
 moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,
                             void* stream);
 
+/* Measurement aid (not a step of the layer): a plain streaming read of
+ * `bytes` bytes at `src` (device, 16-byte aligned, bytes % 16 == 0) by
+ * MOE_STREAM_BLOCKS blocks with 16-byte loads, non-temporal when
+ * `nontemporal` is non-zero. Each block folds the 32-bit words it read into
+ * an XOR and stores it at sink[block] (device, MOE_STREAM_BLOCKS uint32), so
+ * the XOR of all sink entries is the XOR of every word of the buffer. Timing
+ * it gives the HBM read rate the box reaches, the context for the decode
+ * GEMVs' weight-stream rates. */
+#define MOE_STREAM_BLOCKS 4096
+moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
+                           void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -7,7 +7,8 @@ from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_L
                    MOE_BF16, MOE_F32, MOE_W_ASYM, MOE_W_E2M1, EXPORTED, LIB, LIB_PATH,
                    DeviceQMat, MoeError, PackedExperts, act_quant_i8, combine, ffn_down,
                    ffn_gather, ffn_gate_up, grouped_ffn, layer_forward, pack_expert, pack_experts,
-                   packed_expert_bytes, permute, read_flags, route, route_workspace_size, version, workspace,
+                   packed_expert_bytes, permute, read_flags, route, route_workspace_size, stream_read, version,
+                   workspace,
                    workspace_size)
 
 __all__ = [
@@ -17,5 +18,5 @@ __all__ = [
     "MoeError", "PackedExperts", "act_quant_i8", "combine", "ffn_down", "ffn_gather",
     "ffn_gate_up",
     "grouped_ffn", "layer_forward", "pack_expert", "pack_experts", "packed_expert_bytes",
-    "permute", "read_flags", "route", "route_workspace_size", "version", "workspace", "workspace_size",
+    "permute", "read_flags", "route", "route_workspace_size", "stream_read", "version", "workspace", "workspace_size",
 ]

@@ -68,6 +68,7 @@ _SIGS = {
     "moe_ffn_down": ([_vp, ctypes.c_uint32, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
     "moe_combine": ([_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
     "moe_layer_forward": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_stream_read": ([_vp, _sz, _i, _vp, _vp], _i),
     "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
 }
 
@@ -316,3 +317,17 @@ def act_quant_i8(v):
     _check(LIB.moe_act_quant_i8(_ptr(v), _dt(v), rows, cols, _ptr(q), _ptr(s), _stream()),
            "moe_act_quant_i8")
     return q, s
+
+
+STREAM_BLOCKS = 4096
+
+
+def stream_read(buf, nontemporal=True, sink=None):
+    """Streaming read of a device buffer (measurement aid); returns the
+    per-block XOR words (uint32 as int32 tensor)."""
+    buf = _dev(buf, "buf")
+    if sink is None:
+        sink = torch.empty(STREAM_BLOCKS, dtype=torch.int32, device=buf.device)
+    _check(LIB.moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
+                               _ptr(sink), _stream()), "moe_stream_read")
+    return sink

@@ -366,4 +366,12 @@ moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int
   return hip_status(launch_act_quant_i8(v, dt, rows, cols, q, s, (hipStream_t)stream));
 }
 
+moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
+                           void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink || bytes % 16 != 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_stream_read(src, bytes, nontemporal, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -247,4 +247,49 @@ hipError_t launch_combine(const float* yp, int splits, const float* w, const int
 }
 
 
+// Streaming read (measurement aid): thread t of block b reads the 16-byte
+// chunks b*256 + t + j*256*blocks and folds them into one XOR word per block.
+namespace {
+
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                          size_t n16, uint32_t* __restrict__ sink) {
+  __shared__ uint32_t part[4];
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  // eight loads in flight per thread
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
+                              hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(MOE_STREAM_BLOCKS), dim3(256), 0, s,
+                       (const u32x4*)src, n16, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(MOE_STREAM_BLOCKS), dim3(256), 0, s,
+                       (const u32x4*)src, n16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace moeq

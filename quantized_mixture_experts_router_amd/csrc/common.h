@@ -240,6 +240,8 @@ hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offs
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
+                              hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,
                               void* params, hipStream_t s);
 

@@ -221,7 +221,7 @@ LAYER_CASES = [
     ("hotcold", 2048, 256, 128, 256, 8),
     ("w4a8", 16, 512, 512, 8, 2),
     ("w4a8", 300, 512, 512, 8, 2),
-    # small enough for the fused one-block front (T*E*H <= 2^16)
+    # small decode batches: the one-block front after the logits kernel
     ("mixtral", 2, 512, 1024, 8, 2),
     ("fine_e2m1", 1, 256, 256, 32, 6),
 ]
@@ -318,6 +318,49 @@ def test_nan_token(moeq, T):
     assert torch.equal(ids2, ids) and torch.equal(w2, w)
 
 
+GRAPH_CASES = [
+    ("mixtral", 8, 512, 1024, 8, 2),      # decode: logits + one-block front
+    ("hotcold", 2048, 256, 128, 256, 8),  # prefill: multi-block permutation
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k", GRAPH_CASES)
+def test_layer_graph_replay(moeq, name, T, H, I, E, k):
+    """moe_layer_forward captured once in a HIP graph: every replay, with eager
+    layer calls on other inputs in between (they rewrite the workspace),
+    equals the eager result bit for bit."""
+    cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode="quantize",
+                              n_hot=min(64, E // 4) if name == "hotcold" else None)
+    _say(f"[graph] {name} T={T} H={H} I={I} E={E} k={k}")
+    wl = Workload(cfg)
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+    ref, ids_ref, w_ref = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+    torch.cuda.synchronize()
+    ref, ids_ref, w_ref = ref.clone(), ids_ref.clone(), w_ref.clone()
+    out, ids, w = torch.empty_like(ref), torch.empty_like(ids_ref), torch.empty_like(w_ref)
+    kw = dict(act=cfg.act, ws=ws, out=out, ids=ids, w=w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, **kw)
+    other = wl.x.flip(0).contiguous()
+    for rep in range(3):
+        out.zero_()
+        ids.zero_()
+        w.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        assert torch.equal(ids, ids_ref) and torch.equal(w, w_ref), rep
+        moeq.layer_forward(other, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+        torch.cuda.synchronize()
+    del graph
+
+
 def test_empty_batch(moeq):
     cfg = synth.scaled_config("tiny", T=4, H=256, I=512, E=8, k=2, weight_mode="quantize")
     wl = Workload(cfg)
@@ -334,3 +377,19 @@ def test_bf16_output(moeq):
     o16 = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, out_dtype=torch.bfloat16)[0]
     torch.cuda.synchronize()
     assert torch.equal(o32.to(torch.bfloat16), o16)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 256 * 16 * 8 + 48, 3 << 20])
+def test_stream_read_xor(moeq, nbytes):
+    """The measurement aid reads every word: the XOR of its per-block words is
+    the XOR of the buffer's 32-bit words (remainder loop, 8-deep main loop,
+    fewer chunks than threads)."""
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    for nt in (False, True):
+        sink = moeq.stream_read(buf, nontemporal=nt)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words)
+
