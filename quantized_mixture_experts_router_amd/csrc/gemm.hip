@@ -86,6 +86,7 @@ struct FfnArgs {
   int out_f32;
   int R;
   int splits;
+  int lpt;        // prefill task order: longest first (1) or expert-major (0)
 };
 
 struct Task {
@@ -159,15 +160,19 @@ __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task
   return task.e >= 0;
 }
 
-// Task lookup of the prefill kernel for block b, longest tasks first on each
-// XCD. Tasks are split into full m-tiles (count_e / BM per expert and
-// n-tile) and partial last m-tiles (one per expert and n-tile when count_e
-// is not a multiple of BM), each list expert-major, then n-tile, then m-tile.
-// Blocks are dealt round-robin to the 8 XCDs; XCD x takes a contiguous
-// share of the full list, then a contiguous share of the partial list, in
-// slot order, so blocks sharing weight tiles share an L2 and the short
-// partial tiles run last, filling the tail of the launch. The grid needs 16
-// blocks more than there are tasks (spare blocks find nothing and exit).
+// Task lookup of the prefill kernel for block b. Tasks are full m-tiles
+// (count_e / BM per expert and n-tile) and partial last m-tiles (one per
+// expert and n-tile when count_e is not a multiple of BM). Blocks are dealt
+// round-robin to the 8 XCDs, and XCD x runs, in slot order, an equal
+// contiguous share of the tasks that exist (not of the grid, which is an
+// upper bound), in one of two orders:
+//  - expert-major (a.lpt == 0): expert, then n-tile, then m-tile, so the
+//    m-tiles sharing a weight tile run together and find it in L2;
+//  - longest first (a.lpt == 1): a share of all full m-tiles, then a share
+//    of the partial ones, so short blocks fill the tail of a launch that has
+//    few blocks per slot.
+// The grid needs 16 blocks more than there are tasks (spare blocks find
+// nothing and exit).
 template <bool GU>
 __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, Task& task) {
   __shared__ int s_wsum[2][16];  // up to 1024 threads
@@ -218,34 +223,59 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
     F += s_wsum[0][w];
     P += s_wsum[1][w];
   }
-  // this block's place: XCD x, slot s; the XCD's shares of the two lists
   const int x = b & 7, slot = b >> 3;
-  const int qf = F >> 3, rf = F & 7, qp = P >> 3, rp = P & 7;
-  const int nf = qf + (x < rf ? 1 : 0);
-  const int bf = x * qf + min(x, rf);
-  // the partial list's extras go to the last XCDs (the full list's to the
-  // first), so no XCD takes two
-  const int np = qp + (x >= 8 - rp ? 1 : 0);
-  const int bp = x * qp + max(0, x - (8 - rp));
-  const bool full = slot < nf;
-  const int L = full ? bf + slot : bp + (slot - nf);
-  if (full || slot - nf < np) {
+  if (!a.lpt) {
+    // one list, expert-major; XCD x takes tasks [x q8 + min(x, r8), + n8)
+    const int TOT = F + P;
+    const int q8 = TOT >> 3, r8 = TOT & 7;
+    const int n8 = q8 + (x < r8 ? 1 : 0);
+    const int L = x * q8 + min(x, r8) + slot;
+    if (slot < n8) {
+      int st = sf + sp;  // the thread's experts start here in the combined list
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = 2 * tid + q;
-      const int st = full ? sf : sp;
-      const int n = full ? nfu[q] : npa[q];
-      if (L >= st && L < st + n) {
-        const int rel = L - st;
-        const int mf = cnt[q] / BM;  // full m-tiles of the expert
-        const int mi = full ? rel % mf : mf;
-        s_res[0] = e;
-        s_res[1] = a.offsets[e] + mi * BM;
-        s_res[2] = min(BM, cnt[q] - mi * BM);
-        s_res[3] = full ? rel / mf : rel;
+      for (int q = 0; q < 2; ++q) {
+        const int n = nfu[q] + npa[q];
+        if (L >= st && L < st + n) {
+          const int rel = L - st;
+          const int mt = (cnt[q] + BM - 1) / BM;
+          const int mi = rel % mt;
+          s_res[0] = 2 * tid + q;
+          s_res[1] = a.offsets[2 * tid + q] + mi * BM;
+          s_res[2] = min(BM, cnt[q] - mi * BM);
+          s_res[3] = rel / mt;
+        }
+        st += n;
       }
-      sf += nfu[q];
-      sp += npa[q];
+    }
+  } else {
+    // the XCD's shares of the two lists
+    const int qf = F >> 3, rf = F & 7, qp = P >> 3, rp = P & 7;
+    const int nf = qf + (x < rf ? 1 : 0);
+    const int bf = x * qf + min(x, rf);
+    // the partial list's extras go to the last XCDs (the full list's to the
+    // first), so no XCD takes two
+    const int np = qp + (x >= 8 - rp ? 1 : 0);
+    const int bp = x * qp + max(0, x - (8 - rp));
+    const bool full = slot < nf;
+    const int L = full ? bf + slot : bp + (slot - nf);
+    if (full || slot - nf < np) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        const int st = full ? sf : sp;
+        const int n = full ? nfu[q] : npa[q];
+        if (L >= st && L < st + n) {
+          const int rel = L - st;
+          const int mf = cnt[q] / BM;  // full m-tiles of the expert
+          const int mi = full ? rel % mf : mf;
+          s_res[0] = e;
+          s_res[1] = a.offsets[e] + mi * BM;
+          s_res[2] = min(BM, cnt[q] - mi * BM);
+          s_res[3] = full ? rel / mf : rel;
+        }
+        sf += nfu[q];
+        sp += npa[q];
+      }
     }
   }
   __syncthreads();
@@ -661,6 +691,15 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
 
 inline int max_tiles(int R, int E, int BM) { return (R + BM - 1) / BM + (R < E ? R : E); }
 
+// compute units of the current device
+inline int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 template <int FID, bool GU>
 hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   using F = typename FmtOf<FID>::T;
@@ -676,9 +715,14 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   } else {
     const int NU = a.N / (GU ? 32 : 64);
     const int NB = (NU + kPW - 1) / kPW;
+    // longest-first order when the launch has fewer than 4 blocks per block
+    // slot of the device (its tail is then a large share of its time)
+    const long nblk = (long)max_tiles(a.R, a.E, kBM) * NB;
+    FfnArgs b = a;
+    b.lpt = nblk < 4L * device_cus() * kBPC;
     // 16 spare blocks: the per-XCD task shares may round up (find_task_lpt)
-    dim3 grid(max_tiles(a.R, a.E, kBM) * NB + 16);
-    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(64 * kPW), 0, s, a);
+    dim3 grid(nblk + 16);
+    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(64 * kPW), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -726,6 +770,7 @@ hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* o
   a.out_f32 = h_f32;
   a.R = T * k;
   a.splits = 1;
+  a.lpt = 0;
   return launch_all<true>(a, decode, s);
 }
 
@@ -747,6 +792,7 @@ hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offs
   a.out_f32 = 1;
   a.R = T * k;
   a.splits = decode ? splits : 1;
+  a.lpt = 0;
   return launch_all<false>(a, decode, s);
 }
 
