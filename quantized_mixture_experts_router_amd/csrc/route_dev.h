@@ -19,9 +19,11 @@
 // k-index g of A (token r) and B (expert r). Any bijection between (step,
 // k-index) and columns gives the same dot products, and this one makes every
 // lane's loads contiguous 8/16-byte reads. Output: element i of lane l is
-// D[4i + l/16][l%16] (token 4i + g, expert r). Several waves may split the
-// hidden dimension; each writes its fp64 partial sums and the consumer adds
-// them in split order, so results do not depend on scheduling.
+// D[4i + l/16][l%16] (token 4i + g, expert r). The waves of a block split
+// the hidden dimension and add their tiles in LDS in wave order; blocks that
+// split it further leave fp64 partial logits that the top-k adds in block
+// order. Every sum is in a fixed order, so results do not depend on
+// scheduling.
 #pragma once
 
 #include "common.h"
@@ -32,7 +34,6 @@ namespace rt {
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTT = 16;  // tokens per wavefront tile
-constexpr int kInvalid = 0x7fffffff;
 
 // raw operands of one 16-column chunk for one lane: a token row, NTW
 // expert rows
