@@ -12,7 +12,7 @@ same layer are measured alongside (weight GB/s against HBM peak), each
 repetition preceded by a 1 GiB buffer write so that the 256 MB last-level cache
 holds no weights.
 
-Prints one JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints one JSON line. `--gpus N` with N > 1 exits: the layer runs on one GPU.
 """
 import argparse
 import hashlib
@@ -108,8 +108,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is designed, not built)", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is designed, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
