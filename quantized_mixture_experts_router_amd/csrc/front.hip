@@ -26,17 +26,24 @@ __global__ __launch_bounds__(kFT) void front_kernel(
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* __restrict__ flags, int quant,
     f16* __restrict__ a16, float* __restrict__ ascale) {
+  // LDS: the permutation's scratch, then copies of the ids, of perm and of
+  // the row count, so each phase reads the previous one's results from LDS
+  // rather than through memory
   extern __shared__ int32_t smem[];
+  const int R = T * k;
+  int32_t* s_ids = smem + pm::permute_smem_words(kFW, E);
+  int32_t* s_perm = s_ids + R;
+  int32_t* s_rows = s_perm + R;
   // 1. top-k + softmax, one wavefront per token
   for (int t = threadIdx.x / 64; t < T; t += kFW)
-    rt::topk_token(P, KB, bias, T, E, k, t, ids, w, nullptr);
+    rt::topk_token(P, KB, bias, T, E, k, t, ids, w, nullptr, s_ids);
   __syncthreads();
-  // 2. permutation (its barriers make the ids written above visible)
+  // 2. permutation
   const uint32_t bits =
-      pm::permute_block<kFW>(ids, T * k, k, E, counts, offsets, perm, inv, smem);
+      pm::permute_block<kFW>(s_ids, R, k, E, counts, offsets, perm, inv, smem, s_perm, s_rows);
   __syncthreads();
   // 3. gather of the rows the permutation produced
-  const int rows_used = offsets[E];
+  const int rows_used = *s_rows;
   if (!quant) {
     // every thread moves 8-column chunks of any row; a batch of kU chunks per
     // thread is loaded before any is stored, so one memory round trip covers
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(kFT) void front_kernel(
       for (int u = 0; u < kU; ++u) {
         const int idx = min(b0 + u * kFT, total - 1);
         const int r = idx / CH, c = idx % CH;
-        const size_t src = (size_t)perm[r] * H + 8 * c;
+        const size_t src = (size_t)s_perm[r] * H + 8 * c;
         dsto[u] = r * H + 8 * c;
         if (XDT == MOE_BF16) {
           raw[u][0] = *reinterpret_cast<const u32x4*>((const uint16_t*)x + src);
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(kFT) void front_kernel(
     // int8: wavefront w quantises rows w, w + 8, ...
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     for (int r = wave; r < rows_used; r += kFT / 64) {
-      const size_t src = (size_t)perm[r] * H;
+      const size_t src = (size_t)s_perm[r] * H;
       f16* dst = a16 + (size_t)r * H;
       float m = 0.f;
       for (int c = 8 * lane; c < H; c += 512) {
@@ -119,7 +126,7 @@ hipError_t launch_front(const double* P, int KB, const void* x, int xdt, const f
                         int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags, int quant,
                         f16* a16, float* ascale, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const size_t smem = sizeof(int32_t) * pm::permute_smem_words(kFW, E);
+  const size_t smem = sizeof(int32_t) * (pm::permute_smem_words(kFW, E) + 2 * (size_t)T * k + 1);
   if (xdt == MOE_BF16)
     hipLaunchKernelGGL(front_kernel<MOE_BF16>, dim3(1), dim3(kFT), smem, s, P, KB, x, b, T, H, E,
                        k, ids, w, counts, offsets, perm, inv, flags, quant, a16, ascale);

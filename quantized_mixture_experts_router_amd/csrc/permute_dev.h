@@ -58,9 +58,10 @@ __device__ inline uint32_t wave_hist(const int32_t* __restrict__ ids, int c0, in
 // Stable scatter of assignments [c0, c1): row base[e] + rank for the r-th
 // assignment of expert e in the slice (base[] in LDS, advanced as it goes).
 // Assignment a belongs to token a / k. Ids outside [0, E) get inv = -1.
+// perm_lds (optional, LDS) receives a copy of the perm entries written.
 __device__ inline void wave_scatter(const int32_t* __restrict__ ids, int c0, int c1, int E, int k,
                                     int32_t* base, int32_t* __restrict__ perm,
-                                    int32_t* __restrict__ inv) {
+                                    int32_t* __restrict__ inv, int32_t* perm_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const int bits = 32 - __clz(E > 1 ? E - 1 : 1);
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -84,6 +85,7 @@ __device__ inline void wave_scatter(const int32_t* __restrict__ ids, int c0, int
         const int rank = __popcll(m & lt_mask);
         const int pos = base[e] + rank;
         perm[pos] = a / k;
+        if (perm_lds) perm_lds[pos] = a / k;
         inv[a] = pos;
         const bool last = (m >> lane) == 1ull;  // no same-expert lane above this one
         if (last) base[e] += rank + 1;
@@ -120,11 +122,14 @@ __host__ __device__ inline int permute_smem_words(int W, int E) { return W * E +
 // the block. Returns (to every thread) the flag bits found: ids equal to
 // MOE_ID_NAN raise MOE_FLAG_NAN_LOGIT, any other id outside [0,E)
 // MOE_FLAG_BAD_EXPERT_ID; such assignments get inv = -1 and no row.
+// Optional LDS copies for a consumer in the same block: perm_lds[R] of
+// perm, *rows_lds of offsets[E] (the rows written).
 template <int W>
 __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R, int k, int E,
                                          int32_t* __restrict__ counts,
                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                         int32_t* __restrict__ inv, int32_t* sm) {
+                                         int32_t* __restrict__ inv, int32_t* sm,
+                                         int32_t* perm_lds = nullptr, int32_t* rows_lds = nullptr) {
   constexpr int NTH = W * 64;
   int32_t* base = sm;              // [W][E]
   int32_t* scan = sm + W * E;      // [NTH] scan scratch
@@ -172,11 +177,14 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
       excl += counts[e];
     }
   }
-  if (tid == 0) offsets[E] = total;
+  if (tid == 0) {
+    offsets[E] = total;
+    if (rows_lds) *rows_lds = total;
+  }
   __syncthreads();
 
   // 3. stable scatter
-  wave_scatter(ids, c0, c1, E, k, base + wave * E, perm, inv);
+  wave_scatter(ids, c0, c1, E, k, base + wave * E, perm, inv, perm_lds);
   __syncthreads();
   return *s_flags;
 }

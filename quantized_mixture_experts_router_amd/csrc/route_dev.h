@@ -164,10 +164,12 @@ __device__ inline uint64_t wave_max_u64(uint64_t k) {
 // loaded up front. Then k rounds of a wave-wide argmax over the untaken
 // candidates; the softmax over the k winners' exact fp64 logits. A NaN
 // among the token's logits makes its routing undefined: every slot gets
-// MOE_ID_NAN and weight 0. logits_out (optional) receives the fp32 logits.
+// MOE_ID_NAN and weight 0. logits_out (optional) receives the fp32 logits;
+// ids_lds (optional, LDS) a copy of the ids.
 __device__ inline void topk_token(const double* __restrict__ P, int KB, const float* __restrict__ bias,
                                   int T, int E, int k, int t, int32_t* __restrict__ ids_out,
-                                  float* __restrict__ w_out, float* __restrict__ logits_out) {
+                                  float* __restrict__ w_out, float* __restrict__ logits_out,
+                                  int32_t* ids_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const size_t stride = (size_t)T * E;
   const double* row = P + (size_t)t * E;
@@ -232,8 +234,10 @@ __device__ inline void topk_token(const double* __restrict__ P, int KB, const fl
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   if (lane < k) {
-    ids_out[(size_t)t * k + lane] = nan_row ? MOE_ID_NAN : my_i;
+    const int id = nan_row ? MOE_ID_NAN : my_i;
+    ids_out[(size_t)t * k + lane] = id;
     w_out[(size_t)t * k + lane] = nan_row ? 0.f : (float)(ex / den);
+    if (ids_lds) ids_lds[t * k + lane] = id;  // a copy for a consumer in the same block
   }
 }
 
