@@ -583,9 +583,6 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
           n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
           n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
         }
-        // LDS reads of step s+1 stay above the MFMAs of step s (vector and
-        // scalar ALU work may still move across)
-        __builtin_amdgcn_sched_barrier(0x0006);
         // (a wavefront with no row tile of its own computes on the clamped
         // tile and stores nothing: no branch around the matrix-core chain)
 #pragma unroll
@@ -599,6 +596,18 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         }
         d0 = n0;
         d1 = n1;
+        // one scheduling region per step: each MFMA of step s is followed by
+        // a share of step s+1's decode and one of its LDS reads, so a lone
+        // wavefront keeps the matrix core fed while it decodes
+        constexpr int NM = 2 * AMT;
+        constexpr int VPM = (24 + NM - 1) / NM;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          if (i < AMT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if constexpr (DEEP) {
