@@ -436,6 +436,11 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   }
 }
 
+// decode: fewest K tiles a wavefront of a K-split group streams
+#ifndef MOEQ_DEC_MINT
+#define MOEQ_DEC_MINT 16
+#endif
+
 // ===========================================================================
 // Prefill family
 // ===========================================================================
@@ -599,12 +604,15 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         // one scheduling region per step: each MFMA of step s is followed by
         // a share of step s+1's decode and one of its LDS reads, so a lone
         // wavefront keeps the matrix core fed while it decodes
+        // (about 2/3 of the decode is pinned behind the MFMAs; the scheduler
+        // places the rest, which measured 1% faster than pinning all of it)
         constexpr int NM = 2 * AMT;
         constexpr int VPM = (24 + NM - 1) / NM;
+        constexpr int VG = VPM > 2 ? VPM - 1 : VPM;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);
           if (i < AMT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -714,10 +722,13 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   using F = typename FmtOf<FID>::T;
   if (decode) {
     // wavefronts splitting K inside a block: as many as keep >= 16 K tiles
-    // (per split) on each
+    // (per split) on each; when few weight rows are in flight (a handful of
+    // tokens on small experts) streams of >= 8 tiles on more wavefronts
     const int KTn = a.K / F::KT / (GU ? 1 : a.splits);
-    const int ksw = KTn >= 64 ? 4 : (KTn >= 32 ? 2 : 1);
     const int NRG = GU ? a.N / 32 : a.N / 64;
+    int ksw = KTn >= 4 * MOEQ_DEC_MINT ? 4 : (KTn >= 2 * MOEQ_DEC_MINT ? 2 : 1);
+    const long groups = (long)(a.R < a.E ? a.R : a.E) * NRG * (GU ? 1 : a.splits);
+    while (ksw < 4 && groups * ksw < 2048 && KTn >= 2 * ksw * (MOEQ_DEC_MINT / 2)) ksw *= 2;
     const int NB = (NRG + 4 / ksw - 1) / (4 / ksw);
     dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
     hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a, ksw);

@@ -51,6 +51,7 @@ CASES = [
     ("mixtral", 1, 1, 2),
     ("mixtral", 32, 6, 3),
     ("mixtral", 2048, 8, 3),
+    ("fine_e2m1", 1, 1, 6),
     ("fine_e2m1", 64, 16, 40),
     ("fine_e2m1", 4096, 24, 40),
     ("hotcold", 4096, 24, 40),

@@ -224,6 +224,9 @@ LAYER_CASES = [
     # small decode batches: the one-block front after the logits kernel
     ("mixtral", 2, 512, 1024, 8, 2),
     ("fine_e2m1", 1, 256, 256, 32, 6),
+    # few weight rows in flight: K split over more wavefronts (8-tile streams)
+    ("fine_e2m1", 1, 2048, 256, 32, 6),
+    ("fine_e2m1", 3, 1024, 256, 32, 6),
 ]
 
 
