@@ -729,6 +729,19 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
     int ksw = KTn >= 4 * MOEQ_DEC_MINT ? 4 : (KTn >= 2 * MOEQ_DEC_MINT ? 2 : 1);
     const long groups = (long)(a.R < a.E ? a.R : a.E) * NRG * (GU ? 1 : a.splits);
     while (ksw < 4 && groups * ksw < 2048 && KTn >= 2 * ksw * (MOEQ_DEC_MINT / 2)) ksw *= 2;
+    // blocks (one per touched expert and row-group set, as when each touched
+    // expert has at most 32 rows) that would spill a little past one round
+    // of the device's block slots: half as many, on twice longer K streams,
+    // so the launch ends after one round (one token: 1.5 us of 37)
+    if (ksw > 1) {
+      const long blocks = groups / (4 / ksw);
+      int bpc = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void*)ffn_decode_kernel<F, GU>,
+                                                       kThreads, 0) != hipSuccess || bpc <= 0)
+        bpc = 1;
+      const long slots = (long)device_cus() * bpc;
+      if (blocks > slots && blocks <= 2 * slots) ksw /= 2;
+    }
     const int NB = (NRG + 4 / ksw - 1) / (4 / ksw);
     dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
     hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a, ksw);
