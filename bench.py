@@ -117,7 +117,7 @@ def main():
 
     import synth
     import quantized_mixture_experts_router_amd as moeq
-    from layer_cases import Workload, rel_l2_rows, tolerance
+    from layer_cases import Workload, rel_l2_rows, tolerance, x_to_torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -152,16 +152,17 @@ def main():
     Y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
 
     # every launch goes to torch's current stream, which the events time
-    def step(evs=None):
+    def step(evs=None, pk=None):
+        pk = wl.packed if pk is None else pk
         ids_, w_ = moeq.route(wl.x, wl.Wr, wl.b, k)
         counts, offsets, perm, inv, _ = moeq.permute(ids_, E, ws)
-        moeq.ffn_gather(wl.x, perm, k, wl.packed, act, ws)
+        moeq.ffn_gather(wl.x, perm, k, pk, act, ws)
         if evs is not None:
             evs[0].record()
-        moeq.ffn_gate_up(T, wl.packed, offsets, k, act, ws)
+        moeq.ffn_gate_up(T, pk, offsets, k, act, ws)
         if evs is not None:
             evs[1].record()
-        moeq.ffn_down(T, wl.packed, offsets, k, act, Y, ws)
+        moeq.ffn_down(T, pk, offsets, k, act, Y, ws)
         if evs is not None:
             evs[2].record()
         o = moeq.combine(Y, w_, inv, T, k)
@@ -223,6 +224,64 @@ def main():
                    "layer_tflops": flop_layer / (ms_step * 1e-3) / 1e12},
         "split_api_equals_layer_forward": same,
     }
+
+    # ------------------------------------------------------------------ tiers
+    # Expert-aware precision from a routing profile: the routing of T held-out
+    # calibration tokens (the T rows after the bench's own) is counted on the
+    # device, the tier plan gives 4-bit to the most used experts within the
+    # byte budget of the workload's bias-ranked hot set, and the layer is
+    # repacked by that plan and timed again. The hot experts' share of the
+    # bench's own routing slots is compared for the two hot sets.
+    if cfg.cold_fmt is not None and cfg.n_hot > 0 and not args.decode_only:
+        from dataclasses import replace
+        x_cal = x_to_torch(synth.gen_x(cfg, 2 * T)[T:], cfg.x_dtype, dev)
+        hist = torch.zeros(E, dtype=torch.int64, device=dev)
+        ids_c, _ = moeq.route(x_cal, wl.Wr, wl.b, k)
+        moeq.expert_histogram(ids_c, E)  # first launch loads the kernel: not timed
+        h0, h1 = event(), event()
+        step()  # queued GPU work ahead of the events, so they time the kernel, not the launch
+        h0.record()
+        moeq.expert_histogram(ids_c, E, hist)
+        h1.record()
+        torch.cuda.synchronize()
+        hist_ms = h0.elapsed_time(h1)
+        counts_cal = hist.cpu().numpy()
+        sizes = []
+        for f in (cfg.fmt, cfg.cold_fmt):
+            ex = synth.gen_expert(replace(cfg, expert_fmts=(f,) * E), 0)
+            sizes.append(moeq.packed_expert_bytes(
+                *[moeq.DeviceQMat.from_host(ex[r], dev) for r in ("gate", "up", "down")]))
+        budget = cfg.n_hot * sizes[0] + (E - cfg.n_hot) * sizes[1]
+        tp0 = time.perf_counter()
+        tiers, used = moeq.plan_tiers(counts_cal, sizes, budget)
+        plan_us = (time.perf_counter() - tp0) * 1e6
+        own = moeq.expert_histogram(ids_, E).cpu().numpy()
+        prior = np.array([synth.expert_format(cfg, e) == cfg.fmt for e in range(E)])
+        hot = tiers == 0
+        cfg_p = replace(cfg, expert_fmts=tuple(cfg.fmt if t == 0 else cfg.cold_fmt for t in tiers))
+        wl_p = Workload(cfg_p, device=dev)
+        for _ in range(args.warmup):
+            step(pk=wl_p.packed)
+        torch.cuda.synchronize()
+        tt0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(pk=wl_p.packed)
+        torch.cuda.synchronize()
+        ms_p = (time.perf_counter() - tt0) * 1e3 / args.steps
+        del wl_p
+        result["tiers"] = {
+            "calibration_tokens": T, "hot_experts": int(hot.sum()),
+            "tier_bytes": sizes, "budget_bytes": int(budget), "used_bytes": int(used),
+            "histogram_ms": hist_ms, "plan_us": plan_us,
+            "hot_set_overlap": int((hot & prior).sum()),
+            "hot_share_profiled": float(own[hot].sum() / own.sum()),
+            "hot_share_bias_ranked": float(own[prior].sum() / own.sum()),
+            "prefill_ms_profiled": ms_p, "prefill_ms_bias_ranked": ms_step,
+        }
+        log(f"[bench] tiers: profiled hot set shares {result['tiers']['hot_share_profiled']:.3f} "
+            f"of the slots (bias-ranked {result['tiers']['hot_share_bias_ranked']:.3f}; "
+            f"overlap {result['tiers']['hot_set_overlap']}/{cfg.n_hot}); prefill {ms_p:.3f} ms "
+            f"(bias-ranked {ms_step:.3f}); histogram {hist_ms * 1e3:.1f} us, plan {plan_us:.0f} us")
 
     # ------------------------------------------------------------------ decode
     if not args.no_decode and cfg.decode_T:

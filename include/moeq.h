@@ -253,6 +253,36 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
 moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,
                             void* stream);
 
+/* Routing profile for expert-aware precision (expert-aware quantisation
+ * digest, profiling and results sections: a profiling run over task data
+ * marks the experts the router actually uses as hot and keeps them at higher
+ * precision, the rest at 2 bits; its conclusion sketches a gradient of ever
+ * coarser tiers for ever colder experts).
+ * hist[e] += the number of slots of topk_ids [T,k] (device, int32) equal to e,
+ * for e in [0,E); ids outside [0,E) (MOE_ID_NAN included) are not counted.
+ * hist (device): int64 [E], accumulated across calls (the caller zeroes it
+ * once). Integer adds: the result does not depend on their order.
+ * T*k <= 2^30, E <= 256. */
+moe_status moe_expert_histogram(const int32_t* topk_ids, int T, int k, int E, int64_t* hist,
+                                void* stream);
+
+/* Precision tiers from a routing profile (host only: no device work, no
+ * stream). counts [E] (host, >= 0): routing counts, e.g. a
+ * moe_expert_histogram profile. tier_bytes [ntiers] (host): the bytes one
+ * expert takes at each tier (moe_packed_expert_bytes of its packing), most
+ * precise first, non-increasing, each <= 2^40. Experts are ranked by count,
+ * descending, ties to the lower index; walking that ranking, each expert
+ * gets the most precise tier whose bytes leave room, within budget_bytes,
+ * for every expert after it at the last tier. So the tiers never get more
+ * precise as the counts fall, and the first expert below the top tier could
+ * not be raised one tier without exceeding the budget. tier_of [E] (host,
+ * out): the tier index of each expert; *used_bytes (host, out, nullable):
+ * their total. MOE_ERR_INVALID_ARG if an argument is out of range or even
+ * every expert at the last tier exceeds the budget (tier_of is then left
+ * untouched). 1 <= E <= 65536, 1 <= ntiers <= 16. */
+moe_status moe_plan_tiers(const int64_t* counts, int E, const uint64_t* tier_bytes, int ntiers,
+                          uint64_t budget_bytes, int32_t* tier_of, uint64_t* used_bytes);
+
 /* Measurement aid (not a step of the layer): a plain streaming read of
  * `bytes` bytes at `src` (device, 16-byte aligned, bytes % 16 == 0) by
  * MOE_STREAM_BLOCKS blocks with 16-byte loads, non-temporal when

@@ -7,12 +7,13 @@ binding never import, call or link it, and it shares no code with them.
 It is plain, slow and meant to be checked by eye against the method's
 statement: fp64 router logits, an exact stable top-k, a softmax over the
 selected logits, a stable counting-sort permutation, blocks decoded to fp32,
-fp64 matmuls and an fp64 weighted combine.
+fp64 matmuls and an fp64 weighted combine; also the routing histogram and
+the precision-tier plan of expert-aware quantisation.
 """
 from .moe import (decode_qmat, router_logits, topk_softmax, canonical_permute,
                   act_quant_i8, dq8, swiglu, expert_ffn, combine, moe_layer,
-                  x_to_f64, NEAR_TIE, E2M1_TABLE)
+                  x_to_f64, expert_histogram, plan_tiers, NEAR_TIE, E2M1_TABLE)
 
 __all__ = ["decode_qmat", "router_logits", "topk_softmax", "canonical_permute",
            "act_quant_i8", "dq8", "swiglu", "expert_ffn", "combine", "moe_layer",
-           "x_to_f64", "NEAR_TIE", "E2M1_TABLE"]
+           "x_to_f64", "expert_histogram", "plan_tiers", "NEAR_TIE", "E2M1_TABLE"]

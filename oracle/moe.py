@@ -18,6 +18,10 @@ Sources (pages as titled; sections as numbered on each page):
   [FFN]       "AlphaQ" blog, section 2.2 and the mixed-precision notes,
               section 3.3: each expert is a three-matrix FFN (gate, up/middle,
               down/output); its gated form is SwiGLU.
+  [Tiers]     expert-aware quantisation digest, profiling, results and
+              conclusion sections: profile which experts the router uses,
+              keep the most used ones precise and the rest at 2 bits, and
+              more generally coarser tiers for colder experts.
 
 Readings where the pages are silent (each listed with its reason in the
 design notes): ties and near-ties go to the lower expert index; the bias adds
@@ -25,6 +29,10 @@ to the logits before selection; segments are ordered by ascending token;
 asymmetric blocks decode as w = s*q + m with one fp32 rounding; e2m1 uses the
 OCP MX value set; int8 activations are symmetric absmax/127, round half to
 even, clamped to +-127; the router sees the unquantised hidden states.
+
+The tier plan is a reading too: experts ranked by routing count (ties to
+the lower index), each taking the most precise tier that leaves room in the
+byte budget for all experts after it at the cheapest tier.
 
 Parity pins: see tests/test_oracle.py (brute-force dense MoE, invariants,
 closed forms, textbook special cases, hand-written golden blobs).
@@ -259,3 +267,37 @@ def moe_layer(x, x_dtype: str, Wr, b, get_expert, E: int, k: int, act: int = 0,
     out = combine(Y, w, inv, T, k)
     return dict(logits=L, ids=ids, w=w, gap=gap, flagged=flagged, counts=counts,
                 offsets=offsets, perm_token=perm_token, inv=inv, Y=Y, out=out)
+
+
+# --------------------------------------------------------------------------
+# Routing profile and precision tiers [Tiers]
+# --------------------------------------------------------------------------
+def expert_histogram(ids: np.ndarray, E: int) -> np.ndarray:
+    """Number of routing slots per expert, ids outside [0, E) not counted."""
+    ids = np.asarray(ids).reshape(-1)
+    out = np.zeros(E, dtype=np.int64)
+    for e in ids:
+        if 0 <= e < E:
+            out[e] += 1
+    return out
+
+
+def plan_tiers(counts, tier_bytes, budget: int):
+    """Tier index per expert (0 = most precise) and the bytes they use, or None
+    when even every expert at the last tier exceeds the budget. Hottest first
+    (count descending, ties to the lower index), each expert takes the first
+    tier whose bytes still leave room for all later experts at the last tier."""
+    counts = [int(c) for c in counts]
+    tier_bytes = [int(b) for b in tier_bytes]
+    E, last = len(counts), tier_bytes[-1]
+    if E * last > budget:
+        return None
+    order = sorted(range(E), key=lambda e: (-counts[e], e))
+    tiers = [0] * E
+    used = 0
+    for i, e in enumerate(order):
+        rest = (E - 1 - i) * last
+        t = next(t for t, b in enumerate(tier_bytes) if used + b + rest <= budget)
+        tiers[e] = t
+        used += tier_bytes[t]
+    return np.array(tiers, dtype=np.int32), used

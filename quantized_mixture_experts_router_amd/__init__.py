@@ -5,9 +5,10 @@ include/moeq.h); this package is its thin Python binding.
 """
 from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT, ID_NAN,
                    MOE_BF16, MOE_F32, MOE_W_ASYM, MOE_W_E2M1, EXPORTED, LIB, LIB_PATH,
-                   DeviceQMat, MoeError, PackedExperts, act_quant_i8, combine, ffn_down,
+                   DeviceQMat, MoeError, PackedExperts, act_quant_i8, combine, expert_histogram, ffn_down,
                    ffn_gather, ffn_gate_up, grouped_ffn, layer_forward, pack_expert, pack_experts,
-                   packed_expert_bytes, permute, read_flags, route, route_workspace_size, stream_read, version,
+                   packed_expert_bytes, permute, plan_tiers, read_flags, route, route_workspace_size,
+                   stream_read, version,
                    workspace,
                    workspace_size)
 
@@ -15,8 +16,9 @@ __all__ = [
     "ACT_I8_X", "ACT_I8_XH", "ACT_NONE", "FLAG_BAD_EXPERT_ID", "FLAG_NAN_LOGIT", "ID_NAN",
     "MOE_BF16",
     "MOE_F32", "MOE_W_ASYM", "MOE_W_E2M1", "EXPORTED", "LIB", "LIB_PATH", "DeviceQMat",
-    "MoeError", "PackedExperts", "act_quant_i8", "combine", "ffn_down", "ffn_gather",
+    "MoeError", "PackedExperts", "act_quant_i8", "combine", "expert_histogram", "ffn_down",
+    "ffn_gather",
     "ffn_gate_up",
     "grouped_ffn", "layer_forward", "pack_expert", "pack_experts", "packed_expert_bytes",
-    "permute", "read_flags", "route", "route_workspace_size", "stream_read", "version", "workspace", "workspace_size",
+    "permute", "plan_tiers", "read_flags", "route", "route_workspace_size", "stream_read", "version", "workspace", "workspace_size",
 ]

@@ -70,6 +70,8 @@ _SIGS = {
     "moe_layer_forward": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_stream_read": ([_vp, _sz, _i, _vp, _vp], _i),
     "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
+    "moe_expert_histogram": ([_vp, _i, _i, _i, _vp, _vp], _i),
+    "moe_plan_tiers": ([_vp, _i, _vp, _i, ctypes.c_uint64, _vp, _vp], _i),
 }
 
 
@@ -331,3 +333,29 @@ def stream_read(buf, nontemporal=True, sink=None):
     _check(LIB.moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
                                _ptr(sink), _stream()), "moe_stream_read")
     return sink
+
+
+def expert_histogram(ids, E, hist=None):
+    """Adds the per-expert counts of routing ids [T, k] (device int32) into
+    hist (device int64 [E], a new zeroed one if None) and returns hist."""
+    ids = _dev(ids, "ids")
+    T, k = ids.shape
+    if hist is None:
+        hist = torch.zeros(E, dtype=torch.int64, device=ids.device)
+    _check(LIB.moe_expert_histogram(_ptr(ids), T, k, E, _ptr(hist), _stream()),
+           "moe_expert_histogram")
+    return hist
+
+
+def plan_tiers(counts, tier_bytes, budget):
+    """Precision tier per expert from a routing profile (host only).
+    counts: E non-negative ints; tier_bytes: bytes of one expert per tier, most
+    precise first. Returns (tier index per expert as int32 array, bytes used)."""
+    c = np.ascontiguousarray(np.asarray(counts, dtype=np.int64))
+    tb = np.ascontiguousarray(np.asarray(tier_bytes, dtype=np.uint64))
+    out = np.empty(c.shape[0], dtype=np.int32)
+    used = ctypes.c_uint64(0)
+    _check(LIB.moe_plan_tiers(c.ctypes.data, c.shape[0], tb.ctypes.data, tb.shape[0],
+                              ctypes.c_uint64(int(budget)), out.ctypes.data, ctypes.byref(used)),
+           "moe_plan_tiers")
+    return out, used.value

@@ -366,6 +366,30 @@ moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int
   return hip_status(launch_act_quant_i8(v, dt, rows, cols, q, s, (hipStream_t)stream));
 }
 
+moe_status moe_expert_histogram(const int32_t* topk_ids, int T, int k, int E, int64_t* hist,
+                                void* stream) {
+  if (T < 0 || k < 1 || E < 1 || E > kMaxE) return MOE_ERR_INVALID_ARG;
+  if ((long)T * k > (1L << 30)) return MOE_ERR_INVALID_ARG;
+  if (!hist || (T > 0 && !topk_ids)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(hist, 8) || !aligned(topk_ids, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_expert_histogram(topk_ids, (long)T * k, E, hist, (hipStream_t)stream));
+}
+
+moe_status moe_plan_tiers(const int64_t* counts, int E, const uint64_t* tier_bytes, int ntiers,
+                          uint64_t budget_bytes, int32_t* tier_of, uint64_t* used_bytes) {
+  if (!counts || !tier_bytes || !tier_of) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || E > (1 << 16) || ntiers < 1 || ntiers > 16) return MOE_ERR_INVALID_ARG;
+  for (int t = 0; t < ntiers; ++t) {
+    if (tier_bytes[t] > (1ull << 40)) return MOE_ERR_INVALID_ARG;
+    if (t > 0 && tier_bytes[t] > tier_bytes[t - 1]) return MOE_ERR_INVALID_ARG;
+  }
+  for (int e = 0; e < E; ++e)
+    if (counts[e] < 0) return MOE_ERR_INVALID_ARG;
+  return plan_tiers(counts, E, tier_bytes, ntiers, budget_bytes, tier_of, used_bytes)
+             ? MOE_OK
+             : MOE_ERR_INVALID_ARG;
+}
+
 moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                            void* stream) {
   if (bytes == 0) return MOE_OK;

@@ -34,6 +34,7 @@ class LayerConfig:
     fmt: Tuple[int, int, int]    # (fmt, bits, group) of every expert ...
     cold_fmt: Optional[Tuple[int, int, int]] = None  # ... or of the cold ones
     n_hot: int = 0               # hot experts = the n_hot largest router biases
+    expert_fmts: Optional[Tuple[Tuple[int, int, int], ...]] = None  # per-expert override
     zipf_alpha: float = 0.0      # router bias b_e = -alpha * ln(rank_e)
     act: int = ACT_NONE          # per-token int8 expert inputs
     outlier_frac: float = 0.0
@@ -134,6 +135,8 @@ def gen_x(cfg: LayerConfig, T: Optional[int] = None) -> np.ndarray:
 
 
 def expert_format(cfg: LayerConfig, e: int) -> Tuple[int, int, int]:
+    if cfg.expert_fmts is not None:
+        return cfg.expert_fmts[e]
     if cfg.cold_fmt is None:
         return cfg.fmt
     return cfg.fmt if _bias_ranks(cfg)[e] <= cfg.n_hot else cfg.cold_fmt

@@ -152,3 +152,56 @@ def test_layer_forward_rejects():
     assert L.moe_layer_forward(p, 1, p, None, p, 0, 4, 256, 256, 8, 2, 0, p, 9, None, None, p, ws, None) == -1
     # T = 0 is a no-op
     assert L.moe_layer_forward(p, 1, p, None, p, 0, 0, 256, 256, 8, 2, 0, p, 0, None, None, p, ws, None) == 0
+
+
+def test_plan_tiers_matches_oracle():
+    # host-only entry point: no device work, so it runs here
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        E = int(rng.integers(1, 300))
+        nt = int(rng.integers(1, 5))
+        tb = sorted((int(b) for b in rng.integers(1, 1 << 30, size=nt)), reverse=True)
+        counts = rng.integers(0, int(rng.integers(1, 50)), size=E)
+        budget = int(rng.integers(E * tb[-1], E * tb[0] + 2))
+        got, used = moeq.plan_tiers(counts, tb, budget)
+        want, wused = oracle.plan_tiers(counts, tb, budget)
+        np.testing.assert_array_equal(got, want)
+        assert used == wused
+
+
+def test_plan_tiers_rejects():
+    import numpy as np
+    L = _lib.LIB
+    counts = np.array([3, 1, 2], dtype=np.int64)
+    out = np.zeros(3, dtype=np.int32)
+
+    def call(c=counts, E=3, tb=(10, 5), budget=30, o=out):
+        t = np.ascontiguousarray(np.asarray(tb, dtype=np.uint64))
+        return L.moe_plan_tiers(None if c is None else c.ctypes.data, E,
+                                None if t.size == 0 else t.ctypes.data, t.size,
+                                ctypes.c_uint64(budget), None if o is None else o.ctypes.data, None)
+
+    assert call() == 0
+    assert call(c=None) == -1
+    assert call(o=None) == -1
+    assert call(E=0) == -1
+    assert call(tb=()) == -1
+    assert call(tb=(5, 10)) == -1                    # not most precise first
+    assert call(tb=((1 << 40) + 1, 5)) == -1          # tier too large
+    assert call(budget=14) == -1                      # 3 experts at 5 B exceed 14 B
+    out[:] = 7
+    assert call(budget=14) == -1 and list(out) == [7, 7, 7]  # untouched on failure
+    assert call(c=np.array([3, -1, 2], dtype=np.int64)) == -1
+    assert call(budget=15) == 0 and list(out) == [1, 1, 1]
+
+
+def test_expert_histogram_rejects():
+    L = _lib.LIB
+    p = ctypes.c_void_p
+    assert L.moe_expert_histogram(p(16), 4, 2, 8, None, None) == -1
+    assert L.moe_expert_histogram(p(16), 4, 0, 8, p(16), None) == -1
+    assert L.moe_expert_histogram(p(16), 4, 2, 257, p(16), None) == -1
+    assert L.moe_expert_histogram(p(16), -1, 2, 8, p(16), None) == -1
+    assert L.moe_expert_histogram(p(16), 4, 2, 8, p(12), None) == -3

@@ -396,3 +396,69 @@ def test_stream_read_xor(moeq, nbytes):
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(words)
 
+
+
+# ----------------------------------------------------- routing profile and tiers
+@pytest.mark.parametrize("T,k,E", [(1, 2, 8), (1000, 6, 256), (70000, 8, 64), (0, 2, 8)])
+def test_expert_histogram(moeq, T, k, E):
+    _say(f"[histogram] T={T} k={k} E={E}")
+    rng = np.random.default_rng(T + E)
+    ids = rng.integers(-3, E + 3, size=(T, k)).astype(np.int32)
+    if T:
+        ids[0, 0] = moeq.ID_NAN
+    d = torch.from_numpy(ids).cuda()
+    h = moeq.expert_histogram(d, E)
+    h = moeq.expert_histogram(d[: T // 2].contiguous(), E, h)  # accumulates
+    torch.cuda.synchronize()
+    want = oracle.expert_histogram(ids, E) + oracle.expert_histogram(ids[: T // 2], E)
+    np.testing.assert_array_equal(h.cpu().numpy(), want)
+
+
+def test_profiled_tiers_layer(moeq):
+    """Profile the routing of calibration tokens on the device, plan two tiers
+    (4-bit g32 hot, 2-bit g16 cold) for a budget of n_hot hot experts, pack by
+    the plan and check the layer against the oracle."""
+    from dataclasses import replace
+    from synth.configs import A2G16, A4G32
+    n_hot = 16
+    base = synth.scaled_config("hotcold", T=512, H=256, I=128, E=64, k=8,
+                               weight_mode="quantize", n_hot=n_hot)
+    _say(f"[tiers] hotcold T={base.T} H={base.H} I={base.I} E={base.E} k={base.k}")
+    # calibration tokens: the T rows after the layer's own, same router
+    x_cal = synth.gen_x(base, 2 * base.T)[base.T:]
+    Wr_np, b_np = synth.gen_router(base)
+    Wr, b = torch.from_numpy(Wr_np).cuda(), torch.from_numpy(b_np).cuda()
+    ids, _ = moeq.route(x_to_torch(x_cal, base.x_dtype), Wr, b, base.k)
+    hist = moeq.expert_histogram(ids, base.E)
+    torch.cuda.synchronize()
+    counts = hist.cpu().numpy()
+    np.testing.assert_array_equal(counts, oracle.expert_histogram(ids.cpu().numpy(), base.E))
+    # bytes of one expert at each tier, from the library
+    sizes = []
+    for fmt in (A4G32, A2G16):
+        ex = synth.gen_expert(replace(base, expert_fmts=(fmt,) * base.E), 0)
+        qm = [moeq.DeviceQMat.from_host(ex[r]) for r in ("gate", "up", "down")]
+        sizes.append(moeq.packed_expert_bytes(*qm))
+    budget = n_hot * sizes[0] + (base.E - n_hot) * sizes[1]
+    tiers, used = moeq.plan_tiers(counts, sizes, budget)
+    want_t, want_used = oracle.plan_tiers(counts, sizes, budget)
+    np.testing.assert_array_equal(tiers, want_t)
+    assert used == want_used == budget
+    order = sorted(range(base.E), key=lambda e: (-int(counts[e]), e))
+    assert set(np.flatnonzero(tiers == 0).tolist()) == set(order[:n_hot])
+    # the profiled hot set covers at least as many calibration slots as the
+    # bias-ranked one the workload would pick
+    prior = [e for e in range(base.E) if synth.expert_format(base, e) == A4G32]
+    assert counts[tiers == 0].sum() >= counts[prior].sum()
+    cfg = replace(base, expert_fmts=tuple(A4G32 if t == 0 else A2G16 for t in tiers))
+    wl = Workload(cfg)
+    out, ids2, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, wl.b_np, wl.expert, cfg.E, cfg.k,
+                           act=cfg.act)
+    ok = ~ref["flagged"]
+    np.testing.assert_array_equal(ids2.cpu().numpy()[ok], ref["ids"][ok])
+    err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
+    _say(f"    hot share {counts[tiers == 0].sum() / counts.sum():.3f} "
+         f"(bias-ranked {counts[prior].sum() / counts.sum():.3f}); max row rel-L2 {err.max():.3e}")
+    assert err.max() <= tolerance(cfg)

@@ -414,3 +414,99 @@ def test_w4a8_outlier_fraction():
     x = synth.bf16_bits_to_f32(synth.gen_x(cfg))
     frac = np.mean(np.abs(x) > 8.0)  # N(0,1) beyond 8 sigma is ~1e-15; outliers are x20
     assert 0.0006 < frac < 0.0012, frac
+
+
+# --------------------------------------------------------------------------
+# Routing profile and precision tiers (expert-aware quantisation digest)
+# --------------------------------------------------------------------------
+def test_expert_histogram_hand_example():
+    ids = np.array([[0, 3], [3, -2], [7, 0], [3, 1]], dtype=np.int32)
+    # 7 and -2 lie outside [0, 4) and are not counted
+    np.testing.assert_array_equal(oracle.expert_histogram(ids, 4), [2, 1, 0, 3])
+
+
+def _lexmin_by_rank(counts, tier_bytes, budget):
+    """Brute force: of all tier vectors within the budget, the one whose
+    tiers, read hottest first (ties to the lower index), are smallest in
+    lexicographic order."""
+    E = len(counts)
+    order = sorted(range(E), key=lambda e: (-counts[e], e))
+    best = None
+    for tv in itertools.product(range(len(tier_bytes)), repeat=E):
+        if sum(tier_bytes[t] for t in tv) > budget:
+            continue
+        key = tuple(tv[e] for e in order)
+        if best is None or key < best[0]:
+            best = (key, tv)
+    return None if best is None else np.array(best[1], dtype=np.int32)
+
+
+def test_plan_tiers_matches_brute_force():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        E = int(rng.integers(1, 7))
+        nt = int(rng.integers(1, 4))
+        tb = sorted((int(b) for b in rng.integers(1, 40, size=nt)), reverse=True)
+        counts = [int(c) for c in rng.integers(0, 4, size=E)]  # many ties
+        budget = int(rng.integers(0, E * tb[0] + 5))
+        got = oracle.plan_tiers(counts, tb, budget)
+        want = _lexmin_by_rank(counts, tb, budget)
+        if want is None:
+            assert got is None
+        else:
+            np.testing.assert_array_equal(got[0], want)
+            assert got[1] == sum(tb[t] for t in want) <= budget
+
+
+def test_plan_tiers_two_tiers_closed_form():
+    # two tiers: the n = (budget - E*lo) // (hi - lo) hottest experts are hot
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        E = int(rng.integers(1, 300))
+        hi, lo = sorted((int(v) for v in rng.integers(1, 10**6, size=2)), reverse=True)
+        if hi == lo:
+            hi += 1
+        counts = rng.integers(0, 50, size=E)
+        budget = E * lo + int(rng.integers(0, E * (hi - lo) + 1))
+        tiers, used = oracle.plan_tiers(counts, [hi, lo], budget)
+        n = min(E, (budget - E * lo) // (hi - lo))
+        order = sorted(range(E), key=lambda e: (-int(counts[e]), e))
+        assert set(np.flatnonzero(tiers == 0).tolist()) == set(order[:n])
+        assert used == n * hi + (E - n) * lo
+
+
+def test_plan_tiers_digest_configuration():
+    # The digest's configuration: 64 of 256 experts hot at 4 bits, 192 cold at
+    # 2 bits. Bytes of one hidden-2048, intermediate-512 expert: 3*H*I weights
+    # at 0.625 B (4-bit, fp16 scale+min per 32) or 0.5 B (2-bit, per 16).
+    H, I, E = 2048, 512, 256
+    b4, b2 = 3 * H * I * 5 // 8, 3 * H * I // 2
+    rng = np.random.default_rng(13)
+    counts = rng.permutation(E) * 7 + 3  # distinct
+    tiers, used = oracle.plan_tiers(counts, [b4, b2], 64 * b4 + 192 * b2)
+    hot = set(np.argsort(-counts)[:64].tolist())
+    assert set(np.flatnonzero(tiers == 0).tolist()) == hot
+    assert used == 64 * b4 + 192 * b2
+    # one byte less and only 63 fit
+    tiers, _ = oracle.plan_tiers(counts, [b4, b2], 64 * b4 + 192 * b2 - 1)
+    assert int((tiers == 0).sum()) == 63
+
+
+def test_plan_tiers_properties():
+    rng = np.random.default_rng(14)
+    for _ in range(100):
+        E = int(rng.integers(1, 100))
+        tb = sorted((int(b) for b in rng.integers(1, 1000, size=int(rng.integers(1, 5)))),
+                    reverse=True)
+        counts = rng.integers(0, 20, size=E)
+        budget = int(rng.integers(E * tb[-1], E * tb[0] + 1))
+        tiers, used = oracle.plan_tiers(counts, tb, budget)
+        assert used <= budget
+        order = sorted(range(E), key=lambda e: (-int(counts[e]), e))
+        ranked = tiers[order]
+        assert np.all(np.diff(ranked) >= 0)  # never more precise for a colder expert
+        below = np.flatnonzero(ranked > 0)
+        if below.size:  # the first expert below the top tier cannot move up one tier
+            t = ranked[below[0]]
+            assert used - tb[t] + tb[t - 1] > budget
+    assert oracle.plan_tiers([1, 2, 3], [10, 5], 14) is None
