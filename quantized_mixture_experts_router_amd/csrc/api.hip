@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument checks, workspace carving and dispatch.
 // Every check runs before anything is enqueued; nothing here synchronises.
 #include "common.h"
+#include "profile.h"
 
 using namespace moeq;
 

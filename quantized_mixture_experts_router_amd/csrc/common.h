@@ -240,11 +240,6 @@ hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offs
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);
-hipError_t launch_expert_histogram(const int32_t* ids, long n, int E, int64_t* hist,
-                                   hipStream_t s);
-// host only; false when every expert at the last tier exceeds the budget
-bool plan_tiers(const int64_t* counts, int E, const uint64_t* tier_bytes, int ntiers,
-                uint64_t budget, int32_t* tier_of, uint64_t* used_out);
 hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                               hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,

@@ -14,7 +14,7 @@
 //    reading of "hottest most precise, as far as the budget allows": the
 //    resulting tier vector, read in rank order, is the most precise one
 //    (lexicographically) among all within the budget.
-#include "common.h"
+#include "profile.h"
 
 #include <algorithm>
 #include <numeric>
