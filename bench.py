@@ -269,7 +269,32 @@ def main():
         torch.cuda.synchronize()
         ms_p = (time.perf_counter() - tt0) * 1e3 / args.steps
         del wl_p
+        # three tiers under the same budget: a 1-bit tier for the coldest
+        # experts pays for more 4-bit ones (the digest's precision gradient)
+        one = (1, 1, 16)
+        ex = synth.gen_expert(replace(cfg, expert_fmts=(one,) * E), 0)
+        sizes3 = sizes + [moeq.packed_expert_bytes(
+            *[moeq.DeviceQMat.from_host(ex[r], dev) for r in ("gate", "up", "down")])]
+        tiers3, used3 = moeq.plan_tiers(counts_cal, sizes3, budget)
+        fm3 = (cfg.fmt, cfg.cold_fmt, one)
+        wl_3 = Workload(replace(cfg, expert_fmts=tuple(fm3[t] for t in tiers3)), device=dev)
+        for _ in range(args.warmup):
+            step(pk=wl_3.packed)
+        torch.cuda.synchronize()
+        tt0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(pk=wl_3.packed)
+        torch.cuda.synchronize()
+        ms_3 = (time.perf_counter() - tt0) * 1e3 / args.steps
+        del wl_3
+        three = {"tier_bytes": sizes3, "used_bytes": int(used3),
+                 "experts_per_tier": [int((tiers3 == t).sum()) for t in range(3)],
+                 "slot_share_per_tier": [float(own[tiers3 == t].sum() / own.sum()) for t in range(3)],
+                 "prefill_ms": ms_3}
+        log(f"[bench] tiers, 4/2/1-bit in the same budget: experts {three['experts_per_tier']}, "
+            f"slot shares {[round(v, 3) for v in three['slot_share_per_tier']]}, prefill {ms_3:.3f} ms")
         result["tiers"] = {
+            "three_tier": three,
             "calibration_tokens": T, "hot_experts": int(hot.sum()),
             "tier_bytes": sizes, "budget_bytes": int(budget), "used_bytes": int(used),
             "histogram_ms": hist_ms, "plan_us": plan_us,

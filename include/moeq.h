@@ -56,8 +56,10 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Element formats of a weight block.
- * MOE_W_ASYM: w = s*q + m, q unsigned b-bit (b in {2,4}), fp16 s and m per
- *             group; decoded value rounded once to fp32.
+ * MOE_W_ASYM: w = s*q + m, q unsigned b-bit (b in {1,2,4}), fp16 s and m
+ *             per group; decoded value rounded once to fp32. 1 bit is the
+ *             sub-2-bit tier for the coldest experts (expert-aware
+ *             quantisation digest, conclusion).
  * MOE_W_E2M1: w = e2m1(q) * s, 4-bit OCP-MX e2m1 element (bit 3 sign, two
  *             exponent bits with bias 1, one mantissa bit: magnitudes
  *             0, .5, 1, 1.5, 2, 3, 4, 6), fp16 s per group (the 4-bit
@@ -88,15 +90,15 @@ enum {
  * codes (device): uint8 [rows, row_bytes], row_bytes = cols*bits/8 rounded
  *   up to a multiple of 16 (padding bytes are ignored). 4-bit: element 2i in
  *   the low nibble of byte i, 2i+1 in the high nibble. 2-bit: element 4i+j in
- *   bits [2j, 2j+1] of byte i.
+ *   bits [2j, 2j+1] of byte i. 1-bit: element 8i+j in bit j of byte i.
  * params (device): fp16 [rows, cols/group] scales for MOE_W_E2M1, or
  *   [rows, cols/group] (scale, min) pairs for MOE_W_ASYM, row-major.
- * Supported: ASYM with bits 2 or 4 and group 16/32/64/128; E2M1 with bits 4
+ * Supported: ASYM with bits 1, 2 or 4 and group 16/32/64/128; E2M1 with bits 4
  * and group 16/32/64/128. rows % 32 == 0; cols % 128 == 0; codes 16-byte
  * aligned, params 4-byte aligned. */
 typedef struct {
   uint8_t fmt;    /* moe_wfmt */
-  uint8_t bits;   /* 2 or 4 */
+  uint8_t bits;   /* 1, 2 or 4 */
   uint16_t group; /* 16, 32, 64 or 128 */
   uint32_t rows;
   uint32_t cols;
@@ -141,7 +143,7 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
 /* Bit mask of the block formats used by E packed experts (host array of the
  * descriptors moe_pack_expert filled): bit i is set when some gate/up or
  * down matrix has format i, with i = 4*c + g, c = 0 asym 4-bit, 1 asym 2-bit,
- * 2 e2m1, and g = 0,1,2,3 for group 16, 32, 64, 128. The FFN entry points
+ * 2 e2m1, 3 asym 1-bit, and g = 0,1,2,3 for group 16, 32, 64, 128. The FFN entry points
  * take this mask (fmt_mask) and run one kernel per format in it; 0 means
  * every supported format (correct for any expert set, but each absent format
  * still costs a launch). Experts whose format is missing from a non-zero mask

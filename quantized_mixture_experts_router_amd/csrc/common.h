@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moeq.h"
 
 namespace moeq {
@@ -27,6 +29,7 @@ enum FmtId : int {
   F_A4G16 = 0, F_A4G32, F_A4G64, F_A4G128,
   F_A2G16, F_A2G32, F_A2G64, F_A2G128,
   F_E4G16, F_E4G32, F_E4G64, F_E4G128,
+  F_A1G16, F_A1G32, F_A1G64, F_A1G128,
   F_COUNT
 };
 
@@ -36,13 +39,16 @@ __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   if (fmt == MOE_W_ASYM && bits == 4) return F_A4G16 + g;
   if (fmt == MOE_W_ASYM && bits == 2) return F_A2G16 + g;
   if (fmt == MOE_W_E2M1 && bits == 4) return F_E4G16 + g;
+  if (fmt == MOE_W_ASYM && bits == 1) return F_A1G16 + g;
   return -1;
 }
 
 // Device layout of one packed matrix W[N, K] (N rows = GEMM output columns).
-//  - 32-row tiles; one tile spans KT = 2*SPAN columns; one tile is 1 KiB of
-//    codes: lane l = (n = l % 32, kh = l / 32) holds 16 bytes = SPAN codes of
-//    row n, columns [kt*KT + kh*SPAN, +SPAN).
+//  - 32-row tiles; one tile spans KT = 2*SPAN columns; lane l = (n = l % 32,
+//    kh = l / 32) holds CB bytes = SPAN codes of row n, columns
+//    [kt*KT + kh*SPAN, +SPAN). 4- and 2-bit: CB = 16 (SPAN = 32, 64), a tile
+//    is 1 KiB. 1-bit: CB = 8 (SPAN = 64, KT = 128 like 2-bit, so the prefill
+//    token tile keeps its size), a tile is 512 B.
 //  - Inside each 32-bit word the codes are ordered so that (word >> b*i) &
 //    mask yields the pair (code 2i, code 2i+1) in the two 16-bit halves.
 //  - Tiles are stored row-tile major, then K-tile; gate/up are interleaved
@@ -56,7 +62,10 @@ struct Fmt {
   static constexpr int kFmt = FMT;
   static constexpr int kBits = BITS;
   static constexpr int kGroup = GROUP;
-  static constexpr int SPAN = 128 / BITS;                  // codes per lane per tile
+  static constexpr int SPAN = BITS == 1 ? 64 : 128 / BITS;  // codes per lane per tile
+  static constexpr int CB = SPAN * BITS / 8;                // code bytes per lane per tile
+  static constexpr int TB = 64 * CB;                        // code bytes per tile
+  using CodeT = typename std::conditional<CB == 16, u32x4, u32x2>::type;
   static constexpr int KT = 2 * SPAN;                      // K columns per tile
   static constexpr int STEPS = SPAN / 8;                   // 32x32x16 MFMA steps per tile
   static constexpr int GE = GROUP > SPAN ? GROUP : SPAN;   // K columns per param entry
@@ -65,11 +74,12 @@ struct Fmt {
   static constexpr int EB = NP * PSZ;                      // entry bytes
 };
 
-__host__ __device__ inline int fmt_span(int bits) { return 128 / bits; }
-__host__ __device__ inline int fmt_kt(int bits) { return 256 / bits; }
+__host__ __device__ inline int fmt_span(int bits) { return bits == 1 ? 64 : 128 / bits; }
+__host__ __device__ inline int fmt_kt(int bits) { return 2 * fmt_span(bits); }
+__host__ __device__ inline int fmt_cb(int bits) { return fmt_span(bits) * bits / 8; }
 
 inline size_t packed_codes_bytes(int N, int K, int bits) {
-  return (size_t)(N / 32) * (size_t)(K / fmt_kt(bits)) * 1024;
+  return (size_t)(N / 32) * (size_t)(K / fmt_kt(bits)) * 64 * fmt_cb(bits);
 }
 inline size_t packed_params_bytes(int N, int K, int fmt, int bits, int group) {
   int span = fmt_span(bits);

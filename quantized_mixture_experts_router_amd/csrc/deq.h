@@ -2,9 +2,11 @@
 //
 // Asymmetric blocks (w = s*q + m; AWQ-style zero point of the "sparse
 // activation" page, section 4.4; the per-expert bit widths of the AlphaQ blog,
-// section 4.2): a pair of b-bit codes is OR-ed into the mantissas of two fp16
-// numbers (exact), the fp16 offset is subtracted (exact), and one packed fp16
-// fma applies the group scale and minimum (one rounding to fp16).
+// section 4.2; 1-bit for the coldest experts, the sub-2-bit tier of the
+// expert-aware quantisation digest's conclusion): a pair of b-bit codes is
+// OR-ed into the mantissas of two fp16 numbers (exact), the fp16 offset is
+// subtracted (exact), and one packed fp16 fma applies the group scale and
+// minimum (one rounding to fp16).
 // e2m1 blocks (the 4-bit floating-point weights of the quantized-MoE
 // article): the gfx950 fp4 converter yields the exact fp16 value of each code,
 // then one fp16 multiply by the group scale (one rounding).
@@ -97,7 +99,7 @@ __device__ inline DeqConsts make_deq_consts() {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int off = F::kBits * j;
-    const bool used = F::kFmt == MOE_W_ASYM && (F::kBits == 2 || j < 2);
+    const bool used = F::kFmt == MOE_W_ASYM && (F::kBits <= 2 || j < 2);
     const uint32_t mk = ((fm << off) | (fm << (16 + off)));
     const uint32_t e = 25u - off;  // fp16 exponent field of 2^(10 - off)
     const uint32_t mg = (e << 10) | (e << 26);
@@ -116,7 +118,7 @@ __device__ inline f16x2 magic_sub(int off) {
 // Decode the 8 codes of MFMA step `s` from a lane's 16-byte code block into
 // the fp16 B fragment (values in the K order the packer laid out).
 template <class F>
-__device__ inline f16x8 dequant_step(const u32x4& c, const PBuf<F::EB>& pb, int s,
+__device__ inline f16x8 dequant_step(const typename F::CodeT& c, const PBuf<F::EB>& pb, int s,
                                      const DeqConsts& k) {
   // parameter index inside the entry for lane-local codes [8s, 8s+8)
   const int p = F::kGroup < F::SPAN ? (8 * s) / F::kGroup : 0;
@@ -135,6 +137,15 @@ __device__ inline f16x8 dequant_step(const u32x4& c, const PBuf<F::EB>& pb, int 
         const int j = i & 1;
         const uint32_t t = (src & k.mask[j]) | k.magic[j];
         out[i] = __builtin_elementwise_fma(as_f16x2(t) + magic_sub(4 * j), s2, m2);
+      }
+    } else if (F::kBits == 1) {
+      // word s/4 holds four steps; step s uses bits 4q..4q+3 of each 16-bit
+      // half, q = s & 3 (bits of the other half shifted in stay masked out)
+      const uint32_t src = c[s >> 2] >> (4 * (s & 3));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = (src & k.mask[j]) | k.magic[j];
+        out[j] = __builtin_elementwise_fma(as_f16x2(t) + magic_sub(j), s2, m2);
       }
     } else {
       // word s/2 holds two steps; step s uses offsets 0, 2, 4, 6 of byte (s & 1)

@@ -58,6 +58,10 @@ template <> struct FmtOf<F_E4G16> { using T = Fmt<MOE_W_E2M1, 4, 16>; };
 template <> struct FmtOf<F_E4G32> { using T = Fmt<MOE_W_E2M1, 4, 32>; };
 template <> struct FmtOf<F_E4G64> { using T = Fmt<MOE_W_E2M1, 4, 64>; };
 template <> struct FmtOf<F_E4G128> { using T = Fmt<MOE_W_E2M1, 4, 128>; };
+template <> struct FmtOf<F_A1G16> { using T = Fmt<MOE_W_ASYM, 1, 16>; };
+template <> struct FmtOf<F_A1G32> { using T = Fmt<MOE_W_ASYM, 1, 32>; };
+template <> struct FmtOf<F_A1G64> { using T = Fmt<MOE_W_ASYM, 1, 64>; };
+template <> struct FmtOf<F_A1G128> { using T = Fmt<MOE_W_ASYM, 1, 128>; };
 
 __device__ inline f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -302,7 +306,7 @@ __device__ inline void store_dn(const FfnArgs& a, int split, int row, int col, f
 
 template <class F>
 struct BTile {
-  u32x4 w0, w1;
+  typename F::CodeT w0, w1;
   PBuf<F::EB> q0, q1;
 };
 
@@ -333,8 +337,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
   const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
   const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
-  const uint8_t* c0 = codes + (size_t)rt0 * KTn * 1024 + lane * 16;
-  const uint8_t* c1 = c0 + (size_t)KTn * 1024;
+  const uint8_t* c0 = codes + (size_t)rt0 * KTn * F::TB + lane * F::CB;
+  const uint8_t* c1 = c0 + (size_t)KTn * F::TB;
   const uint8_t* p0 = params + ((size_t)rt0 * NE * 32 + n) * F::EB;
   const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
 
@@ -356,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   auto tile_of = [&](int i) { return min(kb + ks + ksw * i, KTn - 1); };
   auto load_b = [&](int i, BTile<F>& b) {
     const int kt = tile_of(i);
-    b.w0 = ldg<true, u32x4>(c0 + (size_t)kt * 1024);
-    b.w1 = ldg<true, u32x4>(c1 + (size_t)kt * 1024);
+    b.w0 = ldg<true, typename F::CodeT>(c0 + (size_t)kt * F::TB);
+    b.w1 = ldg<true, typename F::CodeT>(c1 + (size_t)kt * F::TB);
     const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
     b.q0.template load<true>(p0 + (size_t)ei * 32 * F::EB);
     b.q1.template load<true>(p1 + (size_t)ei * 32 * F::EB);
@@ -506,8 +510,8 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
   // every wavefront runs the same straight-line loop
   const int rt0 = 2 * unit;
   const int rtl = 2 * min(unit, NU - 1);
-  const uint8_t* c0 = codes + (size_t)rtl * KTn * 1024 + lane * 16;
-  const uint8_t* c1 = c0 + (size_t)KTn * 1024;
+  const uint8_t* c0 = codes + (size_t)rtl * KTn * F::TB + lane * F::CB;
+  const uint8_t* c1 = c0 + (size_t)KTn * F::TB;
   const uint8_t* p0 = params + ((size_t)rtl * NE * 32 + n) * F::EB;
   const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
 
@@ -537,8 +541,8 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
           (__attribute__((address_space(3))) void*)(buf + (wave * NI + j) * 1024), 16, 0, 0);
   };
   auto load_b = [&](int kt, BTile<F>& b) {
-    b.w0 = ldg<kPrefillNT, u32x4>(c0 + (size_t)kt * 1024);
-    b.w1 = ldg<kPrefillNT, u32x4>(c1 + (size_t)kt * 1024);
+    b.w0 = ldg<kPrefillNT, typename F::CodeT>(c0 + (size_t)kt * F::TB);
+    b.w1 = ldg<kPrefillNT, typename F::CodeT>(c1 + (size_t)kt * F::TB);
     const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
     b.q0.template load<kPrefillNT>(p0 + (size_t)ei * 32 * F::EB);
     b.q1.template load<kPrefillNT>(p1 + (size_t)ei * 32 * F::EB);
@@ -779,6 +783,10 @@ hipError_t launch_all(const FfnArgs& a, bool decode, hipStream_t s) {
   MOEQ_LAUNCH(F_E4G32)
   MOEQ_LAUNCH(F_E4G64)
   MOEQ_LAUNCH(F_E4G128)
+  MOEQ_LAUNCH(F_A1G16)
+  MOEQ_LAUNCH(F_A1G32)
+  MOEQ_LAUNCH(F_A1G64)
+  MOEQ_LAUNCH(F_A1G128)
 #undef MOEQ_LAUNCH
   return e;
 }

@@ -6,7 +6,8 @@
 // that the weight reads are contiguous (MoE mixed-precision notes, sections
 // 2.3 and 3.5). Here the stream is cut into 1 KiB tiles of 32 rows that a
 // 64-lane wavefront reads with one 16-byte load per lane, already in the
-// order the matrix-core B operand consumes them.
+// order the matrix-core B operand consumes them (512 B tiles of 8 bytes per
+// lane for 1-bit codes).
 #include "common.h"
 
 namespace moeq {
@@ -30,9 +31,9 @@ __device__ inline uint32_t get_field(const uint32_t* w, int idx, int bits) {
   return (w[idx / per] >> ((idx % per) * bits)) & ((1u << bits) - 1u);
 }
 
-// one thread = one lane slot (16 bytes) of one tile
+// one thread = one lane slot (16 or 8 bytes) of one tile
 __global__ void pack_codes_kernel(PackArgs a) {
-  const int span = 128 / a.bits, KT = 2 * span;
+  const int span = fmt_span(a.bits), KT = 2 * span, cb = fmt_cb(a.bits);
   const int KTn = a.K / KT;
   const int NT = a.N / 32;  // row tiles per source
   const long total = (long)NT * a.nsrc * KTn * 64;
@@ -50,12 +51,17 @@ __global__ void pack_codes_kernel(PackArgs a) {
   size_t rb = ((size_t)a.K * a.bits / 8 + 15) / 16 * 16;
   const uint32_t* s =
       reinterpret_cast<const uint32_t*>(a.src_codes[src] + (size_t)row * rb + (size_t)k0 * a.bits / 8);
-  uint32_t w[4] = {s[0], s[1], s[2], s[3]};
+  const int nw = cb / 4;  // 32-bit words per lane slot
+  uint32_t w[4] = {s[0], s[1], 0u, 0u};
+  if (nw > 2) {
+    w[2] = s[2];
+    w[3] = s[3];
+  }
   uint32_t out[4];
-  const int per = 32 / a.bits;        // codes per word (8 or 16)
+  const int per = 32 / a.bits;        // codes per word (8, 16 or 32)
   const int half = per / 2;
   const bool pairs = a.fmt == MOE_W_ASYM;  // e2m1 keeps the natural order
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < nw; ++d) {
     uint32_t v = 0;
     for (int p = 0; p < per; ++p) {
       // asymmetric: field p of word d holds code per*d + (p < half ? 2p : 2(p-half)+1),
@@ -65,16 +71,13 @@ __global__ void pack_codes_kernel(PackArgs a) {
     }
     out[d] = v;
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + ((size_t)vrt * KTn + kt) * 1024 + lane * 16);
-  dst[0] = out[0];
-  dst[1] = out[1];
-  dst[2] = out[2];
-  dst[3] = out[3];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + ((size_t)vrt * KTn + kt) * 64 * cb + lane * cb);
+  for (int d = 0; d < nw; ++d) dst[d] = out[d];
 }
 
 // one thread = one (row, entry)
 __global__ void pack_params_kernel(PackArgs a) {
-  const int span = 128 / a.bits;
+  const int span = fmt_span(a.bits);
   const int ge = a.group > span ? a.group : span;
   const int np = a.group < span ? span / a.group : 1;
   const int psz = a.fmt == MOE_W_ASYM ? 4 : 2;
@@ -118,7 +121,7 @@ hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b, void* codes,
   pa.group = a->group;
   pa.codes = (uint8_t*)codes;
   pa.params = (uint8_t*)params;
-  const int span = 128 / pa.bits, KT = 2 * span;
+  const int span = fmt_span(pa.bits), KT = 2 * span;
   long nc = (long)(pa.N / 32) * pa.nsrc * (pa.K / KT) * 64;
   hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, pa);
   hipError_t e = hipGetLastError();

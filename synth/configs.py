@@ -47,6 +47,8 @@ class LayerConfig:
 A4G32 = (FMT_ASYM, 4, 32)
 A2G16 = (FMT_ASYM, 2, 16)
 A4G128 = (FMT_ASYM, 4, 128)
+A1G16 = (FMT_ASYM, 1, 16)
+A1G32 = (FMT_ASYM, 1, 32)
 E2M1G16 = (FMT_E2M1, 4, 16)
 
 # Router bias strength for the hot/cold workload: with alpha = 0.375 the 32

@@ -67,8 +67,12 @@ def _pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
         packed = q[:, 0::2] | (q[:, 1::2] << 4)
     elif bits == 2:
         packed = q[:, 0::4] | (q[:, 1::4] << 2) | (q[:, 2::4] << 4) | (q[:, 3::4] << 6)
+    elif bits == 1:
+        packed = np.zeros((rows, cols // 8), dtype=np.uint8)
+        for j in range(8):
+            packed |= q[:, j::8] << j
     else:
-        raise ValueError("bits must be 2 or 4")
+        raise ValueError("bits must be 1, 2 or 4")
     out[:, : packed.shape[1]] = packed
     return out
 

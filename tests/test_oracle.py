@@ -30,7 +30,7 @@ def _qmat_from_golden(d):
 
 
 # ---------------------------------------------------------------- blocks
-@pytest.mark.parametrize("key", ["asym4_g32", "asym2_g16", "e2m1_g16"])
+@pytest.mark.parametrize("key", ["asym4_g32", "asym2_g16", "asym1_g16", "e2m1_g16"])
 def test_decode_hand_worked_blobs(key):
     d = _golden("blob_examples.json")[key]
     got = oracle.decode_qmat(_qmat_from_golden(d))
@@ -51,7 +51,8 @@ def test_e2m1_code_table():
     assert np.array_equal(np.signbit(got), np.signbit(np.array(g["code_to_value"])))
 
 
-@pytest.mark.parametrize("bits,group", [(4, 16), (4, 32), (4, 64), (4, 128), (2, 16), (2, 32), (2, 128)])
+@pytest.mark.parametrize("bits,group", [(4, 16), (4, 32), (4, 64), (4, 128), (2, 16), (2, 32), (2, 128),
+                                        (1, 16), (1, 32), (1, 128)])
 def test_asym_zero_error_roundtrip(bits, group):
     """Weights built exactly representable (s = 2^-j, m = n*2^-j, every group
     using codes 0 and 2^b-1) survive quantise -> decode bit-exactly, and the
