@@ -225,6 +225,43 @@ def main():
         "split_api_equals_layer_forward": same,
     }
 
+    # ------------------------------------------------------- int8 router logits
+    # The int8 router variant: calibrated on T held-out tokens (the rows
+    # after the bench's own), then measured on the bench's tokens against the
+    # exact routing of the timed steps: tokens whose k experts are the same
+    # set, and the share of (token, expert) assignments kept.
+    if not args.decode_only:
+        x_cal = x_to_torch(synth.gen_x(cfg, 2 * T)[T:], cfg.x_dtype, dev)
+        lo, hi = moeq.router_logit_range(x_cal, wl.Wr, wl.b)
+        ids_ex = ids_.cpu().numpy()
+        r8 = {"calibration_tokens": T}
+        for shared in (False, True):
+            sc, zp = moeq.router_i8_params(lo, hi, shared)
+            sc_d, zp_d = torch.from_numpy(sc).to(dev), torch.from_numpy(zp).to(dev)
+            ids8, _ = moeq.route_i8(wl.x, wl.Wr, wl.b, k, sc_d, zp_d)
+            i8 = ids8.cpu().numpy()
+            same = float(np.mean([set(a) == set(c) for a, c in zip(i8, ids_ex)]))
+            kept = float(np.mean([len(set(a) & set(c)) / k for a, c in zip(i8, ids_ex)]))
+            r8["per_expert" if not shared else "shared"] = {"same_expert_set": same,
+                                                           "assignments_kept": kept}
+        times = {}
+        for name, fn in (("route_ms", lambda: moeq.route(wl.x, wl.Wr, wl.b, k)),
+                         ("route_i8_ms", lambda: moeq.route_i8(wl.x, wl.Wr, wl.b, k, sc_d, zp_d))):
+            fn()
+            step()  # queued work ahead of the events
+            a0, a1 = event(), event()
+            a0.record()
+            for _ in range(10):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            times[name] = a0.elapsed_time(a1) / 10
+        r8.update(times)
+        result["router_i8"] = r8
+        log(f"[bench] int8 router logits: same expert set on {r8['per_expert']['same_expert_set']:.3f} "
+            f"of tokens per-expert scales, {r8['shared']['same_expert_set']:.3f} shared; route "
+            f"{times['route_ms'] * 1e3:.1f} us, route_i8 {times['route_i8_ms'] * 1e3:.1f} us")
+
     # ------------------------------------------------------------------ tiers
     # Expert-aware precision from a routing profile: the routing of T held-out
     # calibration tokens (the T rows after the bench's own) is counted on the

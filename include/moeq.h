@@ -255,6 +255,39 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
 moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,
                             void* stream);
 
+/* int8 router logits (the "AlphaQ" blog, sections 2.2 and 4.1, DRAQ: leave
+ * the router's weights alone and quantise its output logits to int8 with a
+ * scale and zero point calibrated on real data). A variant of
+ * moe_route that trades routing exactness for int8 logits: it is measured
+ * against the exact routing, not used by moe_layer_forward.
+ *
+ * moe_router_logit_range: the fp64 logits of the T tokens (as moe_route
+ *   computes them), merged into the per-expert running minimum lo[E] and
+ *   maximum hi[E] (device, double; the caller starts them at +inf / -inf).
+ *   NaN logits are skipped. Same arguments, constraints and workspace as
+ *   moe_route.
+ * moe_router_i8_params (host only): from lo[E] <= hi[E] (host, finite), per
+ *   expert (shared == 0; the per-output-channel parameters of the blog's
+ *   section 2.2) or for the range over all experts (shared != 0; one scale
+ *   and zero point, so the int8 codes themselves rank as the top-k "in int8
+ *   space" of section 4.1): scale s = fp32((hi - lo) / 255), at least the
+ *   smallest normal fp32, and zero point z = -128 - rint(lo / s) (int32,
+ *   saturated), so lo maps to code -128 and hi to 126 or 127.
+ * moe_route_i8: as moe_route, except that the top-k and the softmax use
+ *   each logit after an int8 round trip, (clamp(rint(L/s) + z, -128, 127) - z)
+ *   * s in fp64 (round half to even); experts with s <= 0 get 0. Equal
+ *   values go to the lower expert index. scale (device, fp32 [E]) and zero
+ *   (device, int32 [E]) as moe_router_i8_params gives them. logits
+ *   (optional) receives the logits before the round trip. */
+moe_status moe_router_logit_range(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                                  int T, int H, int E, double* lo, double* hi, void* ws,
+                                  size_t ws_bytes, void* stream);
+moe_status moe_router_i8_params(const double* lo, const double* hi, int E, int shared,
+                                float* scale, int32_t* zero);
+moe_status moe_route_i8(const void* x, moe_dtype xdt, const float* Wr, const float* b, int T, int H,
+                        int E, int k, const float* scale, const int32_t* zero, int32_t* topk_ids,
+                        float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream);
+
 /* Routing profile for expert-aware precision (expert-aware quantisation
  * digest, profiling and results sections: a profiling run over task data
  * marks the experts the router actually uses as hot and keeps them at higher

@@ -18,6 +18,10 @@ Sources (pages as titled; sections as numbered on each page):
   [FFN]       "AlphaQ" blog, section 2.2 and the mixed-precision notes,
               section 3.3: each expert is a three-matrix FFN (gate, up/middle,
               down/output); its gated form is SwiGLU.
+  [DRAQ]      "AlphaQ" blog, sections 2.2 and 4.1: the router's output
+              logits, not its weights, are quantised to int8 with a scale and
+              zero point calibrated on real data (range / 255), per output
+              channel, and the top-k runs on the quantised values.
   [Tiers]     expert-aware quantisation digest, profiling, results and
               conclusion sections: profile which experts the router uses,
               keep the most used ones precise and the rest at 2 bits, and
@@ -301,3 +305,64 @@ def plan_tiers(counts, tier_bytes, budget: int):
         tiers[e] = t
         used += tier_bytes[t]
     return np.array(tiers, dtype=np.int32), used
+
+
+# --------------------------------------------------------------------------
+# int8 router logits [DRAQ]
+# --------------------------------------------------------------------------
+def router_logit_range(L: np.ndarray):
+    """Per expert, the smallest and largest logit over the tokens (NaN logits
+    skipped; +inf / -inf when an expert has none)."""
+    L = np.asarray(L, dtype=np.float64)
+    lo = np.full(L.shape[1], np.inf)
+    hi = np.full(L.shape[1], -np.inf)
+    for e in range(L.shape[1]):
+        col = L[:, e][~np.isnan(L[:, e])]
+        if col.size:
+            lo[e], hi[e] = col.min(), col.max()
+    return lo, hi
+
+
+def router_i8_params(lo, hi, shared: bool = False):
+    """Scale s = fp32((hi - lo) / 255), at least the smallest normal fp32, and
+    zero point z = -128 - rint(lo / s) saturated to int32: lo maps to code
+    -128. With shared, one pair from the range over all experts."""
+    lo = np.asarray(lo, dtype=np.float64)
+    hi = np.asarray(hi, dtype=np.float64)
+    if shared:
+        lo = np.full_like(lo, lo.min())
+        hi = np.full_like(hi, hi.max())
+    s = ((hi - lo) / 255.0).astype(np.float32)
+    s = np.maximum(s, np.finfo(np.float32).tiny)
+    z = -128.0 - np.rint(lo / s.astype(np.float64))
+    return s, np.clip(z, -2.0**31, 2.0**31 - 1).astype(np.int64)  # int32, saturated
+
+
+def quantize_logits_i8(L, scale, zero):
+    """Logits after the int8 round trip (clamp(rint(L/s) + z, -128, 127) - z) * s
+    (fp64 division, round half to even; experts with s <= 0 give 0), and per
+    token whether some L/s lies within 1e-9 of a rounding boundary, where the
+    order of an fp64 sum could decide the code."""
+    L = np.asarray(L, dtype=np.float64)
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)[None, :]
+    z = np.asarray(zero, dtype=np.float64)[None, :]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = L / s
+    q = np.clip(np.rint(r) + z, -128.0, 127.0)
+    Lq = np.where(s > 0, (q - z) * s, 0.0)
+    with np.errstate(invalid="ignore"):
+        amb = (s > 0) & (np.abs(r - np.floor(r) - 0.5) < 1e-9)
+    return Lq, amb.any(axis=1)
+
+
+def topk_softmax_i8(L, scale, zero, k: int):
+    """Routing on the int8 round trip of the logits: stable top-k (equal
+    values to the lower index) and softmax over the selected quantised
+    logits. Returns ids, w, and the tokens to exclude (rounding ambiguous)."""
+    L = np.asarray(L, dtype=np.float64)
+    nan_row = np.isnan(L).any(axis=1)
+    Lq, amb = quantize_logits_i8(np.where(nan_row[:, None], 0.0, L), scale, zero)
+    ids, w, _, _ = topk_softmax(Lq, k)
+    ids[nan_row] = -2  # undefined routing, as for the unquantised router
+    w[nan_row] = 0.0
+    return ids, w, amb

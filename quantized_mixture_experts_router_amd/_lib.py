@@ -72,6 +72,9 @@ _SIGS = {
     "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "moe_expert_histogram": ([_vp, _i, _i, _i, _vp, _vp], _i),
     "moe_plan_tiers": ([_vp, _i, _vp, _i, ctypes.c_uint64, _vp, _vp], _i),
+    "moe_router_logit_range": ([_vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_router_i8_params": ([_vp, _vp, _i, _i, _vp, _vp], _i),
+    "moe_route_i8": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
 }
 
 
@@ -359,3 +362,51 @@ def plan_tiers(counts, tier_bytes, budget):
                               ctypes.c_uint64(int(budget)), out.ctypes.data, ctypes.byref(used)),
            "moe_plan_tiers")
     return out, used.value
+
+
+def router_logit_range(x, Wr, b, lo=None, hi=None, ws=None):
+    """Per-expert running min / max (device fp64 [E]) of the router logits of
+    x, merged into lo / hi (new +inf / -inf ones if None); returns (lo, hi)."""
+    x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
+    T, H = x.shape
+    E = Wr.shape[0]
+    if lo is None:
+        lo = torch.full((E,), float("inf"), dtype=torch.float64, device=x.device)
+    if hi is None:
+        hi = torch.full((E,), float("-inf"), dtype=torch.float64, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(route_workspace_size(T, H, E), 256), dtype=torch.uint8, device=x.device)
+    _check(LIB.moe_router_logit_range(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), T, H, E, _ptr(lo), _ptr(hi),
+                                      _ptr(ws), ws.numel(), _stream()), "moe_router_logit_range")
+    return lo, hi
+
+
+def router_i8_params(lo, hi, shared=False):
+    """int8 scale (fp32) and zero point (int32) per expert from a logit range
+    (host arrays or tensors); returns numpy arrays."""
+    lo = np.ascontiguousarray(np.asarray(lo.cpu() if hasattr(lo, "cpu") else lo, dtype=np.float64))
+    hi = np.ascontiguousarray(np.asarray(hi.cpu() if hasattr(hi, "cpu") else hi, dtype=np.float64))
+    E = lo.shape[0]
+    scale = np.empty(E, dtype=np.float32)
+    zero = np.empty(E, dtype=np.int32)
+    _check(LIB.moe_router_i8_params(lo.ctypes.data, hi.ctypes.data, E, int(bool(shared)),
+                                    scale.ctypes.data, zero.ctypes.data), "moe_router_i8_params")
+    return scale, zero
+
+
+def route_i8(x, Wr, b, k, scale, zero, want_logits=False, ws=None):
+    """moe_route with the int8 round trip of the logits (scale fp32 [E],
+    zero int32 [E], device tensors)."""
+    x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
+    scale, zero = _dev(scale, "scale"), _dev(zero, "zero")
+    T, H = x.shape
+    E = Wr.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    if ws is None:
+        ws = torch.empty(max(route_workspace_size(T, H, E), 256), dtype=torch.uint8, device=x.device)
+    _check(LIB.moe_route_i8(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), T, H, E, k, _ptr(scale), _ptr(zero),
+                            _ptr(ids), _ptr(w), _ptr(logits), _ptr(ws), ws.numel(), _stream()),
+           "moe_route_i8")
+    return (ids, w, logits) if want_logits else (ids, w)

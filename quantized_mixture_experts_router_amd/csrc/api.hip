@@ -218,6 +218,65 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
                                  (double*)ws, (hipStream_t)stream));
 }
 
+static moe_status check_route_args(const void* x, moe_dtype xdt, const float* Wr, int T, int H,
+                                   int E, void* ws, size_t ws_bytes) {
+  if (T < 0 || H <= 0 || E <= 0 || E > kMaxE) return MOE_ERR_INVALID_ARG;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (H % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < moe_route_workspace_size(T, H, E)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status moe_route_i8(const void* x, moe_dtype xdt, const float* Wr, const float* b, int T, int H,
+                        int E, int k, const float* scale, const int32_t* zero, int32_t* topk_ids,
+                        float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  if (k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_route_args(x, xdt, Wr, T, H, E, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!scale || !zero || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, (double*)ws, s));
+  return hip_status(launch_route_topk_q((const double*)ws, route_plan(T, H, E).kb, b, T, E, k, scale,
+                                        zero, topk_ids, topk_w, logits, s));
+}
+
+moe_status moe_router_logit_range(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                                  int T, int H, int E, double* lo, double* hi, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  moe_status st = check_route_args(x, xdt, Wr, T, H, E, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!lo || !hi) return MOE_ERR_INVALID_ARG;
+  if (!aligned(lo, 8) || !aligned(hi, 8)) return MOE_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, (double*)ws, s));
+  return hip_status(
+      launch_logit_range((const double*)ws, route_plan(T, H, E).kb, b, T, E, lo, hi, s));
+}
+
+moe_status moe_router_i8_params(const double* lo, const double* hi, int E, int shared,
+                                float* scale, int32_t* zero) {
+  if (!lo || !hi || !scale || !zero || E < 1 || E > kMaxE) return MOE_ERR_INVALID_ARG;
+  double glo = lo[0], ghi = hi[0];
+  for (int e = 0; e < E; ++e) {
+    const double a = lo[e], b = hi[e];
+    if (!(a <= b) || a < -1e30 || b > 1e30) return MOE_ERR_INVALID_ARG;
+    glo = a < glo ? a : glo;
+    ghi = b > ghi ? b : ghi;
+  }
+  for (int e = 0; e < E; ++e) {
+    const double a = shared ? glo : lo[e], b = shared ? ghi : hi[e];
+    float sc = (float)((b - a) / 255.0);
+    if (!(sc >= 1.17549435e-38f)) sc = 1.17549435e-38f;  // smallest normal fp32
+    const double z = -128.0 - rint(a / (double)sc);
+    scale[e] = sc;
+    zero[e] = (int32_t)(z < -2147483648.0 ? -2147483648.0 : (z > 2147483647.0 ? 2147483647.0 : z));
+  }
+  return MOE_OK;
+}
+
 size_t moe_permute_workspace_size(int T, int k, int E) {
   if (T < 0 || k < 1 || E <= 0 || (long)T * k > (1L << 30)) return 0;
   return 256 + permute_plan(T * k, E).scratch_bytes;

@@ -166,15 +166,14 @@ __device__ inline uint64_t wave_max_u64(uint64_t k) {
 // among the token's logits makes its routing undefined: every slot gets
 // MOE_ID_NAN and weight 0. logits_out (optional) receives the fp32 logits;
 // ids_lds (optional, LDS) a copy of the ids.
-__device__ inline void topk_token(const double* __restrict__ P, int KB, const float* __restrict__ bias,
-                                  int T, int E, int k, int t, int32_t* __restrict__ ids_out,
-                                  float* __restrict__ w_out, float* __restrict__ logits_out,
-                                  int32_t* ids_lds = nullptr) {
+// Token t's logits L[t, lane + 64 j] (j < 4, clamped to E-1 past E) into
+// cand[]: the KB fp64 partials added in kb order, then the bias.
+__device__ inline void token_logits(const double* __restrict__ P, int KB,
+                                    const float* __restrict__ bias, int T, int E, int t,
+                                    int ec[4], double cand[4]) {
   const int lane = threadIdx.x & 63;
   const size_t stride = (size_t)T * E;
   const double* row = P + (size_t)t * E;
-  int ec[4];
-  double cand[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     ec[j] = min(lane + 64 * j, E - 1);
@@ -193,14 +192,40 @@ __device__ inline void topk_token(const double* __restrict__ P, int KB, const fl
       for (int j = 0; j < 4; ++j)
         if (q0 + u < KB) cand[j] += pv[u][j];
   }
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cand[j] += (double)bias[ec[j]];
+  }
+}
+
+// qscale/qzero (optional, per expert; the int8 router logits of the AlphaQ
+// blog's DRAQ, section 4.1): the router ranks and weighs the logits after an
+// affine int8 round trip, (clamp(rint(L/s) + z, -128, 127) - z) * s, in
+// fp64; experts with s <= 0 (or NaN) get 0. NaN detection and logits_out use
+// the logits before it.
+__device__ inline void topk_token(const double* __restrict__ P, int KB, const float* __restrict__ bias,
+                                  int T, int E, int k, int t, int32_t* __restrict__ ids_out,
+                                  float* __restrict__ w_out, float* __restrict__ logits_out,
+                                  int32_t* ids_lds = nullptr, const float* __restrict__ qscale = nullptr,
+                                  const int32_t* __restrict__ qzero = nullptr) {
+  const int lane = threadIdx.x & 63;
+  int ec[4];
+  double cand[4];
+  token_logits(P, KB, bias, T, E, t, ec, cand);
   bool nan_seen = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (bias) cand[j] += (double)bias[ec[j]];
     const int e = lane + 64 * j;
     if (e < E) {
       nan_seen |= cand[j] != cand[j];
       if (logits_out) logits_out[(size_t)t * E + e] = (float)cand[j];
+    }
+    if (qscale) {
+      const double sc = (double)qscale[ec[j]];
+      const double z = (double)qzero[ec[j]];
+      double q = rint(cand[j] / sc) + z;
+      q = q < -128.0 ? -128.0 : (q > 127.0 ? 127.0 : q);
+      cand[j] = sc > 0.0 ? (q - z) * sc : 0.0;
     }
   }
   uint32_t taken = 0;

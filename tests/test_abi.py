@@ -205,3 +205,46 @@ def test_expert_histogram_rejects():
     assert L.moe_expert_histogram(p(16), 4, 2, 257, p(16), None) == -1
     assert L.moe_expert_histogram(p(16), -1, 2, 8, p(16), None) == -1
     assert L.moe_expert_histogram(p(16), 4, 2, 8, p(12), None) == -3
+
+
+def test_router_i8_params_matches_oracle():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(41)
+    for shared in (False, True):
+        for _ in range(50):
+            E = int(rng.integers(1, 257))
+            lo = rng.uniform(-5, 2, size=E)
+            hi = lo + rng.choice([0.0, 1e-3, 1.0, 7.0], size=E)
+            s, z = moeq.router_i8_params(lo, hi, shared)
+            s0, z0 = oracle.router_i8_params(lo, hi, shared)
+            np.testing.assert_array_equal(s, s0)
+            np.testing.assert_array_equal(z, z0)
+
+
+def test_router_i8_rejects():
+    import numpy as np
+    L = _lib.LIB
+    lo = np.zeros(4)
+    hi = np.ones(4)
+    s = np.zeros(4, dtype=np.float32)
+    z = np.zeros(4, dtype=np.int32)
+    call = lambda lo_, hi_, E=4: L.moe_router_i8_params(lo_.ctypes.data, hi_.ctypes.data, E, 0,
+                                                        s.ctypes.data, z.ctypes.data)
+    assert call(lo, hi) == 0
+    assert call(hi, lo) == -1                       # lo > hi
+    assert call(lo, np.array([1, 1, np.nan, 1.0])) == -1
+    assert call(lo, hi, E=0) == -1
+    p = ctypes.c_void_p
+    # route_i8 / logit range check their arguments like moe_route
+    assert L.moe_route_i8(p(16), 1, p(16), None, 4, 64, 8, 0, p(16), p(16), p(16), p(16), None,
+                          p(256), 1 << 20, None) == -1          # k = 0
+    assert L.moe_route_i8(p(16), 1, p(16), None, 4, 64, 8, 2, None, p(16), p(16), p(16), None,
+                          p(256), 1 << 20, None) == -1          # no scale
+    assert L.moe_route_i8(p(16), 1, p(16), None, 4, 64, 8, 2, p(16), p(16), p(16), p(16), None,
+                          p(256), 0, None) == -4                # workspace
+    assert L.moe_router_logit_range(p(16), 1, p(16), None, 4, 64, 8, None, p(16), p(256), 1 << 20,
+                                    None) == -1
+    assert L.moe_router_logit_range(p(16), 1, p(16), None, 4, 64, 8, p(12), p(16), p(256), 1 << 20,
+                                    None) == -3
+    assert L.moe_router_logit_range(p(16), 1, p(16), None, 0, 64, 8, None, None, None, 0, None) == 0

@@ -500,3 +500,36 @@ def test_layer_parity_one_bit_tiers(moeq, name, T, H, I, E, k):
     err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
     _say(f"    max row rel-L2 {err.max():.3e}")
     assert err.max() <= tolerance(cfg)
+
+
+# ------------------------------------------------------------ int8 router logits
+@pytest.mark.parametrize("T,H,E,k,shared", [(1, 256, 8, 2, False), (300, 512, 64, 6, False),
+                                            (2000, 1024, 256, 8, True), (64, 4096, 8, 2, True)])
+def test_router_i8_parity(moeq, T, H, E, k, shared):
+    _say(f"[router-i8] T={T} H={H} E={E} k={k} shared={shared}")
+    rng = np.random.default_rng(T + E)
+    x_np = rng.standard_normal((2 * T, H), dtype=np.float32)
+    Wr_np = (rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
+    b_np = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    x = torch.from_numpy(x_np).cuda()
+    Wr, b = torch.from_numpy(Wr_np).cuda(), torch.from_numpy(b_np).cuda()
+    # calibration range over two calls (the first T rows, then the rest)
+    lo, hi = moeq.router_logit_range(x[:T], Wr, b)
+    lo, hi = moeq.router_logit_range(x[T:], Wr, b, lo, hi)
+    torch.cuda.synchronize()
+    L = oracle.router_logits(x_np.astype(np.float64), Wr_np, b_np)
+    lo0, hi0 = oracle.router_logit_range(L)
+    np.testing.assert_allclose(lo.cpu().numpy(), lo0, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(hi.cpu().numpy(), hi0, rtol=1e-12, atol=1e-15)
+    s, z = moeq.router_i8_params(lo0, hi0, shared)  # the same parameters on both sides
+    ids, w = moeq.route_i8(x[:T], Wr, b, k, torch.from_numpy(s).cuda(),
+                           torch.from_numpy(z).cuda())
+    torch.cuda.synchronize()
+    ids0, w0, amb = oracle.topk_softmax_i8(L[:T], s, z, k)
+    ok = ~amb
+    np.testing.assert_array_equal(ids.cpu().numpy()[ok], ids0[ok])
+    np.testing.assert_allclose(w.cpu().numpy()[ok], w0[ok], rtol=0, atol=1e-6)
+    # agreement with the exact routing, for the record
+    ids_x, _, _, _ = oracle.topk_softmax(L[:T], k)
+    same = np.mean([set(a) == set(b2) for a, b2 in zip(ids.cpu().numpy(), ids_x)])
+    _say(f"    ambiguous {int(amb.sum())}; same expert set as exact routing {same:.3f}")

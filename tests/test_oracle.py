@@ -511,3 +511,68 @@ def test_plan_tiers_properties():
             t = ranked[below[0]]
             assert used - tb[t] + tb[t - 1] > budget
     assert oracle.plan_tiers([1, 2, 3], [10, 5], 14) is None
+
+
+# --------------------------------------------------------------------------
+# int8 router logits ("AlphaQ" blog, DRAQ)
+# --------------------------------------------------------------------------
+def test_i8_router_hand_example():
+    # s = 0.5, z = 0: L/s = 0.6, 0.4, 2, 0.2 -> codes 1, 0, 2, 0 -> 0.5, 0, 1, 0;
+    # experts 1 and 3 tie at 0 and the lower index wins
+    ids, w, amb = oracle.topk_softmax_i8([[0.3, 0.2, 1.0, 0.1]], [0.5] * 4, [0] * 4, 3)
+    np.testing.assert_array_equal(ids, [[2, 0, 1]])
+    e = np.exp([0.0, -0.5, -1.0])
+    np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-15)
+    assert not amb[0]
+
+
+def test_i8_router_exact_on_the_grid():
+    """Logits that are codes times the scale survive the round trip exactly,
+    so the routing is the unquantised one, weights included."""
+    rng = np.random.default_rng(31)
+    E, T, k = 16, 200, 4
+    s = np.ldexp(1.0, -rng.integers(3, 9, size=E)).astype(np.float32)
+    z = rng.integers(-20, 20, size=E)
+    codes = rng.integers(-128, 128, size=(T, E))
+    L = (codes - z[None, :]) * s.astype(np.float64)[None, :]
+    Lq, amb = oracle.quantize_logits_i8(L, s, z)
+    np.testing.assert_array_equal(Lq, L)
+    ids, w, _ = oracle.topk_softmax_i8(L, s, z, k)
+    ids0, w0, _, _ = oracle.topk_softmax(L, k)
+    np.testing.assert_array_equal(ids, ids0)
+    np.testing.assert_array_equal(w, w0)
+
+
+def test_i8_router_params_map_range_to_codes():
+    rng = np.random.default_rng(32)
+    for shared in (False, True):
+        lo = rng.uniform(-3, 1, size=64)
+        hi = lo + rng.uniform(0.01, 4, size=64)
+        s, z = oracle.router_i8_params(lo, hi, shared)
+        glo, ghi = (np.full(64, lo.min()), np.full(64, hi.max())) if shared else (lo, hi)
+        q = lambda v: np.clip(np.rint(v / s.astype(np.float64)) + z, -128, 127)
+        np.testing.assert_array_equal(q(glo), -128)
+        assert set(np.unique(q(ghi)).tolist()) <= {126.0, 127.0}
+        if shared:
+            assert np.all(s == s[0]) and np.all(z == z[0])
+        # beyond the range the codes saturate
+        np.testing.assert_array_equal(q(ghi + 10 * s.astype(np.float64)), 127)
+
+
+def test_i8_router_shared_codes_rank_like_values():
+    """With one scale and zero point the int8 codes themselves give the top-k
+    (stable, lower index first): the top-k 'in int8 space'."""
+    rng = np.random.default_rng(33)
+    L = rng.standard_normal((300, 32)) * 0.8
+    s, z = oracle.router_i8_params(*oracle.router_logit_range(L), shared=True)
+    ids, _, _ = oracle.topk_softmax_i8(L, s, z, 6)
+    codes = np.clip(np.rint(L / s.astype(np.float64)) + z, -128, 127)
+    for t in range(L.shape[0]):
+        np.testing.assert_array_equal(ids[t], np.argsort(-codes[t], kind="stable")[:6])
+
+
+def test_logit_range_skips_nan():
+    L = np.array([[1.0, np.nan, -2.0], [0.5, np.nan, 3.0], [-1.0, np.nan, 0.0]])
+    lo, hi = oracle.router_logit_range(L)
+    np.testing.assert_array_equal(lo, [-1.0, np.inf, -2.0])
+    np.testing.assert_array_equal(hi, [1.0, -np.inf, 3.0])
