@@ -606,10 +606,10 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         d0 = n0;
         d1 = n1;
         // one scheduling region per step: each MFMA of step s is followed by
-        // a share of step s+1's decode and one of its LDS reads, so a lone
-        // wavefront keeps the matrix core fed while it decodes
-        // (about 2/3 of the decode is pinned behind the MFMAs; the scheduler
-        // places the rest, which measured 1% faster than pinning all of it)
+        // a share of step s+1's decode, so a lone wavefront keeps the matrix
+        // core fed while it decodes (about 2/3 of the decode is pinned behind
+        // the MFMAs; the scheduler places the rest and the LDS reads, which
+        // measured 1-4% faster than pinning all of them)
         constexpr int NM = 2 * AMT;
         constexpr int VPM = (24 + NM - 1) / NM;
         constexpr int VG = VPM > 2 ? VPM - 1 : VPM;
@@ -617,7 +617,6 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         for (int i = 0; i < NM; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);
-          if (i < AMT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
