@@ -150,36 +150,49 @@ __device__ inline uint32_t permute_block(const int32_t* __restrict__ ids, int R,
   if (bad) atomicOr(s_flags, bad);
   __syncthreads();
 
-  // 2. per-expert totals (thread e loops over waves; the wave bases become
-  //    prefixes over the waves), then the exclusive scan over experts
-  const int EPT = (E + NTH - 1) / NTH;  // experts per thread (1 for E <= 1024)
-  int local_total = 0;
-  for (int q = 0; q < EPT; ++q) {
-    const int e = tid * EPT + q;
-    if (e < E) {
+  // 2. per-expert totals and the exclusive scan over experts, by wavefront 0
+  //    alone (E <= 256: experts 4 lane .. 4 lane + 3 per lane, a shuffle scan
+  //    over lanes), so the block waits at one barrier instead of a block
+  //    scan's log2(NTH) pairs; the wave bases become prefixes over the waves
+  if (wave == 0) {
+    const int lane = tid & 63;
+    int tot[4];
+    int lane_sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
       int run = 0;
-      for (int w = 0; w < W; ++w) {
-        const int c = base[w * E + e];
-        base[w * E + e] = run;
-        run += c;
+      if (e < E) {
+        for (int w = 0; w < W; ++w) {
+          const int c = base[w * E + e];
+          base[w * E + e] = run;
+          run += c;
+        }
       }
-      counts[e] = run;
-      local_total += run;
+      tot[j] = run;
+      lane_sum += run;
     }
-  }
-  int total;
-  int excl = block_excl_scan<NTH>(local_total, scan, &total);
-  for (int q = 0; q < EPT; ++q) {
-    const int e = tid * EPT + q;
-    if (e < E) {
-      for (int w = 0; w < W; ++w) base[w * E + e] += excl;
-      offsets[e] = excl;
-      excl += counts[e];
+    int incl = lane_sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
     }
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    if (rows_lds) *rows_lds = total;
+    int excl = incl - lane_sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      if (e < E) {
+        for (int w = 0; w < W; ++w) base[w * E + e] += excl;
+        counts[e] = tot[j];
+        offsets[e] = excl;
+      }
+      excl += tot[j];
+    }
+    if (lane == 63) {
+      offsets[E] = incl;
+      if (rows_lds) *rows_lds = incl;
+    }
   }
   __syncthreads();
 
