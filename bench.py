@@ -424,7 +424,7 @@ def main():
             dec.append(d)
         result["decode"] = dec
         # context: what a plain streaming read of the 1 GiB flush buffer
-        # reaches on this machine (median of 5, cached and non-temporal loads)
+        # reaches on this device (median of 5, cached and non-temporal loads)
         ctx = {"buffer_bytes": flush.numel()}
         for nt in (False, True):
             moeq.stream_read(flush, nontemporal=nt)

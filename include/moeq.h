@@ -324,7 +324,7 @@ moe_status moe_plan_tiers(const int64_t* counts, int E, const uint64_t* tier_byt
  * `nontemporal` is non-zero. Each block folds the 32-bit words it read into
  * an XOR and stores it at sink[block] (device, MOE_STREAM_BLOCKS uint32), so
  * the XOR of all sink entries is the XOR of every word of the buffer. Timing
- * it gives the HBM read rate the box reaches, the context for the decode
+ * it gives the HBM read rate the device reaches, the context for the decode
  * GEMVs' weight-stream rates. */
 #define MOE_STREAM_BLOCKS 4096
 moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
