@@ -248,3 +248,33 @@ def test_router_i8_rejects():
     assert L.moe_router_logit_range(p(16), 1, p(16), None, 4, 64, 8, p(12), p(16), p(256), 1 << 20,
                                     None) == -3
     assert L.moe_router_logit_range(p(16), 1, p(16), None, 0, 64, 8, None, None, None, 0, None) == 0
+
+
+def test_package_never_uses_the_oracle():
+    """The library and its binding share no code with the oracle: no source
+    under the package names it, and importing the package loads no oracle
+    module."""
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "quantized_mixture_experts_router_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), os.path.join(dirpath, f)
+    code = ("import sys, quantized_mixture_experts_router_amd as m; "
+            "print(any(k == 'oracle' or k.startswith('oracle.') for k in sys.modules))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "False"
+
+
+def test_package_fails_loudly_without_the_library():
+    import subprocess
+    import sys
+    env = dict(os.environ, MOEQ_LIBRARY=os.path.join(ROOT, "no-such-libmoeq.so"))
+    out = subprocess.run([sys.executable, "-c", "import quantized_mixture_experts_router_amd"],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert out.returncode != 0
+    assert "ImportError" in out.stderr and "no-such-libmoeq.so" in out.stderr
