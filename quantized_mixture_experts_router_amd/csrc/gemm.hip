@@ -90,7 +90,7 @@ struct FfnArgs {
   int out_f32;
   int R;
   int splits;
-  int lpt;        // prefill task order: longest first (1) or expert-major (0)
+  int lpt;        // prefill task order: expert-major (0), longest first in 2 (1) or 4 (2) classes
 };
 
 struct Task {
@@ -290,6 +290,147 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
   return task.e >= 0;
 }
 
+// Task lookup of the prefill kernel for a launch of less than two rounds of
+// block slots: longest first in four classes. The tiles with 4 filled 32-row
+// sub-tiles (full m-tiles, and partial ones of more than 3 BM / 4 rows) come
+// first, then the partial tiles with 3, 2 and 1, so the shortest blocks make
+// the tail. XCD x runs an equal contiguous share of each class in turn; a
+// class's remainder goes to the XCDs after the previous class's, so no XCD
+// takes more than one task above the others. (find_task_lpt holds the other
+// orders; this one pays for four prefix sums instead of two.)
+template <bool GU>
+__device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b, Task& task) {
+  constexpr int NC = 4;  // longest-first classes: 4, 3, 2, 1 filled sub-tiles
+  __shared__ int s_wsum[NC][16];  // up to 1024 threads
+  __shared__ int s_res[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  if (tid == 0) s_res[0] = -1;
+  const int SUB = BM / 4;  // rows of a sub-tile class step
+  int cnt[2], ncl[2][NC], cls[2];
+  int lsum[NC] = {0, 0, 0, 0};
+  bool missing = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    int c = 0, f = -1;
+    if (e < a.E) {
+      c = a.offsets[e + 1] - a.offsets[e];
+      f = expert_fid<GU>(a.experts, e);
+      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
+    }
+    cnt[q] = c;
+    const bool mine = f == fid;
+    const int rem = c % BM;
+    // class of the partial tile: 0 (as long as a full one) .. 3 (shortest)
+    cls[q] = rem ? NC - (rem + SUB - 1) / SUB : 0;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) ncl[q][k] = 0;
+    if (mine) {
+      ncl[q][0] = (c / BM) * NB;
+      if (rem) ncl[q][cls[q]] += NB;
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) lsum[k] += ncl[q][k];
+  }
+  if (missing && blockIdx.x == 0 && a.flags)
+    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  int inc[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) inc[k] = lsum[k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int v = __shfl_up(inc[k], off);
+      if (lane >= off) inc[k] += v;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) s_wsum[k][wave] = inc[k];
+  }
+  __syncthreads();
+  int st[NC], tot[NC];  // the thread's experts' first task in each list; list sizes
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    st[k] = inc[k] - lsum[k];
+    tot[k] = 0;
+  }
+  for (int w = 0; w < nwaves; ++w) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (w < wave) st[k] += s_wsum[k][w];
+      tot[k] += s_wsum[k][w];
+    }
+  }
+  const int x = b & 7, slot = b >> 3;
+  {
+    // XCD x's share of list k: q + 1 tasks on the r XCDs starting at `rot`
+    // (the XCD after the previous list's extras), q on the others
+    int rot = 0, before = 0;
+    int k_sel = -1, L = 0;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int q = tot[k] >> 3, r = tot[k] & 7;
+      const int d = (x - rot + 8) & 7;  // x's position counted from rot
+      const int n = q + (d < r ? 1 : 0);
+      // extras of the XCDs below x: those at positions < r among x' < x
+      int ex = 0;
+      for (int y = 0; y < x; ++y) ex += ((y - rot + 8) & 7) < r ? 1 : 0;
+      if (k_sel < 0 && slot - before < n) {
+        k_sel = k;
+        L = x * q + ex + (slot - before);
+      }
+      before += n;
+      rot = (rot + r) & 7;
+    }
+    if (k_sel >= 0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        int s0 = 0, n = 0;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+          if (k == k_sel) {
+            s0 = st[k];
+            n = ncl[q][k];
+          }
+        }
+        if (L >= s0 && L < s0 + n) {
+          const int rel = L - s0;
+          const int mf = cnt[q] / BM;  // full m-tiles of the expert
+          int mi, nt;
+          if (k_sel == 0) {
+            // the expert's class-0 tiles: its full m-tiles, plus the partial
+            // one when that is class 0 too
+            const int mt = mf + ((cnt[q] % BM) && cls[q] == 0 ? 1 : 0);
+            mi = rel % mt;
+            nt = rel / mt;
+          } else {
+            mi = mf;
+            nt = rel;
+          }
+          s_res[0] = e;
+          s_res[1] = a.offsets[e] + mi * BM;
+          s_res[2] = min(BM, cnt[q] - mi * BM);
+          s_res[3] = nt;
+        }
+        if (k_sel >= 0) {
+#pragma unroll
+          for (int k = 0; k < NC; ++k) st[k] += ncl[q][k];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  task.e = s_res[0];
+  task.row0 = s_res[1];
+  task.mcount = s_res[2];
+  task.nt = s_res[3];
+  return task.e >= 0;
+}
+
 __device__ inline void store_gu(const FfnArgs& a, int row, int col, float g, float u) {
   const float sc = a.ascale ? a.ascale[row] : 1.0f;
   const float h = silu_mul(g * sc, u * sc);
@@ -473,7 +614,10 @@ constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 constexpr int kPW = MOEQ_PF_WAVES;
 constexpr int kBPC = (8 / kPW) * 128 / kBM;  // blocks per CU
 
-template <class F, bool GU>
+// LPT4: the four-class longest-first lookup (down launches of less than two
+// rounds); a separate instantiation, so the other launches keep the kernel
+// that the lighter lookup compiles to
+template <class F, bool GU, bool LPT4 = false>
 __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) {
   // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
   // 16-byte chunks of row r stored at chunk ^ swz(r). The LDS serves a 16-byte
@@ -495,7 +639,12 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
   const int NU = a.N / (GU ? 32 : 64);
   const int NB = (NU + kPW - 1) / kPW;
   Task t;
-  if (!find_task_lpt<GU>(a, F::ID, kBM, NB, blockIdx.x, t)) return;
+  bool found;
+  if constexpr (LPT4)
+    found = find_task_lpt4<GU>(a, F::ID, kBM, NB, blockIdx.x, t);
+  else
+    found = find_task_lpt<GU>(a, F::ID, kBM, NB, blockIdx.x, t);
+  if (!found) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, kh = lane >> 5;
@@ -752,13 +901,20 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
     const int NU = a.N / (GU ? 32 : 64);
     const int NB = (NU + kPW - 1) / kPW;
     // longest-first order when the launch has fewer than 4 blocks per block
-    // slot of the device (its tail is then a large share of its time)
+    // slot of the device (its tail is then a large share of its time); for
+    // the down projection in four classes below 2 blocks per slot
     const long nblk = (long)max_tiles(a.R, a.E, kBM) * NB;
     FfnArgs b = a;
-    b.lpt = nblk < 4L * device_cus() * kBPC;
+    const long slots = (long)device_cus() * kBPC;
+    b.lpt = nblk < 2 * slots ? 2 : (nblk < 4 * slots ? 1 : 0);
     // 16 spare blocks: the per-XCD task shares may round up (find_task_lpt)
     dim3 grid(nblk + 16);
-    hipLaunchKernelGGL((ffn_prefill_kernel<F, GU>), grid, dim3(64 * kPW), 0, s, b);
+    if (!GU && b.lpt == 2) {
+      hipLaunchKernelGGL((ffn_prefill_kernel<F, false, true>), grid, dim3(64 * kPW), 0, s, b);
+    } else {
+      if (b.lpt == 2) b.lpt = 1;  // gate/up: the two-class order
+      hipLaunchKernelGGL((ffn_prefill_kernel<F, GU, false>), grid, dim3(64 * kPW), 0, s, b);
+    }
   }
   return hipGetLastError();
 }
