@@ -75,7 +75,7 @@ def payload_bytes(cfg, e):
 def kernel_names(cfg):
     import synth
     fmts = sorted({synth.expert_format(cfg, e) for e in range(cfg.E)})
-    return [f"ffn_prefill_kernel<moeq::Fmt<{f}, {b}, {g}>, true>" for f, b, g in fmts]
+    return [f"ffn_prefill_kernel<moeq::Fmt<{f}, {b}, {g}>, true, false>" for f, b, g in fmts]
 
 
 def weights_desc(cfg):
