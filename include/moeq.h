@@ -204,7 +204,7 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
  * enter the matrix cores exactly and the per-row scales are applied in fp32.
  * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes, 256-aligned.
  * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I;
- * x 16-byte aligned. */
+ * x and Y 16-byte aligned. */
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
                              uint32_t fmt_mask, const int32_t* offsets, const int32_t* perm_token,
                              int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
@@ -219,8 +219,9 @@ moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expe
  * moe_ffn_gate_up: fused gate/up projection + SwiGLU of every sorted row,
  *   leaving h in the workspace. One kernel.
  * moe_ffn_down: (under MOE_ACT_I8_XH, per-row int8 quantisation of h, then)
- *   the down projection into Y (fp32 [T*k, H]); at decode sizes the K range
- *   is split over blocks and a reduction kernel sums the parts into Y. */
+ *   the down projection into Y (fp32 [T*k, H], 16-byte aligned); at decode
+ *   sizes the K range is split over blocks and a reduction kernel sums the
+ *   parts into Y. */
 moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_token, int T, int H,
                           int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
                           void* stream);

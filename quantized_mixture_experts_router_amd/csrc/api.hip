@@ -330,6 +330,7 @@ moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T > 0 && !Y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(Y, 16)) return MOE_ERR_ALIGNMENT;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   const size_t n = (size_t)T * k * H;

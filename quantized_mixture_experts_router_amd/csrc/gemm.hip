@@ -613,6 +613,9 @@ constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 // streaming its own 64 weight rows (one block per CU at 8)
 constexpr int kPW = MOEQ_PF_WAVES;
 constexpr int kBPC = (8 / kPW) * 128 / kBM;  // blocks per CU
+// bytes of LDS a prefill wavefront stages its output through: 16 rows of 64
+// fp32 at a pitch of 72
+constexpr int kStageB = 16 * 72 * 4;
 
 // LPT4: the four-class longest-first lookup (down launches of less than two
 // rounds); a separate instantiation, so the other launches keep the kernel
@@ -830,19 +833,76 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     // no LDS DMA may still be in flight when the block's LDS is released
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
+    // Epilogue, staged through LDS 16 rows at a time so each lane stores 16
+    // bytes of a row instead of one element: a wavefront's output rows are 64
+    // fp32 (down) or 32 fp16/fp32 (gate/up) values held one column per lane,
+    // and one-element stores made the end of a block slow (20% of the
+    // short-K down launches). Each wavefront writes its own 4.5 KiB of the
+    // token buffers (wavefronts 0/1 in lds0, 2/3 in lds1) once every
+    // wavefront is past its last token tile. Row pitches are padded so rows
+    // r and r+4, written by the two lane halves, fall on different banks.
+    static_assert(kPW <= 4 && 2 * kStageB <= TILEB, "epilogue staging exceeds the token buffers");
+    __syncthreads();
     if (!on) return;
+    uint8_t* stg = (wave >> 1 ? lds1 : lds0) + (wave & 1) * kStageB;
 #pragma unroll
     for (int mi = 0; mi < AMT; ++mi) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = mi * 32 + acc_row(r, lane);
-        if (i < t.mcount) {
-          const int row = t.row0 + i;
-          if (GU) {
-            store_gu(a, row, 32 * unit + n, acc[mi][0][r], acc[mi][1][r]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int i0 = mi * 32 + 16 * hh;  // first tile row of this half
+        // a wavefront's LDS operations run in order: the fences only keep
+        // the compiler from moving reads of other lanes' values across writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
+          const int lr = 8 * ((r >> 2) & 1) + 4 * kh + (r & 3);  // == acc_row(r) - 16 hh
+          if constexpr (GU) {
+            const float sc = (a.ascale && i0 + lr < t.mcount) ? a.ascale[t.row0 + i0 + lr] : 1.0f;
+            const float h = silu_mul(acc[mi][0][r] * sc, acc[mi][1][r] * sc);
+            if (a.out_f32)
+              reinterpret_cast<float*>(stg)[lr * 36 + n] = h;
+            else
+              reinterpret_cast<f16*>(stg)[lr * 40 + n] = (f16)h;
           } else {
-            store_dn(a, 0, row, 32 * rt0 + n, acc[mi][0][r]);
-            store_dn(a, 0, row, 32 * (rt0 + 1) + n, acc[mi][1][r]);
+            reinterpret_cast<float*>(stg)[lr * 72 + n] = acc[mi][0][r];
+            reinterpret_cast<float*>(stg)[lr * 72 + 32 + n] = acc[mi][1][r];
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (GU) {
+          if (a.out_f32) {
+            // 16 rows x 32 fp32: 8 lanes per row, two stores
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int lr = 8 * j + (lane >> 3), c4 = lane & 7;
+              const float4 v = *reinterpret_cast<const float4*>(stg + (lr * 36 + 4 * c4) * 4);
+              if (i0 + lr < t.mcount)
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
+                                           (size_t)(t.row0 + i0 + lr) * a.N + 32 * unit + 4 * c4) = v;
+            }
+          } else {
+            // 16 rows x 32 fp16: 4 lanes per row, one store
+            const int lr = lane >> 2, c8 = lane & 3;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + (lr * 40 + 8 * c8) * 2);
+            if (i0 + lr < t.mcount)
+              *reinterpret_cast<uint4*>(reinterpret_cast<f16*>(a.out) +
+                                        (size_t)(t.row0 + i0 + lr) * a.N + 32 * unit + 8 * c8) = v;
+          }
+        } else {
+          // 16 rows x 64 fp32: 16 lanes per row, four stores
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int lr = 4 * j + (lane >> 4), c4 = lane & 15;
+            float4 v = *reinterpret_cast<const float4*>(stg + (lr * 72 + 4 * c4) * 4);
+            if (i0 + lr < t.mcount) {
+              const float sc = a.ascale ? a.ascale[t.row0 + i0 + lr] : 1.0f;
+              v.x *= sc;
+              v.y *= sc;
+              v.z *= sc;
+              v.w *= sc;
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
+                                         (size_t)(t.row0 + i0 + lr) * a.N + 32 * rt0 + 4 * c4) = v;
+            }
           }
         }
       }

@@ -137,6 +137,8 @@ def test_ffn_rejects_small_workspace():
     assert L.moe_ffn_gather(p, 1, p, 8, 256, 256, 4, 2, 0, p, need - 1, None) == -4
     assert L.moe_ffn_gather(p, 1, None, 8, 256, 256, 4, 2, 0, p, need, None) == -1
     assert L.moe_ffn_down(p, 0, p, 8, 256, 256, 4, 2, 3, p, p, need, None) == -1
+    # Y is stored 16 bytes per lane
+    assert L.moe_ffn_down(p, 0, p, 8, 256, 256, 4, 2, 0, ctypes.c_void_p(264), p, need, None) == -3
     assert L.moe_ffn_gather(p, 1, None, 0, 256, 256, 4, 2, 0, p, need, None) == 0
 
 
