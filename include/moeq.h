@@ -136,7 +136,9 @@ size_t moe_packed_expert_bytes(const moe_expert_canon* src);
 /* Repack one expert from the canonical format (device planes named in *src)
  * into the device layout at dst_dev (256-byte aligned, dst_bytes >=
  * moe_packed_expert_bytes(src)). Fills *out_desc (host). Enqueues the repack
- * on `stream`; the canonical planes must stay valid until it has run. */
+ * on `stream`; the canonical planes must stay valid until it has run.
+ * I * H <= 2^31 (else MOE_ERR_UNSUPPORTED: the kernels address a packed
+ * matrix with 32-bit byte offsets). */
 moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t dst_bytes,
                            moe_packed_expert* out_desc, void* stream);
 
@@ -204,7 +206,9 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* co
  * enter the matrix cores exactly and the per-row scales are applied in fp32.
  * ws: at least moe_workspace_size(T, H, I, E, k, aq) bytes, 256-aligned.
  * Constraints: H % 128 == 0, I % 128 == 0, every expert packed with these H, I;
- * x and Y 16-byte aligned. */
+ * x and Y 16-byte aligned; T * k * max(H, I) * 2 < 2^32 (else
+ * MOE_ERR_UNSUPPORTED: the fp16 expert inputs are addressed with 32-bit byte
+ * offsets). */
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
                              uint32_t fmt_mask, const int32_t* offsets, const int32_t* perm_token,
                              int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,

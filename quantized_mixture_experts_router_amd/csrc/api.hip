@@ -25,6 +25,8 @@ moe_status check_canon(const moe_expert_canon* src) {
   if (!src) return MOE_ERR_INVALID_ARG;
   const uint32_t I = src->gate.rows, H = src->gate.cols;
   if (I == 0 || H == 0) return MOE_ERR_INVALID_ARG;
+  // packed matrices are addressed with 32-bit byte offsets
+  if ((uint64_t)I * H > (1ull << 31)) return MOE_ERR_UNSUPPORTED;
   moe_status s;
   if ((s = check_qmat(src->gate, I, H)) != MOE_OK) return s;
   if ((s = check_qmat(src->up, I, H)) != MOE_OK) return s;
@@ -55,6 +57,8 @@ moe_status check_sizes(int T, int H, int I, int E, int k) {
   if (k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
   if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_INVALID_ARG;
   if ((long)T * k > (1L << 30)) return MOE_ERR_INVALID_ARG;
+  // the expert GEMMs address their fp16 input rows with 32-bit byte offsets
+  if ((uint64_t)T * k * (H > I ? H : I) * 2 > 0xFFFFFFFFull) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

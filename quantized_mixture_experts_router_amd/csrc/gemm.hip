@@ -18,10 +18,12 @@
 //    v_mfma_f32_32x32x16_f16 with the token rows padded to 32; partial sums
 //    meet in LDS. The down projection also splits K across blocks.
 //  * prefill (many rows per expert): a block owns 128 token rows and 4 x 64
-//    weight rows; the token tile reaches LDS by DMA (global_load_lds, rows
-//    swizzled for the 64-bank LDS, three buffers for 4-bit tiles) and is
-//    shared by the 4 wavefronts, each of which streams its own weight rows
-//    into registers and decodes step s+1 while the MFMAs of step s run; two
+//    weight rows; the token tile reaches LDS by DMA (buffer loads with an
+//    LDS destination, rows swizzled for the 64-bank LDS, three buffers for
+//    4-bit tiles) and is shared by the 4 wavefronts, each of which streams
+//    its own weight rows into registers (buffer loads: scalar base and tile
+//    offset, so no vector address arithmetic) and decodes step s+1 while the
+//    MFMAs of step s run; two
 //    blocks share a CU so one block's decode overlaps the other's MFMAs. The
 //    pipeline is specialised on the number of 32-row sub-tiles holding rows,
 //    so a partial last m-tile costs only its own MFMAs, and each XCD runs
@@ -157,10 +159,12 @@ __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task
     start += ntk[q];
   }
   __syncthreads();
-  task.e = s_res[0];
-  task.row0 = s_res[1];
-  task.mcount = s_res[2];
-  task.nt = s_res[3];
+  // block-uniform: held in scalar registers, so what derives from them
+  // (weight addresses, buffer descriptors) is computed on the scalar unit
+  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
+  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
+  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
+  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
   return task.e >= 0;
 }
 
@@ -283,10 +287,12 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
     }
   }
   __syncthreads();
-  task.e = s_res[0];
-  task.row0 = s_res[1];
-  task.mcount = s_res[2];
-  task.nt = s_res[3];
+  // block-uniform: held in scalar registers, so what derives from them
+  // (weight addresses, buffer descriptors) is computed on the scalar unit
+  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
+  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
+  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
+  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
   return task.e >= 0;
 }
 
@@ -424,10 +430,12 @@ __device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b,
     }
   }
   __syncthreads();
-  task.e = s_res[0];
-  task.row0 = s_res[1];
-  task.mcount = s_res[2];
-  task.nt = s_res[3];
+  // block-uniform: held in scalar registers, so what derives from them
+  // (weight addresses, buffer descriptors) is computed on the scalar unit
+  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
+  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
+  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
+  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
   return task.e >= 0;
 }
 
@@ -589,12 +597,61 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
 // ===========================================================================
 // Prefill family
 // ===========================================================================
-// Prefill tuning knobs (defaults measured best on MI355X): non-temporal
-// weight loads (0: tiles are re-read by every m-tile of an expert), the
-// three-buffer pipeline for 16 KiB token tiles, wavefronts per block.
-#ifndef MOEQ_PF_NT
-#define MOEQ_PF_NT 0
-#endif
+// Buffer-resource loads: the base and size sit in scalar registers, the
+// per-lane part of the address is a 32-bit offset and the per-tile part a
+// scalar offset, so a load costs no vector address arithmetic.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+// a pointer every lane holds, moved to scalar registers
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <class T>
+__device__ inline T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(T) == 16) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  } else if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  } else {
+    static_assert(sizeof(T) == 2, "load size");
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+  }
+}
+// 16 bytes per lane from r at voff + soff into LDS at lds + 16 lane
+__device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+template <int EB>
+__device__ inline void pbuf_load(PBuf<EB>& pb, rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (EB == 2) {
+    pb.w[0] = bload<uint16_t>(r, voff, soff);
+  } else if constexpr (EB == 4) {
+    pb.w[0] = bload<uint32_t>(r, voff, soff);
+  } else if constexpr (EB == 8) {
+    const u32x2 v = bload<u32x2>(r, voff, soff);
+    pb.w[0] = v.x;
+    pb.w[1] = v.y;
+  } else {
+    const u32x4 v = bload<u32x4>(r, voff, soff);
+    pb.w[0] = v.x;
+    pb.w[1] = v.y;
+    pb.w[2] = v.z;
+    pb.w[3] = v.w;
+  }
+}
+
+// Prefill tuning knobs (defaults measured best on MI355X): the three-buffer
+// pipeline for 16 KiB token tiles, wavefronts per block. Weight loads are
+// cached: the m-tiles of an expert re-read each weight tile.
 #ifndef MOEQ_PF_DEEP
 #define MOEQ_PF_DEEP 1
 #endif
@@ -607,7 +664,6 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
 #define MOEQ_PF_BM 128
 #endif
 constexpr int kBM = MOEQ_PF_BM;
-constexpr bool kPrefillNT = MOEQ_PF_NT;  // weight tiles: non-temporal loads
 constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
 // wavefronts per prefill block: they share one token tile in LDS, each
 // streaming its own 64 weight rows (one block per CU at 8)
@@ -649,7 +705,7 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     found = find_task_lpt<GU>(a, F::ID, kBM, NB, blockIdx.x, t);
   if (!found) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, kh = lane >> 5;
   const int KTn = a.K / F::KT;
   const int NE = a.K / F::GE;
@@ -662,10 +718,18 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
   // every wavefront runs the same straight-line loop
   const int rt0 = 2 * unit;
   const int rtl = 2 * min(unit, NU - 1);
-  const uint8_t* c0 = codes + (size_t)rtl * KTn * F::TB + lane * F::CB;
-  const uint8_t* c1 = c0 + (size_t)KTn * F::TB;
-  const uint8_t* p0 = params + ((size_t)rtl * NE * 32 + n) * F::EB;
-  const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
+  // rows of weight tiles in this matrix: 2I (gate/up interleaved) or H
+  const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
+  const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
+  const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
+  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
+  const uint32_t vc0 = (uint32_t)rtl * KTn * F::TB + lane * F::CB;
+  const uint32_t vc1 = vc0 + (uint32_t)KTn * F::TB;
+  // the group of a lane's first element in tile kt is kt KT / GE plus, when
+  // groups are no longer than a tile, its half's kh SPAN / GE
+  const uint32_t vp0 =
+      ((uint32_t)rtl * NE * 32 + n + (F::GE <= F::KT ? kh * (F::SPAN / F::GE) : 0) * 32) * F::EB;
+  const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
 
   const DeqConsts dk = make_deq_consts<F>();
   // Token tile DMA: instruction j of wavefront w fills LDS slots
@@ -685,19 +749,16 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
   }
   auto dma_a = [&](int kt, uint8_t* buf) {
-    const uint8_t* src = (const uint8_t*)a.a + (size_t)kt * ROWB;
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const MOEQ_GLOBAL void*)(src + doff[j]),
-          (__attribute__((address_space(3))) void*)(buf + (wave * NI + j) * 1024), 16, 0, 0);
+      dma16(rA, buf + (wave * NI + j) * 1024, doff[j], (uint32_t)kt * ROWB);
   };
   auto load_b = [&](int kt, BTile<F>& b) {
-    b.w0 = ldg<kPrefillNT, typename F::CodeT>(c0 + (size_t)kt * F::TB);
-    b.w1 = ldg<kPrefillNT, typename F::CodeT>(c1 + (size_t)kt * F::TB);
-    const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
-    b.q0.template load<kPrefillNT>(p0 + (size_t)ei * 32 * F::EB);
-    b.q1.template load<kPrefillNT>(p1 + (size_t)ei * 32 * F::EB);
+    b.w0 = bload<typename F::CodeT>(rC, vc0, (uint32_t)kt * F::TB);
+    b.w1 = bload<typename F::CodeT>(rC, vc1, (uint32_t)kt * F::TB);
+    const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
+    pbuf_load(b.q0, rP, vp0, sp);
+    pbuf_load(b.q1, rP, vp1, sp);
   };
   // The block's pipeline, specialised on the number of 32-row sub-tiles
   // that hold rows (the last m-tile of an expert is usually partial): empty

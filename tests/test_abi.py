@@ -111,6 +111,7 @@ def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bi
     (dict(fmt=2, bits=2), False), (dict(I=100), False), (dict(codes=8), False),
     (dict(params=2), False), (dict(codes=0), False), (dict(fmt=2, group=16), True),
     (dict(bits=2, group=16), True), (dict(down_bits=2), True),
+    (dict(I=65536, H=65536), False),  # beyond 32-bit offsets into a packed matrix
 ])
 def test_packed_bytes_validation(kw, ok):
     ec = _canon(**kw)
@@ -137,6 +138,8 @@ def test_ffn_rejects_small_workspace():
     assert L.moe_ffn_gather(p, 1, p, 8, 256, 256, 4, 2, 0, p, need - 1, None) == -4
     assert L.moe_ffn_gather(p, 1, None, 8, 256, 256, 4, 2, 0, p, need, None) == -1
     assert L.moe_ffn_down(p, 0, p, 8, 256, 256, 4, 2, 3, p, p, need, None) == -1
+    # expert inputs beyond 32-bit byte offsets: T*k*max(H, I)*2 >= 2^32
+    assert L.moe_ffn_gate_up(p, 0, p, 1 << 19, 4096, 4096, 8, 2, 0, p, 1 << 62, None) == -2
     # Y is stored 16 bytes per lane
     assert L.moe_ffn_down(p, 0, p, 8, 256, 256, 4, 2, 0, ctypes.c_void_p(264), p, need, None) == -3
     assert L.moe_ffn_gather(p, 1, None, 0, 256, 256, 4, 2, 0, p, need, None) == 0

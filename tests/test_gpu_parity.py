@@ -221,6 +221,9 @@ LAYER_CASES = [
     ("hotcold", 2048, 256, 128, 256, 8),
     ("w4a8", 16, 512, 512, 8, 2),
     ("w4a8", 300, 512, 512, 8, 2),
+    # prefill with idle wavefronts: H = 384 leaves two of the last down block's
+    # four 64-row units empty, I = 384 gives three gate/up blocks per m-tile
+    ("mixtral", 500, 384, 384, 8, 2),
     # small decode batches: the one-block front after the logits kernel
     ("mixtral", 2, 512, 1024, 8, 2),
     ("fine_e2m1", 1, 256, 256, 32, 6),
