@@ -16,60 +16,67 @@
 
 namespace moeq {
 
-// Global-address-space views: loads through them compile to global_load_*
-// (not flat_load_*), which keeps LDS and memory wait counters separate.
-#define MOEQ_GLOBAL __attribute__((address_space(1)))
-template <class T>
-__device__ inline const MOEQ_GLOBAL T* gptr(const void* p) {
-  return (const MOEQ_GLOBAL T*)(p);
-}
-
 __device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Loads of weight streams. NT = non-temporal: data read once per call (the
-// decode GEMVs) streams past the caches, which sustains a much higher HBM
-// read rate than cached loads.
-template <bool NT, class T>
-__device__ inline T ldg(const void* p) {
-  if (NT) return __builtin_nontemporal_load(gptr<T>(p));
-  return *gptr<T>(p);
+// Buffer-resource loads: base and size in scalar registers, a 32-bit
+// per-lane offset and a scalar per-tile offset, so a load costs no vector
+// address arithmetic. AUX holds the cache-policy bits: 0 (cached) or kNT,
+// the non-temporal hint for data read once per call (the decode GEMVs'
+// weight streams), which sustains a higher HBM read rate.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kNT = 2;
+
+// a pointer every lane holds, moved to scalar registers
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+// descriptor of `bytes` bytes at p (raw buffer: no stride, no format);
+// loads past the end return zero
+__device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <class T, int AUX = 0>
+__device__ inline T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(T) == 16) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+  } else if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+  } else {
+    static_assert(sizeof(T) == 2, "load size");
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX));
+  }
 }
 
+// Block parameters of one lane's codes (EB bytes: fp16 scale, or scale and
+// minimum, for one or two groups), zero-extended into 32-bit words.
 template <int EB>
-struct PBuf;
-template <>
-struct PBuf<2> {
-  uint32_t w[1];
-  template <bool NT = false>
-  __device__ inline void load(const uint8_t* p) { w[0] = ldg<NT, uint16_t>(p); }
-};
-template <>
-struct PBuf<4> {
-  uint32_t w[1];
-  template <bool NT = false>
-  __device__ inline void load(const uint8_t* p) { w[0] = ldg<NT, uint32_t>(p); }
-};
-template <>
-struct PBuf<8> {
-  uint32_t w[2];
-  template <bool NT = false>
-  __device__ inline void load(const uint8_t* p) {
-    u32x2 v = ldg<NT, u32x2>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-  }
-};
-template <>
-struct PBuf<16> {
-  uint32_t w[4];
-  template <bool NT = false>
-  __device__ inline void load(const uint8_t* p) {
-    u32x4 v = ldg<NT, u32x4>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
+struct PBuf {
+  static_assert(EB == 2 || EB == 4 || EB == 8 || EB == 16, "parameter bytes");
+  uint32_t w[EB <= 4 ? 1 : EB / 4];
+  template <int AUX = 0>
+  __device__ inline void load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (EB == 2) {
+      w[0] = bload<uint16_t, AUX>(r, voff, soff);
+    } else if constexpr (EB == 4) {
+      w[0] = bload<uint32_t, AUX>(r, voff, soff);
+    } else if constexpr (EB == 8) {
+      const u32x2 v = bload<u32x2, AUX>(r, voff, soff);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      const u32x4 v = bload<u32x4, AUX>(r, voff, soff);
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    }
   }
 };
 

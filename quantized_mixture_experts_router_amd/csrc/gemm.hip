@@ -459,6 +459,12 @@ struct BTile {
   PBuf<F::EB> q0, q1;
 };
 
+// 16 bytes per lane from r at voff + soff into LDS at lds + 16 lane
+__device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
 // ===========================================================================
 // Decode family
 // ===========================================================================
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   Task t;
   if (!find_task<GU>(a, F::ID, 32, NB, blockIdx.x, t)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, kh = lane >> 5;
   const int grp = wave / ksw, ks = wave % ksw;
   const int rg = t.nt * G + grp;
@@ -486,10 +492,16 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
   const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
   const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
-  const uint8_t* c0 = codes + (size_t)rt0 * KTn * F::TB + lane * F::CB;
-  const uint8_t* c1 = c0 + (size_t)KTn * F::TB;
-  const uint8_t* p0 = params + ((size_t)rt0 * NE * 32 + n) * F::EB;
-  const uint8_t* p1 = p0 + (size_t)NE * 32 * F::EB;
+  const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
+  const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
+  const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
+  const uint32_t vc0 = (uint32_t)rt0 * KTn * F::TB + lane * F::CB;
+  const uint32_t vc1 = vc0 + (uint32_t)KTn * F::TB;
+  // group of the lane's first element in tile kt: kt KT / GE, plus kh SPAN / GE
+  // when groups are no longer than a tile
+  const uint32_t vp0 =
+      ((uint32_t)rt0 * NE * 32 + n + (F::GE <= F::KT ? kh * (F::SPAN / F::GE) : 0) * 32) * F::EB;
+  const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
 
   const DeqConsts dk = make_deq_consts<F>();
   const int split = blockIdx.y;
@@ -497,7 +509,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const int kb = split * per, ke = min(KTn, kb + per);
 
   const bool arow = n < t.mcount;
-  const f16* ap = a.a + (size_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN;
+  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
+  const uint32_t va = ((uint32_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN) * 2;
 
   struct AFrag {
     f16x8 v[F::STEPS];
@@ -509,18 +522,19 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   auto tile_of = [&](int i) { return min(kb + ks + ksw * i, KTn - 1); };
   auto load_b = [&](int i, BTile<F>& b) {
     const int kt = tile_of(i);
-    b.w0 = ldg<true, typename F::CodeT>(c0 + (size_t)kt * F::TB);
-    b.w1 = ldg<true, typename F::CodeT>(c1 + (size_t)kt * F::TB);
-    const int ei = (kt * F::KT + kh * F::SPAN) / F::GE;
-    b.q0.template load<true>(p0 + (size_t)ei * 32 * F::EB);
-    b.q1.template load<true>(p1 + (size_t)ei * 32 * F::EB);
+    b.w0 = bload<typename F::CodeT, kNT>(rC, vc0, (uint32_t)kt * F::TB);
+    b.w1 = bload<typename F::CodeT, kNT>(rC, vc1, (uint32_t)kt * F::TB);
+    const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
+    b.q0.template load<kNT>(rP, vp0, sp);
+    b.q1.template load<kNT>(rP, vp1, sp);
   };
   auto load_a = [&](int i, AFrag& af) {
     const int kt = tile_of(i);
     // every lane loads: rows past the tile read the tile's first row, and
     // their outputs (MFMA rows of their own) are never stored
 #pragma unroll
-    for (int s = 0; s < F::STEPS; ++s) af.v[s] = *gptr<f16x8>(ap + (size_t)kt * F::KT + 8 * s);
+    for (int s = 0; s < F::STEPS; ++s)
+      af.v[s] = bload<f16x8>(rA, va, (uint32_t)(kt * F::KT + 8 * s) * 2);
   };
   f32x16 acc0 = {}, acc1 = {};
   auto compute = [&](const BTile<F>& b, const AFrag& af) {
@@ -597,58 +611,6 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
 // ===========================================================================
 // Prefill family
 // ===========================================================================
-// Buffer-resource loads: the base and size sit in scalar registers, the
-// per-lane part of the address is a 32-bit offset and the per-tile part a
-// scalar offset, so a load costs no vector address arithmetic.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-// a pointer every lane holds, moved to scalar registers
-template <class T>
-__device__ inline T* uniform_ptr(T* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T*)(((uint64_t)hi << 32) | lo);
-}
-__device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-template <class T>
-__device__ inline T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (sizeof(T) == 16) {
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-  } else if constexpr (sizeof(T) == 8) {
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-  } else if constexpr (sizeof(T) == 4) {
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-  } else {
-    static_assert(sizeof(T) == 2, "load size");
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-  }
-}
-// 16 bytes per lane from r at voff + soff into LDS at lds + 16 lane
-__device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-template <int EB>
-__device__ inline void pbuf_load(PBuf<EB>& pb, rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (EB == 2) {
-    pb.w[0] = bload<uint16_t>(r, voff, soff);
-  } else if constexpr (EB == 4) {
-    pb.w[0] = bload<uint32_t>(r, voff, soff);
-  } else if constexpr (EB == 8) {
-    const u32x2 v = bload<u32x2>(r, voff, soff);
-    pb.w[0] = v.x;
-    pb.w[1] = v.y;
-  } else {
-    const u32x4 v = bload<u32x4>(r, voff, soff);
-    pb.w[0] = v.x;
-    pb.w[1] = v.y;
-    pb.w[2] = v.z;
-    pb.w[3] = v.w;
-  }
-}
-
 // Prefill tuning knobs (defaults measured best on MI355X): the three-buffer
 // pipeline for 16 KiB token tiles, wavefronts per block. Weight loads are
 // cached: the m-tiles of an expert re-read each weight tile.
@@ -757,8 +719,8 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     b.w0 = bload<typename F::CodeT>(rC, vc0, (uint32_t)kt * F::TB);
     b.w1 = bload<typename F::CodeT>(rC, vc1, (uint32_t)kt * F::TB);
     const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
-    pbuf_load(b.q0, rP, vp0, sp);
-    pbuf_load(b.q1, rP, vp1, sp);
+    b.q0.load(rP, vp0, sp);
+    b.q1.load(rP, vp1, sp);
   };
   // The block's pipeline, specialised on the number of 32-row sub-tiles
   // that hold rows (the last m-tile of an expert is usually partial): empty
