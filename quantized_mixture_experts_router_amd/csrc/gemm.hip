@@ -492,6 +492,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
   const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
   const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
+  // 32-row weight tiles of the matrix (2I rows of interleaved gate/up, or H)
   const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
   const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
   const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
@@ -680,7 +681,8 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
   // every wavefront runs the same straight-line loop
   const int rt0 = 2 * unit;
   const int rtl = 2 * min(unit, NU - 1);
-  // rows of weight tiles in this matrix: 2I (gate/up interleaved) or H
+  // 32-row weight tiles of the matrix (2I rows of interleaved gate/up, or H);
+  // the descriptors span the whole matrix
   const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
   const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
   const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
