@@ -226,6 +226,10 @@ LAYER_CASES = [
     ("mixtral", 500, 384, 384, 8, 2),
     # small decode batches: the one-block front after the logits kernel
     ("mixtral", 2, 512, 1024, 8, 2),
+    # one token
+    ("mixtral", 1, 512, 1024, 8, 2),
+    ("tiny", 1, 256, 512, 8, 2),            # fp32 activations
+    ("w4a8", 1, 512, 512, 16, 2),           # int8 expert inputs, 16 experts
     ("fine_e2m1", 1, 256, 256, 32, 6),
     # few weight rows in flight: K split over more wavefronts (8-tile streams)
     ("fine_e2m1", 1, 2048, 256, 32, 6),
@@ -297,7 +301,7 @@ def test_layer_deterministic(moeq):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("T", [6, 600])  # fused front / separate kernels
+@pytest.mark.parametrize("T", [1, 6, 600])  # fused front (one token, a few) / separate kernels
 def test_nan_token(moeq, T):
     """A token with a NaN input: its routing is MOE_ID_NAN with weight 0, the
     layer flags MOE_FLAG_NAN_LOGIT and leaves its row 0, and every other
