@@ -76,8 +76,17 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_I8_X = 1, MOE_ACT_I8_XH = 2 } moe_actq;
 enum {
   MOE_FLAG_BAD_EXPERT_ID = 1u << 0, /* an id outside [0,E) reached moe_permute */
   MOE_FLAG_NAN_LOGIT = 1u << 1,     /* a router logit was NaN (routing undefined) */
-  MOE_FLAG_FORMAT_NOT_LAUNCHED = 1u << 2 /* an expert with rows has a format outside
-                                            fmt_mask: its rows were not computed */
+  MOE_FLAG_FORMAT_NOT_LAUNCHED = 1u << 2, /* an expert with rows has a format outside
+                                             fmt_mask: its rows were not computed */
+  MOE_FLAG_BAD_SEGMENT = 1u << 3,   /* caller offsets leave [0, T*k] or decrease: each
+                                       segment was clamped to [offsets[e], T*k) and
+                                       rows outside it were not computed */
+  MOE_FLAG_EXPERT_SHAPE = 1u << 4,  /* an expert with rows has a descriptor whose H or
+                                       I differs from the call's: its rows were not
+                                       computed */
+  MOE_FLAG_FP16_RANGE = 1u << 5     /* an expert input (fp16 path) or a SwiGLU output h
+                                       stored as fp16 exceeded |v| = 65504: it became
+                                       +-inf, and so did the rows it feeds */
 };
 
 /* Routing id that moe_route writes in every slot of a token whose router

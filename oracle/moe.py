@@ -56,17 +56,17 @@ E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64
 # Weight blocks [PerExpert]
 # --------------------------------------------------------------------------
 def _unpack_codes(codes: np.ndarray, bits: int, cols: int) -> np.ndarray:
-    """uint8 [rows, row_bytes] -> int64 [rows, cols]. 4-bit: element 2i is the
-    low nibble of byte i. 2-bit: element 4i+j is bits [2j, 2j+1] of byte i."""
+    """uint8 [rows, row_bytes] -> uint8 [rows, cols]. 4-bit: element 2i is the
+    low nibble of byte i. 2-bit: element 4i+j is bits [2j, 2j+1] of byte i.
+    1-bit: element 8i+j is bit j of byte i."""
     codes = np.asarray(codes, dtype=np.uint8)
     per_byte = 8 // bits
     nbytes = cols // per_byte
-    b = codes[:, :nbytes].astype(np.int64)
+    b = codes[:, :nbytes]
     mask = (1 << bits) - 1
-    parts = [(b >> (bits * j)) & mask for j in range(per_byte)]
-    out = np.empty((codes.shape[0], cols), dtype=np.int64)
+    out = np.empty((codes.shape[0], cols), dtype=np.uint8)
     for j in range(per_byte):
-        out[:, j::per_byte] = parts[j]
+        out[:, j::per_byte] = (b >> (bits * j)) & mask
     return out
 
 
@@ -78,19 +78,23 @@ def decode_qmat(qm) -> np.ndarray:
     there) and rounded once to fp32.
     e2m1 (fmt 2): w = round_fp32(v(q) * s), v from the 3 magnitude bits, bit 3
     the sign, fp16 s per group.
+    Each group's parameters apply to its `group` consecutive columns.
     """
-    q = _unpack_codes(qm.codes, qm.bits, qm.cols)
-    G = qm.cols // qm.group
+    rows, cols, g = qm.rows, qm.cols, qm.group
+    G = cols // g
+    q = _unpack_codes(qm.codes, qm.bits, cols).reshape(rows, G, g)
     p = np.asarray(qm.params, dtype=np.uint16).view(np.float16).astype(np.float64)
     if qm.fmt == 1:
-        s = np.repeat(p[:, 0::2][:, :G], qm.group, axis=1)
-        m = np.repeat(p[:, 1::2][:, :G], qm.group, axis=1)
-        return (s * q.astype(np.float64) + m).astype(np.float32)
-    if qm.fmt == 2:
-        s = np.repeat(p[:, :G], qm.group, axis=1)
+        s = p[:, 0::2][:, :G, None]
+        m = p[:, 1::2][:, :G, None]
+        w = (s * q + m).astype(np.float32)
+    elif qm.fmt == 2:
+        s = p[:, :G, None]
         v = E2M1_TABLE[q & 7] * np.where((q & 8) != 0, -1.0, 1.0)
-        return (v * s).astype(np.float32)
-    raise ValueError(f"unknown weight format {qm.fmt}")
+        w = (v * s).astype(np.float32)
+    else:
+        raise ValueError(f"unknown weight format {qm.fmt}")
+    return w.reshape(rows, cols)
 
 
 # --------------------------------------------------------------------------
@@ -228,27 +232,19 @@ def combine(Y: np.ndarray, w: np.ndarray, inv: np.ndarray, T: int, k: int) -> np
 # Whole layer
 # --------------------------------------------------------------------------
 def moe_layer(x, x_dtype: str, Wr, b, get_expert, E: int, k: int, act: int = 0,
-              tokens=None, ids_override=None):
+              tokens=None):
     """Forward pass of the layer.
 
     get_expert(e) returns {"gate", "up", "down"} canonical block matrices; it
     is called once per expert with assignments, one expert at a time.
     tokens: optional subset of token indices whose outputs are computed (the
     routing and permutation always cover every token).
-    ids_override: route with these ids instead of the oracle's own top-k
-    (the weights are still the softmax over L[t, ids]).
     act: 0 none; 1 int8 x before gate/up; 2 int8 x and int8 h before down.
     """
     X = x_to_f64(x, x_dtype)
     T = X.shape[0]
     L = router_logits(X, Wr, b)
     ids, w, gap, flagged = topk_softmax(L, k)
-    if ids_override is not None:
-        ids = np.asarray(ids_override, dtype=np.int32)
-        for t in range(T):
-            z = L[t, ids[t]] - L[t, ids[t]].max()
-            e_ = np.exp(z)
-            w[t] = e_ / e_.sum()
     counts, offsets, perm_token, inv = canonical_permute(ids, E)
     A_all = dq8(X.astype(np.float32)) if act in (1, 2) else X
 

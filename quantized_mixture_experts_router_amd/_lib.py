@@ -19,6 +19,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_W_ASYM, MOE_W_E2M1 = 1, 2
 ACT_NONE, ACT_I8_X, ACT_I8_XH = 0, 1, 2
 FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT, FLAG_FORMAT_NOT_LAUNCHED = 1, 2, 4
+FLAG_BAD_SEGMENT, FLAG_EXPERT_SHAPE, FLAG_FP16_RANGE = 8, 16, 32
 ID_NAN = -2  # routing id of a token whose router logits include a NaN
 
 
@@ -259,14 +260,19 @@ def permute(ids, E, ws=None):
     return counts, offsets, perm[:T * k], inv[:T * k], ws
 
 
-def grouped_ffn(x, packed, offsets, perm, k, act=ACT_NONE, ws=None):
+def grouped_ffn(x, packed, offsets, perm, k, act=ACT_NONE, ws=None, Y=None, I=None):
+    """moe_grouped_ffn_q. Y: an fp32 device tensor of at least T*k*H elements
+    (a new [T*k, H] one if None); I: the intermediate size passed to the
+    library (the packed experts' own if None)."""
     x = _dev(x, "x")
     T, H = x.shape
-    Y = torch.empty((T * k, H), dtype=torch.float32, device=x.device)
+    I = packed.I if I is None else I
+    if Y is None:
+        Y = torch.empty((T * k, H), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = workspace(T, H, packed.I, packed.E, k, act, x.device)
+        ws = workspace(T, H, I, packed.E, k, act, x.device)
     _check(LIB.moe_grouped_ffn_q(_ptr(x), _dt(x), _ptr(packed.dev), packed.fmt_mask, _ptr(offsets), _ptr(perm), T, H,
-                                 packed.I, packed.E, k, act, _ptr(Y), _ptr(ws), ws.numel(), _stream()),
+                                 I, packed.E, k, act, _ptr(Y), _ptr(ws), ws.numel(), _stream()),
            "moe_grouped_ffn_q")
     return Y
 

@@ -76,7 +76,7 @@ inline char* ws_at(void* ws, size_t off) { return (char*)ws + off; }
 moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, int H, int k,
                       moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
   MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
-                          (float*)ws_at(ws, L.ascale), s));
+                          (float*)ws_at(ws, L.ascale), (uint32_t*)ws_at(ws, L.flags), s));
   return MOE_OK;
 }
 

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restri
                                                           const int32_t* __restrict__ perm, int T,
                                                           int H,
                                                           int quant, f16* __restrict__ a16,
-                                                          float* __restrict__ ascale) {
+                                                          float* __restrict__ ascale,
+                                                          uint32_t* __restrict__ flags) {
   __shared__ float s_red[kThreads / 64];
   const int r = blockIdx.x;
   const int t = perm[r];
@@ -76,11 +77,13 @@ __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restri
     }
     if (threadIdx.x == 0) ascale[r] = s;
   } else {
+    bool over = false;
     for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
       float v[8];
       load8(x, dt, base + c, v);
-      store8_f16(dst + c, v);
+      over |= store8_f16(dst + c, v);
     }
+    if (over && flags) atomicOr(flags, (uint32_t)MOE_FLAG_FP16_RANGE);
   }
 }
 
@@ -181,9 +184,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   const int c4 = blockIdx.x * kThreads + threadIdx.x;
   if (c4 >= H / 4) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int R = (int)(split_stride / H);  // T * k rows of Y
   for (int j = 0; j < k; ++j) {
     const int r = inv[(size_t)t * k + j];
-    if (r < 0) continue;  // dropped assignment (out-of-range expert id)
+    // a dropped assignment (out-of-range expert id), or a caller's inv entry
+    // outside Y's rows: no row of Y is read for it
+    if (r < 0 || r >= R) continue;
     const float wt = w[(size_t)t * k + j];
     const float* src = yp + (size_t)r * H + 4 * c4;
     f32x4 y = *reinterpret_cast<const f32x4*>(src);
@@ -206,11 +212,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
-                           int quant, f16* a16, float* ascale, hipStream_t s) {
+                           int quant, f16* a16, float* ascale, uint32_t* flags, hipStream_t s) {
   const int R = T * k;
   if (R == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_a_kernel, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, T, H, quant,
-                     a16, ascale);
+                     a16, ascale, flags);
   return hipGetLastError();
 }
 

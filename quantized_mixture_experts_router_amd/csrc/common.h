@@ -234,7 +234,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
                           void* scratch, hipStream_t s);
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
-                           int quant, f16* a16, float* ascale, hipStream_t s);
+                           int quant, f16* a16, float* ascale, uint32_t* flags, hipStream_t s);
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
                                  hipStream_t s);
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kFT) void front_kernel(
   __syncthreads();
   // 3. gather of the rows the permutation produced
   const int rows_used = *s_rows;
+  bool over = false;  // an fp16 expert input out of range
   if (!quant) {
     // every thread moves 8-column chunks of any row; a batch of kU chunks per
     // thread is loaded before any is stored, so one memory round trip covers
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kFT) void front_kernel(
             v[4 + q] = __uint_as_float(raw[u][XDT == MOE_BF16 ? 0 : 1][q]);
           }
         }
-        rows::store8_f16(a16 + dsto[u], v);
+        over |= rows::store8_f16(a16 + dsto[u], v);
       }
     }
   } else {
@@ -110,7 +111,9 @@ __global__ __launch_bounds__(kFT) void front_kernel(
       }
     }
   }
-  if (threadIdx.x == 0) *flags = bits;  // the call's flag word starts here
+  // the call's flag word starts here
+  const bool any_over = __syncthreads_or(over);
+  if (threadIdx.x == 0) *flags = bits | (any_over ? (uint32_t)MOE_FLAG_FP16_RANGE : 0u);
 }
 
 }  // namespace

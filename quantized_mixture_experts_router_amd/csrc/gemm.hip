@@ -99,11 +99,34 @@ struct Task {
   int e, row0, mcount, nt;
 };
 
-// Format id of expert e's gate/up (GU) or down matrices.
+// Rows and format of expert e as every task lookup sees them. The caller's
+// segment [offsets[e], offsets[e+1]) is clamped to [0, R) (bit
+// MOE_FLAG_BAD_SEGMENT in *bad when that changes it), so no row outside the
+// expert inputs, h or Y is ever addressed; an expert whose descriptor has
+// another H or I than the call gets no rows (MOE_FLAG_EXPERT_SHAPE), so its
+// packed matrices are never read with the call's sizes; an expert with rows
+// whose format is not in the launch mask is reported
+// (MOE_FLAG_FORMAT_NOT_LAUNCHED). Returns the format id of the expert's
+// gate/up (GU) or down matrices.
 template <bool GU>
-__device__ inline int expert_fid(const moe_packed_expert* experts, int e) {
-  const uint32_t w = reinterpret_cast<const uint32_t*>(experts + e)[GU ? 0 : 1];
-  return fmt_id(w & 0xff, (w >> 8) & 0xff, w >> 16);
+__device__ inline int expert_rows(const FfnArgs& a, int e, int& row0, int& count, uint32_t& bad) {
+  // fmt words, H and I: the descriptor's first 16 bytes
+  const u32x4 d = *reinterpret_cast<const u32x4*>(a.experts + e);
+  const int o0 = a.offsets[e], o1 = a.offsets[e + 1];
+  const int lo = min(max(o0, 0), a.R);
+  const int hi = min(max(o1, lo), a.R);
+  if (lo != o0 || hi != o1) bad |= MOE_FLAG_BAD_SEGMENT;
+  int c = hi - lo;
+  const uint32_t w = GU ? d[0] : d[1];
+  const int f = fmt_id(w & 0xff, (w >> 8) & 0xff, w >> 16);
+  if (c > 0 && (d[2] != (uint32_t)(GU ? a.K : a.N) || d[3] != (uint32_t)(GU ? a.N : a.K))) {
+    bad |= MOE_FLAG_EXPERT_SHAPE;
+    c = 0;
+  }
+  if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) bad |= MOE_FLAG_FORMAT_NOT_LAUNCHED;
+  row0 = lo;
+  count = c;
+  return f;
 }
 
 // Task lookup over the experts of format `fid` (decode): tasks of expert e
@@ -116,24 +139,20 @@ __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task
   __shared__ int s_res[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_res[0] = -1;
-  int cnt[2], ntk[2];
+  int cnt[2], ntk[2], r0[2];
   int local = 0;
-  bool missing = false;
+  uint32_t bad = 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * tid + q;
-    int c = 0, f = -1;
-    if (e < a.E) {
-      c = a.offsets[e + 1] - a.offsets[e];
-      f = expert_fid<GU>(a.experts, e);
-      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
-    }
+    int c = 0, f = -1, lo = 0;
+    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
     cnt[q] = c;
+    r0[q] = lo;
     ntk[q] = f == fid ? ((c + BM - 1) / BM) * NB : 0;
     local += ntk[q];
   }
-  if (missing && blockIdx.x == 0 && blockIdx.y == 0 && a.flags)
-    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  if (bad && blockIdx.x == 0 && blockIdx.y == 0 && a.flags) atomicOr(a.flags, bad);
   int incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -152,7 +171,7 @@ __device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task
       const int mt = (cnt[q] + BM - 1) / BM;
       const int mi = rel % mt;
       s_res[0] = e;
-      s_res[1] = a.offsets[e] + mi * BM;
+      s_res[1] = r0[q] + mi * BM;
       s_res[2] = min(BM, cnt[q] - mi * BM);
       s_res[3] = rel / mt;
     }
@@ -188,26 +207,22 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   if (tid == 0) s_res[0] = -1;
-  int cnt[2], nfu[2], npa[2];
+  int cnt[2], nfu[2], npa[2], r0[2];
   int lf = 0, lp = 0;
-  bool missing = false;
+  uint32_t bad = 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * tid + q;
-    int c = 0, f = -1;
-    if (e < a.E) {
-      c = a.offsets[e + 1] - a.offsets[e];
-      f = expert_fid<GU>(a.experts, e);
-      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
-    }
+    int c = 0, f = -1, lo = 0;
+    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
     cnt[q] = c;
+    r0[q] = lo;
     nfu[q] = f == fid ? (c / BM) * NB : 0;
     npa[q] = f == fid && c % BM ? NB : 0;
     lf += nfu[q];
     lp += npa[q];
   }
-  if (missing && blockIdx.x == 0 && a.flags)
-    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  if (bad && blockIdx.x == 0 && a.flags) atomicOr(a.flags, bad);
   int incf = lf, incp = lp;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -248,7 +263,7 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
           const int mt = (cnt[q] + BM - 1) / BM;
           const int mi = rel % mt;
           s_res[0] = 2 * tid + q;
-          s_res[1] = a.offsets[2 * tid + q] + mi * BM;
+          s_res[1] = r0[q] + mi * BM;
           s_res[2] = min(BM, cnt[q] - mi * BM);
           s_res[3] = rel / mt;
         }
@@ -277,7 +292,7 @@ __device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, 
           const int mf = cnt[q] / BM;  // full m-tiles of the expert
           const int mi = full ? rel % mf : mf;
           s_res[0] = e;
-          s_res[1] = a.offsets[e] + mi * BM;
+          s_res[1] = r0[q] + mi * BM;
           s_res[2] = min(BM, cnt[q] - mi * BM);
           s_res[3] = full ? rel / mf : rel;
         }
@@ -313,19 +328,16 @@ __device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b,
   const int nwaves = blockDim.x >> 6;
   if (tid == 0) s_res[0] = -1;
   const int SUB = BM / 4;  // rows of a sub-tile class step
-  int cnt[2], ncl[2][NC], cls[2];
+  int cnt[2], ncl[2][NC], cls[2], r0[2];
   int lsum[NC] = {0, 0, 0, 0};
-  bool missing = false;
+  uint32_t bad = 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * tid + q;
-    int c = 0, f = -1;
-    if (e < a.E) {
-      c = a.offsets[e + 1] - a.offsets[e];
-      f = expert_fid<GU>(a.experts, e);
-      if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) missing = true;
-    }
+    int c = 0, f = -1, lo = 0;
+    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
     cnt[q] = c;
+    r0[q] = lo;
     const bool mine = f == fid;
     const int rem = c % BM;
     // class of the partial tile: 0 (as long as a full one) .. 3 (shortest)
@@ -339,8 +351,7 @@ __device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b,
 #pragma unroll
     for (int k = 0; k < NC; ++k) lsum[k] += ncl[q][k];
   }
-  if (missing && blockIdx.x == 0 && a.flags)
-    atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+  if (bad && blockIdx.x == 0 && a.flags) atomicOr(a.flags, bad);
   int inc[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) inc[k] = lsum[k];
@@ -418,7 +429,7 @@ __device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b,
             nt = rel;
           }
           s_res[0] = e;
-          s_res[1] = a.offsets[e] + mi * BM;
+          s_res[1] = r0[q] + mi * BM;
           s_res[2] = min(BM, cnt[q] - mi * BM);
           s_res[3] = nt;
         }
@@ -439,13 +450,19 @@ __device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b,
   return task.e >= 0;
 }
 
-__device__ inline void store_gu(const FfnArgs& a, int row, int col, float g, float u) {
+// fp16 holds |v| <= 65504; beyond, the stored h is +-inf
+constexpr float kF16Max = 65504.0f;
+
+// stores h = silu(g) * u; true when h is stored as fp16 and overflows it
+__device__ inline bool store_gu(const FfnArgs& a, int row, int col, float g, float u) {
   const float sc = a.ascale ? a.ascale[row] : 1.0f;
   const float h = silu_mul(g * sc, u * sc);
-  if (a.out_f32)
+  if (a.out_f32) {
     reinterpret_cast<float*>(a.out)[(size_t)row * a.N + col] = h;
-  else
-    reinterpret_cast<f16*>(a.out)[(size_t)row * a.N + col] = (f16)h;
+    return false;
+  }
+  reinterpret_cast<f16*>(a.out)[(size_t)row * a.N + col] = (f16)h;
+  return fabsf(h) > kF16Max;
 }
 
 __device__ inline void store_dn(const FfnArgs& a, int split, int row, int col, float y) {
@@ -579,6 +596,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   if (!on) return;
   const int RPW = 16 / ksw;
   const int w0 = grp * ksw;
+  bool over = false;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r / RPW != ks || !live(r)) continue;
@@ -595,13 +613,14 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
     if (i < t.mcount) {
       const int row = t.row0 + i;
       if (GU) {
-        store_gu(a, row, 32 * rg + n, v0, v1);
+        over |= store_gu(a, row, 32 * rg + n, v0, v1);
       } else {
         store_dn(a, split, row, 64 * rg + n, v0);
         store_dn(a, split, row, 64 * rg + 32 + n, v1);
       }
     }
   }
+  if (over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
 }
 
 // decode: fewest K tiles a wavefront of a K-split group streams
@@ -870,6 +889,8 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     __syncthreads();
     if (!on) return;
     uint8_t* stg = (wave >> 1 ? lds1 : lds0) + (wave & 1) * kStageB;
+    bool over = false;  // an fp16 h out of range (rows past the segment
+                        // repeat its last row, so they add no false report)
 #pragma unroll
     for (int mi = 0; mi < AMT; ++mi) {
 #pragma unroll
@@ -884,10 +905,12 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
           if constexpr (GU) {
             const float sc = (a.ascale && i0 + lr < t.mcount) ? a.ascale[t.row0 + i0 + lr] : 1.0f;
             const float h = silu_mul(acc[mi][0][r] * sc, acc[mi][1][r] * sc);
-            if (a.out_f32)
+            if (a.out_f32) {
               reinterpret_cast<float*>(stg)[lr * 36 + n] = h;
-            else
+            } else {
               reinterpret_cast<f16*>(stg)[lr * 40 + n] = (f16)h;
+              over |= fabsf(h) > kF16Max;
+            }
           } else {
             reinterpret_cast<float*>(stg)[lr * 72 + n] = acc[mi][0][r];
             reinterpret_cast<float*>(stg)[lr * 72 + 32 + n] = acc[mi][1][r];
@@ -932,6 +955,7 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         }
       }
     }
+    if (GU && over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
   };
   if (amt > 3 * kMT / 4)
     run(IntC<kMT>{});

@@ -41,11 +41,18 @@ __device__ inline void load8(const void* x, int dt, size_t idx, float* v) {
   }
 }
 
-__device__ inline void store8_f16(f16* dst, const float* v) {
+// stores 8 values as fp16; true when one of them is beyond the fp16 range
+// (|v| > 65504: stored as +-inf)
+__device__ inline bool store8_f16(f16* dst, const float* v) {
   f16x8 h;
+  bool over = false;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) h[q] = (f16)v[q];
+  for (int q = 0; q < 8; ++q) {
+    h[q] = (f16)v[q];
+    over |= fabsf(v[q]) > 65504.0f;
+  }
   *reinterpret_cast<f16x8*>(dst) = h;
+  return over;
 }
 
 }  // namespace rows

@@ -51,3 +51,25 @@ def rel_l2_rows(got, ref):
 
 def tolerance(cfg):
     return TOL_I8 if cfg.act != 0 else TOL_F
+
+
+def prefill_order(T, H, I, E, k, bm=128, blocks_per_cu=2):
+    """The kernel family and prefill task order the library picks for these
+    sizes (for the test log): decode GEMV below 48 rows per expert, else the
+    prefill GEMM in expert-major order (lpt 0) from 4 blocks per block slot,
+    longest first below that (lpt 1; the down projection uses four size
+    classes below 2 blocks per slot, lpt 2)."""
+    R = T * k
+    if R < 48 * E:
+        return "decode GEMV"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    slots = cus * blocks_per_cu
+    tiles = (R + bm - 1) // bm + min(R, E)
+    out = []
+    for what, units in (("gate/up", I // 32), ("down", H // 64)):
+        nblk = tiles * ((units + 3) // 4)
+        lpt = 2 if nblk < 2 * slots else (1 if nblk < 4 * slots else 0)
+        if what == "gate/up" and lpt == 2:
+            lpt = 1
+        out.append(f"{what} {nblk} blocks lpt {lpt}")
+    return "prefill GEMM: " + ", ".join(out)

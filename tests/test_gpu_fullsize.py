@@ -3,8 +3,14 @@ benchmark times (moe_layer_forward, one call, device-resident inputs).
 
 Routing is checked on every token (ids bit-exact except oracle-flagged
 near-ties) and the permutation on every assignment (bit-exact against the
-canonical permutation of the GPU's ids); layer outputs are checked on a
-sample of tokens whose experts the oracle decodes one at a time."""
+canonical permutation of the GPU's ids). Layer outputs are checked on every
+token for the Mixtral-shaped, fine-grained and hot/cold layers: the oracle
+runs once per workload over its largest batch, and the decode batches, whose
+tokens are the first rows of the same seeded stream (a token's output depends
+on that token alone), are compared against the same rows. The W4A8 layer
+(13.7 GB of experts) is checked on 8 experts: every row of each one's last,
+partial 128-row m-tile and a sample of its other rows (per-assignment expert
+outputs Y), and every token whose two experts are both among the 8."""
 import sys
 
 import numpy as np
@@ -13,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from layer_cases import Workload, rel_l2_rows, tolerance
+from layer_cases import Workload, prefill_order, rel_l2_rows, tolerance, x_to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -30,71 +36,159 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _sample_tokens(ids, flagged, n_tokens, max_experts):
-    """Up to n_tokens non-flagged tokens whose experts stay within a set of at
-    most max_experts (greedy, in token order)."""
-    chosen, experts = [], set()
-    for t in range(ids.shape[0]):
-        if flagged[t]:
-            continue
-        new = experts | set(ids[t].tolist())
-        if len(new) <= max_experts:
-            chosen.append(t)
-            experts = new
-        if len(chosen) == n_tokens:
-            break
-    return chosen
+_WL = {}
 
 
-CASES = [
-    # name, T, sampled tokens, max distinct experts decoded by the oracle
-    ("mixtral", 1, 1, 2),
-    ("mixtral", 32, 6, 3),
-    ("mixtral", 2048, 8, 3),
-    ("fine_e2m1", 1, 1, 6),
-    ("fine_e2m1", 64, 16, 40),
-    ("fine_e2m1", 4096, 24, 40),
-    ("hotcold", 4096, 24, 40),
-    ("w4a8", 16, 2, 3),
-    ("w4a8", 8192, 3, 3),
-]
+def _workload(name):
+    if name not in _WL:
+        _WL.clear()  # one workload's experts on the device at a time
+        torch.cuda.empty_cache()
+        _WL[name] = Workload(synth.get_config(name))
+    return _WL[name]
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,T,ns,me", CASES)
-def test_fullsize_layer(moeq, name, T, ns, me):
-    cfg = synth.get_config(name, T=T)
-    _say(f"[fullsize] {name} T={T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} act={cfg.act}")
-    wl = Workload(cfg)
-    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act)
-    ids2, w2 = moeq.route(wl.x, wl.Wr, wl.b, cfg.k)
-    counts, offsets, perm, inv, ws = moeq.permute(ids2, cfg.E)
+_REF = {}
+
+
+def _oracle_all(name, wl):
+    """The oracle over every token of the workload's largest batch."""
+    if name not in _REF:
+        cfg = wl.cfg
+        b = wl.b_np if cfg.zipf_alpha > 0 else None
+        _say(f"    oracle over all {cfg.T} tokens of {name} ...")
+        _REF[name] = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, b, wl.expert_uncached,
+                                      cfg.E, cfg.k, act=cfg.act)
+    return _REF[name]
+
+
+def _check_routing(moeq, wl, T, ids, w, ref_ids, ref_w, flagged):
+    """ids bit-exact except near-ties; the permutation of the GPU's ids is the
+    canonical one."""
+    cfg = wl.cfg
+    ids_np = ids.cpu().numpy()
+    ok = ~flagged
+    np.testing.assert_array_equal(ids_np[ok], ref_ids[ok])
+    assert np.max(np.abs(w.cpu().numpy()[ok] - ref_w[ok])) <= 1e-6
+    counts, offsets, perm, inv, ws = moeq.permute(ids, cfg.E)
     torch.cuda.synchronize()
     assert moeq.read_flags(ws) == 0
-    ids_np = ids.cpu().numpy()
-    assert np.array_equal(ids_np, ids2.cpu().numpy())
-
-    # routing on every token
-    b = wl.b_np if cfg.zipf_alpha > 0 else None
-    L = oracle.router_logits(oracle.x_to_f64(wl.x_np, cfg.x_dtype), wl.Wr_np, b)
-    rids, rw, gap, flagged = oracle.topk_softmax(L, cfg.k)
-    ok = ~flagged
-    np.testing.assert_array_equal(ids_np[ok], rids[ok])
-    assert np.max(np.abs(w.cpu().numpy()[ok] - rw[ok])) <= 1e-6
-    # permutation on every assignment
     rc, ro, rp, ri = oracle.canonical_permute(ids_np, cfg.E)
     np.testing.assert_array_equal(counts.cpu().numpy(), rc)
     np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
     np.testing.assert_array_equal(perm.cpu().numpy(), rp)
     np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+    return ok
 
-    # outputs on sampled tokens
-    toks = _sample_tokens(ids_np, flagged, ns, me)
-    assert toks, "no unflagged token to sample"
-    _say(f"    sampled tokens {toks}, experts {sorted(set(ids_np[toks].reshape(-1).tolist()))}")
-    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, b, wl.expert_uncached, cfg.E, cfg.k,
-                           act=cfg.act, tokens=toks, ids_override=ids_np)
-    got = out.cpu().numpy()[toks]
-    err = rel_l2_rows(got, ref["out"][toks])
-    _say(f"    max row rel-L2 {err.max():.3e} (flagged tokens {int(flagged.sum())})")
-    assert err.max() <= tolerance(cfg), err.max()
+
+FULL_CASES = [
+    ("mixtral", (1, 8, 32, 2048)),
+    ("fine_e2m1", (1, 64, 4096)),
+    ("hotcold", (4096,)),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,Ts", FULL_CASES)
+def test_fullsize_every_token(moeq, name, Ts):
+    wl = _workload(name)
+    cfg = wl.cfg
+    outs = {}
+    for T in Ts:
+        _say(f"[fullsize] {name} T={T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} act={cfg.act} "
+             f"({prefill_order(T, cfg.H, cfg.I, cfg.E, cfg.k)})")
+        x = wl.x[:T].contiguous()
+        ws = moeq.workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+        out, ids, w = moeq.layer_forward(x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+        torch.cuda.synchronize()
+        assert moeq.read_flags(ws) == 0
+        outs[T] = (out.cpu().numpy(), ids, w)
+    ref = _oracle_all(name, wl)
+    for T in Ts:
+        out, ids, w = outs[T]
+        ok = _check_routing(moeq, wl, T, ids, w, ref["ids"][:T], ref["w"][:T], ref["flagged"][:T])
+        err = rel_l2_rows(out[ok], ref["out"][:T][ok])
+        _say(f"    T={T}: every token, max row rel-L2 {err.max():.3e} mean {err.mean():.3e} "
+             f"(flagged {int((~ok).sum())})")
+        assert err.max() <= tolerance(cfg), err.max()
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_w4a8(moeq):
+    """W4A8 at 16 and 8192 tokens: routing and permutation on every token;
+    expert outputs Y on 8 experts (all rows of each one's partial last
+    m-tile plus 48 others); combined outputs of every token routed only to
+    those experts."""
+    name = "w4a8"
+    wl = _workload(name)
+    cfg = wl.cfg
+    X = oracle.x_to_f64(wl.x_np, cfg.x_dtype)
+    L = oracle.router_logits(X, wl.Wr_np, None)
+    rids, rw, gap, flagged = oracle.topk_softmax(L, cfg.k)
+    gpu = {}
+    for T in (16, cfg.T):
+        _say(f"[fullsize] {name} T={T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} act={cfg.act} "
+             f"({prefill_order(T, cfg.H, cfg.I, cfg.E, cfg.k)})")
+        x = wl.x[:T].contiguous()
+        ws = moeq.workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+        out, ids, w = moeq.layer_forward(x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+        torch.cuda.synchronize()
+        assert moeq.read_flags(ws) == 0
+        ok = _check_routing(moeq, wl, T, ids, w, rids[:T], rw[:T], flagged[:T])
+        counts, offsets, perm, inv, _ = moeq.permute(ids, cfg.E)
+        Y = moeq.grouped_ffn(x, wl.packed, offsets, perm, cfg.k, act=cfg.act)
+        torch.cuda.synchronize()
+        gpu[T] = dict(out=out.cpu().numpy(), Y=Y.cpu().numpy(), ok=ok,
+                      ids=ids.cpu().numpy(), counts=counts.cpu().numpy(),
+                      offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
+                      inv=inv.cpu().numpy())
+        del out, Y, ws
+    # the 8 experts: those of the first decode tokens, then evenly spread ones
+    S = []
+    for e in list(gpu[16]["ids"][:4].reshape(-1)) + list(range(0, cfg.E, cfg.E // 8)):
+        if int(e) not in S and len(S) < 8:
+            S.append(int(e))
+    _say(f"    experts checked {S}")
+    A_all = oracle.dq8(X.astype(np.float32))
+    rng = np.random.default_rng(7)
+    Sset = set(S)
+    # per batch: the tokens routed only to experts in S, and their rows
+    full_toks, full_rows = {}, {}
+    for T, g in gpu.items():
+        full_toks[T] = [t for t in range(T) if g["ok"][t] and set(g["ids"][t].tolist()) <= Sset]
+        full_rows[T] = {int(g["inv"][t * cfg.k + j]) for t in full_toks[T] for j in range(cfg.k)}
+    Yref = {T: {} for T in gpu}
+    for e in S:
+        ex = wl.expert_uncached(e)
+        Wg, Wu, Wd = (oracle.decode_qmat(ex["gate"]), oracle.decode_qmat(ex["up"]),
+                      oracle.decode_qmat(ex["down"]))
+        for T, g in gpu.items():
+            r0, r1 = int(g["offsets"][e]), int(g["offsets"][e + 1])
+            if r1 == r0:
+                continue
+            c = r1 - r0
+            last = np.arange(r0 + (c // 128) * 128, r1)             # partial m-tile
+            others = np.arange(r0, r0 + (c // 128) * 128)
+            if others.size > 48:
+                others = rng.choice(others, 48, replace=False)
+            mine = [r for r in full_rows[T] if r0 <= r < r1]
+            rows = np.unique(np.concatenate([others, last, mine]).astype(np.int64))
+            ya = oracle.expert_ffn(A_all[g["perm"][rows]], Wg, Wu, Wd, cfg.act)
+            for r, y in zip(rows, ya):
+                Yref[T][int(r)] = y
+            err = rel_l2_rows(g["Y"][rows], ya)
+            _say(f"    T={T} expert {e}: {c} rows, {last.size} in the partial m-tile, "
+                 f"{rows.size} checked, max row rel-L2 {err.max():.3e}")
+            assert err.max() <= tolerance(cfg), (T, e, err.max())
+        del Wg, Wu, Wd
+    # combined outputs of the tokens whose experts are all in S
+    for T, g in gpu.items():
+        toks = full_toks[T]
+        assert toks or T == 16
+        if not toks:
+            continue
+        ref = np.stack([sum(rw[t, j] * Yref[T][int(g["inv"][t * cfg.k + j])] for j in range(cfg.k))
+                        for t in toks])
+        err = rel_l2_rows(g["out"][toks], ref)
+        _say(f"    T={T}: {len(toks)} tokens fully within the checked experts, "
+             f"max row rel-L2 {err.max():.3e}")
+        assert err.max() <= tolerance(cfg), err.max()

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from layer_cases import Workload, rel_l2_rows, tolerance, x_to_torch
+from layer_cases import Workload, prefill_order, rel_l2_rows, tolerance, x_to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -234,13 +234,17 @@ LAYER_CASES = [
     # few weight rows in flight: K split over more wavefronts (8-tile streams)
     ("fine_e2m1", 1, 2048, 256, 32, 6),
     ("fine_e2m1", 3, 1024, 256, 32, 6),
+    # expert-major prefill order: 2304 gate/up blocks, at least 4 per block slot
+    # of a 256-CU device (the down launch, 72 blocks, takes the four-class order)
+    ("mixtral", 4096, 256, 4096, 8, 2),
 ]
 
 
 def _run_layer_case(moeq, name, T, H, I, E, k, weight_mode="quantize"):
     cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode=weight_mode,
                               n_hot=min(64, E // 4) if name == "hotcold" else None)
-    _say(f"[layer] {name} T={T} H={H} I={I} E={E} k={k} act={cfg.act}")
+    _say(f"[layer] {name} T={T} H={H} I={I} E={E} k={k} act={cfg.act} "
+         f"({prefill_order(T, H, I, E, k)})")
     wl = Workload(cfg)
     out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act)
     torch.cuda.synchronize()
@@ -540,3 +544,89 @@ def test_router_i8_parity(moeq, T, H, E, k, shared):
     ids_x, _, _, _ = oracle.topk_softmax(L[:T], k)
     same = np.mean([set(a) == set(b2) for a, b2 in zip(ids.cpu().numpy(), ids_x)])
     _say(f"    ambiguous {int(amb.sum())}; same expert set as exact routing {same:.3f}")
+
+
+# ------------------------------------------------------------ data-dependent flags
+@pytest.mark.parametrize("T", [40, 600])  # decode GEMV / prefill GEMM
+@pytest.mark.parametrize("scale,where", [(1e5, "input"), (2000.0, "h")])
+def test_fp16_range_flag(moeq, T, scale, where):
+    """One token scaled so that its fp16 expert input (x 1e5) or its SwiGLU
+    output h (x 2000: inputs stay within fp16, h does not) leaves the fp16
+    range: MOE_FLAG_FP16_RANGE is raised and every other token still matches
+    the oracle."""
+    cfg = synth.scaled_config("mixtral", T=T, H=512, I=1024, E=8, k=2, weight_mode="quantize")
+    _say(f"[fp16-range] T={T} x{scale:g} ({where})")
+    wl = Workload(cfg)
+    bad = T // 2
+    x32 = synth.bf16_bits_to_f32(wl.x_np).copy()
+    x32[bad] *= np.float32(scale)
+    xb = synth.f32_to_bf16_bits(x32)
+    if where == "h":
+        assert np.abs(synth.bf16_bits_to_f32(xb)).max() < 65504
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    out, ids, w = moeq.layer_forward(x_to_torch(xb, "bf16"), wl.Wr, wl.b, wl.packed, cfg.k, ws=ws)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) & moeq.FLAG_FP16_RANGE
+    ref = oracle.moe_layer(xb, "bf16", wl.Wr_np, None, wl.expert, cfg.E, cfg.k)
+    ok = ~ref["flagged"]
+    ok[bad] = False
+    np.testing.assert_array_equal(ids.cpu().numpy()[ok], ref["ids"][ok])
+    err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
+    assert err.max() <= tolerance(cfg), err.max()
+    # the unscaled batch raises nothing
+    moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, ws=ws)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) == 0
+
+
+@pytest.mark.parametrize("T", [40, 600])
+def test_bad_offsets_are_clamped(moeq, T):
+    """Caller offsets past T*k, or decreasing, are clamped inside the task
+    lookups: MOE_FLAG_BAD_SEGMENT is raised, nothing past Y's T*k rows is
+    written (a canary tail stays intact), and with offsets[E] just past T*k
+    the rows that exist equal those of the correct offsets."""
+    cfg = synth.scaled_config("mixtral", T=T, H=512, I=1024, E=8, k=2, weight_mode="quantize")
+    _say(f"[bad-offsets] T={T}")
+    wl = Workload(cfg)
+    R, H = T * cfg.k, cfg.H
+    ids, w = moeq.route(wl.x, wl.Wr, wl.b, cfg.k)
+    counts, offsets, perm, inv, _ = moeq.permute(ids, cfg.E)
+    Y0 = moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k)
+    torch.cuda.synchronize()
+    canary = -12345.0
+    for kind in ("past_end", "decreasing", "negative"):
+        off = offsets.clone()
+        if kind == "past_end":
+            off[cfg.E] = R + 7
+        elif kind == "decreasing":
+            off[3] = off[2] - 5
+        else:
+            off[0] = -9
+        Yb = torch.full(((R + 64) * H,), canary, dtype=torch.float32, device="cuda")
+        ws = moeq.workspace(T, H, cfg.I, cfg.E, cfg.k)
+        ws[:4].zero_()
+        moeq.grouped_ffn(wl.x, wl.packed, off, perm, cfg.k, ws=ws, Y=Yb)
+        torch.cuda.synchronize()
+        assert moeq.read_flags(ws) & moeq.FLAG_BAD_SEGMENT, kind
+        assert (Yb[R * H:] == canary).all(), kind
+        if kind == "past_end":
+            assert torch.equal(Yb[:R * H].view(R, H), Y0)
+
+
+def test_expert_shape_mismatch_is_skipped(moeq):
+    """Experts packed with I = 256 called with I = 128: MOE_FLAG_EXPERT_SHAPE,
+    and no row of Y is written (prefill sizes: the down GEMM writes Y
+    directly)."""
+    cfg = synth.scaled_config("mixtral", T=600, H=512, I=256, E=8, k=2, weight_mode="quantize")
+    wl = Workload(cfg)
+    R, H = cfg.T * cfg.k, cfg.H
+    ids, w = moeq.route(wl.x, wl.Wr, wl.b, cfg.k)
+    counts, offsets, perm, inv, _ = moeq.permute(ids, cfg.E)
+    canary = 777.0
+    Yb = torch.full((R * H,), canary, dtype=torch.float32, device="cuda")
+    ws = moeq.workspace(cfg.T, H, 128, cfg.E, cfg.k)
+    ws[:4].zero_()
+    moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k, ws=ws, Y=Yb, I=128)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) & moeq.FLAG_EXPERT_SHAPE
+    assert (Yb == canary).all()

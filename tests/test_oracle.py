@@ -543,6 +543,31 @@ def test_i8_router_exact_on_the_grid():
     np.testing.assert_array_equal(w, w0)
 
 
+def test_i8_router_ambiguity_mask():
+    """The mask fires exactly for tokens with some L/s within 1e-9 of a
+    half-integer (where the rounding of an fp64 sum could decide the code):
+    hand-placed logits at, near and away from a rounding boundary."""
+    s = np.array([0.25, 0.5, 0.125], dtype=np.float32)   # exact in fp32
+    z = np.array([3, -7, 0])
+    sd = s.astype(np.float64)
+    L = np.array([
+        [2.5 * sd[0], 0.1, 0.3],               # L/s = 2.5 exactly -> ambiguous
+        [0.1, (-3.5 + 4e-10) * sd[1], 0.3],    # 4e-10 from -3.5 -> ambiguous
+        [0.1, 0.3, (7.5 + 5e-9) * sd[2]],      # 5e-9 away -> not ambiguous
+        [0.1, 0.3, 0.77],                      # L/s = 0.4, 0.6, 6.16 -> not
+        [(2.5 - 3e-9) * sd[0], 0.3, 0.77],     # 3e-9 below 2.5 -> not
+    ])
+    _, amb = oracle.quantize_logits_i8(L, s, z)
+    np.testing.assert_array_equal(amb, [True, True, False, False, False])
+    # an expert whose scale is 0 never makes a token ambiguous
+    _, amb0 = oracle.quantize_logits_i8(np.zeros((2, 3)), np.zeros(3, np.float32), z)
+    np.testing.assert_array_equal(amb0, [False, False])
+    # random logits: a boundary within 1e-9 is a rare event
+    rng = np.random.default_rng(34)
+    _, ambr = oracle.quantize_logits_i8(rng.standard_normal((2000, 3)), s, z)
+    assert ambr.sum() == 0
+
+
 def test_i8_router_params_map_range_to_codes():
     rng = np.random.default_rng(32)
     for shared in (False, True):
