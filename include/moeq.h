@@ -260,6 +260,32 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
                              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): moe_layer_forward
+ * with its workspace in a device array inside the library instead of a
+ * caller buffer. Each GPU the library runs on holds one such array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) from the first call made with that GPU
+ * current until the process ends; the call itself allocates nothing.
+ * Sizes whose workspace (moe_workspace_size) exceeds it return
+ * MOE_ERR_WORKSPACE before anything is enqueued: decode-size batches fit
+ * (the Mixtral-shaped layer up to 314 tokens, the H=8192, I=16384 W4A8 one
+ * up to 113).
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two host threads)
+ * race and must be ordered by the caller. Nothing in the array needs to
+ * start at zero; the call writes its flag word itself.
+ * flags (device, optional, 4-byte aligned): receives the call's flag word
+ * (MOE_FLAG_*) in place of the workspace's first word; NULL keeps it inside
+ * the array, where the caller cannot read it.
+ * Other arguments, outputs and results as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t moe_noalloc_scratch_bytes(void);
+moe_status moe_layer_forward_noalloc(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                                     const moe_packed_expert* experts, uint32_t fmt_mask, int T,
+                                     int H, int I, int E, int k, moe_actq aq, void* out,
+                                     moe_dtype out_dt, int32_t* topk_ids, float* topk_w,
+                                     uint32_t* flags, void* stream);
+
 /* Per-token dynamic int8 quantisation of rows (mixed-precision notes,
  * sections 2.1-2.2), the arithmetic the layer applies to its expert inputs
  * under MOE_ACT_I8_*: per row s = fp32(absmax)/127, q = clamp(rint(v/s),

@@ -70,6 +70,8 @@ _SIGS = {
     "moe_combine": ([_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
     "moe_layer_forward": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_stream_read": ([_vp, _sz, _i, _vp, _vp], _i),
+    "moe_noalloc_scratch_bytes": ([], _sz),
+    "moe_layer_forward_noalloc": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "moe_expert_histogram": ([_vp, _i, _i, _i, _vp, _vp], _i),
     "moe_plan_tiers": ([_vp, _i, _vp, _i, ctypes.c_uint64, _vp, _vp], _i),
@@ -317,6 +319,32 @@ def layer_forward(x, Wr, b, packed, k, act=ACT_NONE, out_dtype=torch.float32, ws
     _check(LIB.moe_layer_forward(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), _ptr(packed.dev), packed.fmt_mask, T, H, packed.I,
                                  E, k, act, _ptr(out), _dt(out), _ptr(ids), _ptr(w), _ptr(ws),
                                  ws.numel(), _stream()), "moe_layer_forward")
+    return out, ids, w
+
+
+def noalloc_scratch_bytes():
+    return int(LIB.moe_noalloc_scratch_bytes())
+
+
+def layer_forward_noalloc(x, Wr, b, packed, k, act=ACT_NONE, out_dtype=torch.float32, out=None,
+                          ids=None, w=None, flags=None):
+    """moe_layer_forward_noalloc: the layer on the library's own device scratch
+    array. flags: an int32 device tensor of >= 1 element receiving the flag
+    word, or None. Output tensors are created here when not given (the
+    library call itself allocates nothing)."""
+    x, Wr = _dev(x, "x"), _dev(Wr, "Wr")
+    T, H = x.shape
+    E = Wr.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(LIB.moe_layer_forward_noalloc(_ptr(x), _dt(x), _ptr(Wr), _ptr(b), _ptr(packed.dev),
+                                         packed.fmt_mask, T, H, packed.I, E, k, act, _ptr(out),
+                                         _dt(out), _ptr(ids), _ptr(w), _ptr(flags), _stream()),
+           "moe_layer_forward_noalloc")
     return out, ids, w
 
 

@@ -84,8 +84,8 @@ inline uint32_t effective_mask(uint32_t m) { return m ? m : ((1u << F_COUNT) - 1
 
 moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
                        int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
-                       hipStream_t s) {
-  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), (uint32_t*)ws_at(ws, L.flags),
+                       uint32_t* flags, hipStream_t s) {
+  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), flags,
                              T, H, I, E, k, (const f16*)ws_at(ws, L.a16),
                              aq != MOE_ACT_NONE ? (const float*)ws_at(ws, L.ascale) : nullptr,
                              ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, s));
@@ -94,7 +94,7 @@ moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const in
 
 moe_status run_down(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
                     int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
-                    float* yp, hipStream_t s) {
+                    uint32_t* flags, float* yp, hipStream_t s) {
   const int R = T * k;
   const f16* ain = (const f16*)ws_at(ws, L.h);
   const float* sc = nullptr;
@@ -105,8 +105,8 @@ moe_status run_down(const moe_packed_expert* experts, uint32_t mask, const int32
     ain = h16;
     sc = hs;
   }
-  MOE_TRY(launch_ffn_down(experts, offsets, effective_mask(mask), (uint32_t*)ws_at(ws, L.flags), T,
-                          H, I, E, k, ain, sc, yp, L.splits, L.decode, s));
+  MOE_TRY(launch_ffn_down(experts, offsets, effective_mask(mask), flags, T, H, I, E, k, ain, sc,
+                          yp, L.splits, L.decode, s));
   return MOE_OK;
 }
 
@@ -129,6 +129,64 @@ moe_status check_experts(const void* experts, const int32_t* offsets) {
 }
 
 }  // namespace
+
+namespace moeq {
+
+// The whole layer on a validated workspace `ws` (layout L). flags: where the
+// call's flag word goes (nullptr: the workspace's own).
+moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                            const moe_packed_expert* experts, uint32_t fmt_mask, int T, int H,
+                            int I, int E, int k, moe_actq aq, void* out, moe_dtype out_dt,
+                            int32_t* topk_ids, float* topk_w, void* ws, const WsLayout& L,
+                            uint32_t* flags, hipStream_t s) {
+  if (!experts) return MOE_ERR_INVALID_ARG;
+  if (!aligned(experts, 16)) return MOE_ERR_ALIGNMENT;
+  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, out_dt == MOE_F32 ? 16 : 8))
+    return MOE_ERR_ALIGNMENT;
+  if (!flags) flags = (uint32_t*)ws_at(ws, L.flags);
+  int32_t* ids = topk_ids ? topk_ids : (int32_t*)ws_at(ws, L.ids);
+  float* w = topk_w ? topk_w : (float*)ws_at(ws, L.w);
+  int32_t* counts = (int32_t*)ws_at(ws, L.counts);
+  int32_t* offsets = (int32_t*)ws_at(ws, L.offsets);
+  int32_t* perm = (int32_t*)ws_at(ws, L.perm);
+  int32_t* inv = (int32_t*)ws_at(ws, L.inv);
+  float* yp = (float*)ws_at(ws, L.yp);
+  double* rpart = (double*)ws_at(ws, L.rpart);
+  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
+  const int kb = route_plan(T, H, E).kb;
+  moe_status st;
+  if (L.decode && front_fits(T, H, E, k)) {
+    // small batch: top-k, permutation and gather in one block
+    MOE_TRY(launch_front(rpart, kb, x, xdt, b, T, H, E, k, ids, w, counts, offsets, perm, inv,
+                         flags, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
+                         (float*)ws_at(ws, L.ascale), s));
+  } else {
+    MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
+    MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags,
+                           ws_at(ws, L.pscratch), s));
+    MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
+                            (float*)ws_at(ws, L.ascale), flags, s));
+  }
+  st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, s);
+  if (st != MOE_OK) return st;
+  st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, yp, s);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(yp, L.decode ? L.splits : 1, w, inv, T, H, k, out, out_dt, s));
+}
+
+moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, WsLayout& L) {
+  moe_status st = check_sizes(T, H, I, E, k);
+  if (st != MOE_OK) return st;
+  if (aq < MOE_ACT_NONE || aq > MOE_ACT_I8_XH) return MOE_ERR_INVALID_ARG;
+  L = ws_layout(T, H, I, E, k, aq);
+  return MOE_OK;
+}
+
+}  // namespace moeq
 
 extern "C" {
 
@@ -323,7 +381,8 @@ moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  return run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, (hipStream_t)stream);
+  return run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+                     (uint32_t*)ws_at(ws, L.flags), (hipStream_t)stream);
 }
 
 moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
@@ -340,11 +399,13 @@ moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
   const size_t n = (size_t)T * k * H;
   if (L.decode && L.splits > 1) {
     float* yp = (float*)ws_at(ws, L.yp);
-    st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, yp, s);
+    st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+                  (uint32_t*)ws_at(ws, L.flags), yp, s);
     if (st != MOE_OK) return st;
     return hip_status(launch_reduce_splits(yp, L.splits, n, Y, s));
   }
-  return run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, Y, s);
+  return run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+                  (uint32_t*)ws_at(ws, L.flags), Y, s);
 }
 
 moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expert* experts,
@@ -383,43 +444,8 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
   WsLayout L;
   moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
-  if (!experts) return MOE_ERR_INVALID_ARG;
-  if (!aligned(experts, 16)) return MOE_ERR_ALIGNMENT;
-  if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (out_dt != MOE_F32 && out_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !Wr || !out) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, out_dt == MOE_F32 ? 16 : 8))
-    return MOE_ERR_ALIGNMENT;
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t* flags = (uint32_t*)ws_at(ws, L.flags);
-  int32_t* ids = topk_ids ? topk_ids : (int32_t*)ws_at(ws, L.ids);
-  float* w = topk_w ? topk_w : (float*)ws_at(ws, L.w);
-  int32_t* counts = (int32_t*)ws_at(ws, L.counts);
-  int32_t* offsets = (int32_t*)ws_at(ws, L.offsets);
-  int32_t* perm = (int32_t*)ws_at(ws, L.perm);
-  int32_t* inv = (int32_t*)ws_at(ws, L.inv);
-  float* yp = (float*)ws_at(ws, L.yp);
-  double* rpart = (double*)ws_at(ws, L.rpart);
-  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
-  const int kb = route_plan(T, H, E).kb;
-  if (L.decode && front_fits(T, H, E, k)) {
-    // small batch: top-k, permutation and gather in one block
-    MOE_TRY(launch_front(rpart, kb, x, xdt, b, T, H, E, k, ids, w, counts, offsets, perm, inv,
-                         flags, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
-                         (float*)ws_at(ws, L.ascale), s));
-  } else {
-    MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
-    MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags,
-                           ws_at(ws, L.pscratch), s));
-    st = run_gather(x, xdt, perm, T, H, k, aq, L, ws, s);
-    if (st != MOE_OK) return st;
-  }
-  st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, s);
-  if (st != MOE_OK) return st;
-  st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, yp, s);
-  if (st != MOE_OK) return st;
-  return hip_status(launch_combine(yp, L.decode ? L.splits : 1, w, inv, T, H, k, out, out_dt, s));
+  return layer_forward_ws(x, xdt, Wr, b, experts, fmt_mask, T, H, I, E, k, aq, out, out_dt,
+                          topk_ids, topk_w, ws, L, nullptr, (hipStream_t)stream);
 }
 
 moe_status moe_act_quant_i8(const void* v, moe_dtype dt, int rows, int cols, int8_t* q, float* s,

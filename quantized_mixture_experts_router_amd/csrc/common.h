@@ -255,4 +255,14 @@ hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, ui
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,
                               void* params, hipStream_t s);
 
+// The whole layer on a validated workspace (api.hip); flags: where the flag
+// word goes (nullptr: the workspace's own). check_layer_sizes validates the
+// sizes and gives the workspace layout.
+moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const float* b,
+                            const moe_packed_expert* experts, uint32_t fmt_mask, int T, int H,
+                            int I, int E, int k, moe_actq aq, void* out, moe_dtype out_dt,
+                            int32_t* topk_ids, float* topk_w, void* ws, const WsLayout& L,
+                            uint32_t* flags, hipStream_t s);
+moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, WsLayout& L);
+
 }  // namespace moeq
