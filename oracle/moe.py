@@ -13,8 +13,12 @@ Sources (pages as titled; sections as numbered on each page):
               and the expert inputs are quantised per token dynamically to
               int8 (W8A8).
   [PerExpert] "AlphaQ" blog, section 4.2: per-expert, per-layer
-              {bit_width, group_size}; expert-aware quantisation digest:
-              hot experts at 4-bit, cold experts at 2-bit.
+              {bit_width, group_size}, and section 2.2: per-matrix bit
+              widths within an expert (a 3-bit gate, 2-bit middle, 4-bit
+              output mix); expert-aware quantisation digest: hot experts at
+              4-bit, cold experts at 2-bit, ever coarser tiers for colder ones.
+  [Outliers]  MoE mixed-precision field notes, section 4.2: isolate the
+              largest weights (about 0.05%) in fp16 and quantise the rest.
   [FFN]       "AlphaQ" blog, section 2.2 and the mixed-precision notes,
               section 3.3: each expert is a three-matrix FFN (gate, up/middle,
               down/output); its gated form is SwiGLU.
@@ -56,15 +60,25 @@ E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64
 # Weight blocks [PerExpert]
 # --------------------------------------------------------------------------
 def _unpack_codes(codes: np.ndarray, bits: int, cols: int) -> np.ndarray:
-    """uint8 [rows, row_bytes] -> uint8 [rows, cols]. 4-bit: element 2i is the
-    low nibble of byte i. 2-bit: element 4i+j is bits [2j, 2j+1] of byte i.
-    1-bit: element 8i+j is bit j of byte i."""
+    """uint8 [rows, row_bytes] -> uint8 [rows, cols]. The codes of a row form
+    one little-endian bit stream: element e occupies bits [b*e, b*e + b), bit
+    i of the stream being bit i % 8 of byte i // 8. So 4-bit: element 2i is
+    the low nibble of byte i; 2-bit: element 4i+j is bits [2j, 2j+1] of byte
+    i; 1-bit: element 8i+j is bit j of byte i; 3-bit: elements 8i..8i+7 fill
+    the 24 bits of bytes 3i..3i+2 (byte 3i lowest), element 8i+j at bits
+    [3j, 3j+2] of that 24-bit word."""
     codes = np.asarray(codes, dtype=np.uint8)
-    per_byte = 8 // bits
-    nbytes = cols // per_byte
-    b = codes[:, :nbytes]
+    rows = codes.shape[0]
     mask = (1 << bits) - 1
-    out = np.empty((codes.shape[0], cols), dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.uint8)
+    if bits == 3:
+        b = codes[:, :cols * 3 // 8].astype(np.uint32).reshape(rows, cols // 8, 3)
+        word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+        for j in range(8):
+            out[:, j::8] = (word >> (3 * j)) & mask
+        return out
+    per_byte = 8 // bits
+    b = codes[:, :cols // per_byte]
     for j in range(per_byte):
         out[:, j::per_byte] = (b >> (bits * j)) & mask
     return out
@@ -74,11 +88,14 @@ def decode_qmat(qm) -> np.ndarray:
     """Decode one canonical block matrix to fp32 [rows, cols].
 
     Asymmetric (fmt 1): w = round_fp32(s*q + m) with fp16 s, m and unsigned
-    b-bit q. The exact value s*q + m is formed in fp64 (both terms are exact
-    there) and rounded once to fp32.
+    b-bit q (b = 1, 2, 3 or 4). The exact value s*q + m is formed in fp64
+    (both terms are exact there) and rounded once to fp32.
     e2m1 (fmt 2): w = round_fp32(v(q) * s), v from the 3 magnitude bits, bit 3
     the sign, fp16 s per group.
     Each group's parameters apply to its `group` consecutive columns.
+    Outliers (MoE mixed-precision field notes, section 4.2: a tiny share of
+    the weights kept in fp16, the rest low-bit): when the matrix carries a
+    side list, each listed element takes its fp16 value instead.
     """
     rows, cols, g = qm.rows, qm.cols, qm.group
     G = cols // g
@@ -94,7 +111,15 @@ def decode_qmat(qm) -> np.ndarray:
         w = (v * s).astype(np.float32)
     else:
         raise ValueError(f"unknown weight format {qm.fmt}")
-    return w.reshape(rows, cols)
+    w = w.reshape(rows, cols)
+    out = getattr(qm, "outliers", None)
+    if out is not None and len(out):
+        # outlier side list: these elements are kept as fp16 values and replace
+        # the block decode at their positions (index = row * cols + col)
+        idx = np.asarray(out[:, 0], dtype=np.int64)
+        val = np.asarray(out[:, 1], dtype=np.uint16).view(np.float16).astype(np.float32)
+        w.reshape(-1)[idx] = val
+    return w
 
 
 # --------------------------------------------------------------------------

@@ -27,11 +27,11 @@ from .formats import (FMT_ASYM, FMT_E2M1, QMat, quantize_asym, quantize_e2m1,
                       random_qmat, row_bytes, f32_to_bf16_bits, bf16_bits_to_f32,
                       E2M1_VALUES)
 from .configs import (LayerConfig, CONFIGS, get_config, gen_router, gen_x,
-                      gen_expert, expert_format, scaled_config)
+                      gen_expert, expert_format, matrix_formats, scaled_config)
 
 __all__ = [
     "FMT_ASYM", "FMT_E2M1", "QMat", "quantize_asym", "quantize_e2m1",
     "random_qmat", "row_bytes", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "E2M1_VALUES", "LayerConfig", "CONFIGS", "get_config", "gen_router",
-    "gen_x", "gen_expert", "expert_format", "scaled_config",
+    "gen_x", "gen_expert", "expert_format", "matrix_formats", "scaled_config",
 ]

@@ -42,6 +42,10 @@ class LayerConfig:
     weight_mode: str = "codes"   # "quantize" (N(0,0.02) then quantise) or "codes"
     seed: int = 0
     decode_T: Tuple[int, ...] = ()
+    # share of each expert matrix kept as an fp16 outlier side list
+    weight_outlier_frac: float = 0.0
+    # per-expert (gate, up, down) formats, overriding the ones above
+    matrix_fmts: Optional[Tuple[Tuple[Tuple[int, int, int], ...], ...]] = None
 
 
 A4G32 = (FMT_ASYM, 4, 32)
@@ -49,6 +53,8 @@ A2G16 = (FMT_ASYM, 2, 16)
 A4G128 = (FMT_ASYM, 4, 128)
 A1G16 = (FMT_ASYM, 1, 16)
 A1G32 = (FMT_ASYM, 1, 32)
+A3G32 = (FMT_ASYM, 3, 32)
+A3G64 = (FMT_ASYM, 3, 64)
 E2M1G16 = (FMT_E2M1, 4, 16)
 
 # Router bias strength for the hot/cold workload: with alpha = 0.375 the 32
@@ -144,20 +150,34 @@ def expert_format(cfg: LayerConfig, e: int) -> Tuple[int, int, int]:
     return cfg.fmt if _bias_ranks(cfg)[e] <= cfg.n_hot else cfg.cold_fmt
 
 
+def matrix_formats(cfg: LayerConfig, e: int):
+    """(gate, up, down) formats of expert e."""
+    if cfg.matrix_fmts is not None:
+        return tuple(cfg.matrix_fmts[e])
+    f = expert_format(cfg, e)
+    return (f, f, f)
+
+
 def gen_expert(cfg: LayerConfig, e: int):
     """Expert e as a dict of canonical QMats: gate [I,H], up [I,H], down [H,I]."""
-    fmt, bits, group = expert_format(cfg, e)
     shapes = {"gate": (cfg.I, cfg.H), "up": (cfg.I, cfg.H), "down": (cfg.H, cfg.I)}
+    fr = cfg.weight_outlier_frac
     out = {}
-    for j, role in enumerate(("gate", "up", "down")):
+    for j, (role, (fmt, bits, group)) in enumerate(zip(("gate", "up", "down"),
+                                                       matrix_formats(cfg, e))):
         rows, cols = shapes[role]
         rng = _rng(cfg, 4, e, j)
         if cfg.weight_mode == "quantize":
             W = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
+            if fr > 0:
+                # heavy tail: a few weights well beyond the Gaussian bulk
+                n = int(np.ceil(fr * rows * cols))
+                pos = rng.choice(rows * cols, size=n, replace=False)
+                W.reshape(-1)[pos] *= np.float32(8.0)
             if fmt == FMT_ASYM:
-                out[role] = quantize_asym(W, bits, group)
+                out[role] = quantize_asym(W, bits, group, fr)
             else:
-                out[role] = quantize_e2m1(W, group)
+                out[role] = quantize_e2m1(W, group, fr)
         else:
-            out[role] = random_qmat(rng, rows, cols, fmt, bits, group)
+            out[role] = random_qmat(rng, rows, cols, fmt, bits, group, outlier_frac=fr)
     return out

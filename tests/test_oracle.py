@@ -26,11 +26,13 @@ def _golden(name):
 def _qmat_from_golden(d):
     codes = np.frombuffer(bytes.fromhex(d["codes_hex"]), dtype=np.uint8).reshape(d["rows"], -1)
     params = np.array(d["params_u16"], dtype=np.uint16).reshape(d["rows"], -1)
-    return QMat(d["fmt"], d["bits"], d["group"], d["rows"], d["cols"], codes, params)
+    out = np.array(d["outliers"], dtype=np.uint32) if "outliers" in d else None
+    return QMat(d["fmt"], d["bits"], d["group"], d["rows"], d["cols"], codes, params, out)
 
 
 # ---------------------------------------------------------------- blocks
-@pytest.mark.parametrize("key", ["asym4_g32", "asym2_g16", "asym1_g16", "e2m1_g16"])
+@pytest.mark.parametrize("key", ["asym4_g32", "asym2_g16", "asym1_g16", "e2m1_g16", "asym3_g16",
+                                 "asym4_g32_outliers"])
 def test_decode_hand_worked_blobs(key):
     d = _golden("blob_examples.json")[key]
     got = oracle.decode_qmat(_qmat_from_golden(d))
@@ -52,7 +54,7 @@ def test_e2m1_code_table():
 
 
 @pytest.mark.parametrize("bits,group", [(4, 16), (4, 32), (4, 64), (4, 128), (2, 16), (2, 32), (2, 128),
-                                        (1, 16), (1, 32), (1, 128)])
+                                        (1, 16), (1, 32), (1, 128), (3, 16), (3, 32), (3, 64), (3, 128)])
 def test_asym_zero_error_roundtrip(bits, group):
     """Weights built exactly representable (s = 2^-j, m = n*2^-j, every group
     using codes 0 and 2^b-1) survive quantise -> decode bit-exactly, and the
@@ -72,6 +74,54 @@ def test_asym_zero_error_roundtrip(bits, group):
     qm2 = synth.quantize_asym(oracle.decode_qmat(qm), bits, group)
     np.testing.assert_array_equal(qm2.codes, qm.codes)
     np.testing.assert_array_equal(qm2.params, qm.params)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (3, 64), (2, 16)])
+def test_outliers_are_excluded_and_exact(bits, group):
+    """Exactly representable groups plus a few planted large values: with the
+    side list holding exactly the planted ones, the groups' min and max come
+    from the rest, so decode reproduces W bit for bit (a quantiser that kept
+    an outlier in its group's range would coarsen that group's step)."""
+    rng = np.random.default_rng(9 + bits)
+    rows, cols = 8, 256
+    qmax = (1 << bits) - 1
+    q = rng.integers(0, qmax + 1, size=(rows, cols // group, group))
+    q[..., 0] = 0
+    q[..., -1] = qmax
+    j = rng.integers(6, 10, size=(rows, cols // group, 1))
+    n = rng.integers(-20, 20, size=(rows, cols // group, 1))
+    s = np.ldexp(1.0, -j)
+    W = (s * q + n * s).reshape(rows, cols).astype(np.float32)
+    planted = np.sort(rng.choice(rows * cols, size=5, replace=False))
+    # planted values are exact in fp16 and beyond every group's range; the
+    # planted positions avoid each group's first and last element
+    planted = np.unique([p + 1 if p % group == 0 else (p - 1 if p % group == group - 1 else p)
+                         for p in planted])
+    W.reshape(-1)[planted] = np.array([96.0, -80.5, 70.25, -64.0, 100.0],
+                                      dtype=np.float32)[:len(planted)]
+    frac = len(planted) / W.size
+    qm = synth.quantize_asym(W, bits, group, outlier_frac=frac)
+    np.testing.assert_array_equal(qm.outliers[:, 0], np.sort(planted))
+    np.testing.assert_array_equal(oracle.decode_qmat(qm), W)
+    # the side list replaces exactly those elements: without it they decode
+    # to a clipped code of their group
+    bare = QMat(qm.fmt, qm.bits, qm.group, qm.rows, qm.cols, qm.codes, qm.params)
+    diff = np.flatnonzero(oracle.decode_qmat(bare).reshape(-1) != W.reshape(-1))
+    np.testing.assert_array_equal(diff, np.sort(planted))
+
+
+def test_e2m1_outliers_excluded_from_absmax():
+    rng = np.random.default_rng(12)
+    rows, cols, group = 4, 64, 16
+    code = rng.integers(0, 16, size=(rows, cols // group, group))
+    code[..., 0] = 7
+    v = oracle.E2M1_TABLE[code & 7] * np.where(code & 8, -1.0, 1.0)
+    W = (v * 0.125).reshape(rows, cols).astype(np.float32)
+    W[1, 5] = 50.0
+    W[3, 60] = -33.0
+    qm = synth.quantize_e2m1(W, group, outlier_frac=2 / W.size)
+    np.testing.assert_array_equal(qm.outliers[:, 0], [1 * cols + 5, 3 * cols + 60])
+    np.testing.assert_array_equal(oracle.decode_qmat(qm), W)
 
 
 @pytest.mark.parametrize("group", [16, 32])
@@ -244,11 +294,17 @@ def _tiny_layer(seed, T, H, I, E, k, formats, x_dtype="f32", bias=None):
     b = (rng.standard_normal(E) * bias).astype(np.float32) if bias else None
     experts = []
     for e in range(E):
-        fmt, bits, group = formats[e % len(formats)]
+        f = formats[e % len(formats)]
+        # one (fmt, bits, group[, outlier fraction]) for all three matrices,
+        # or a (gate, up, down) triple of them
+        per_role = f if isinstance(f[0], tuple) else (f, f, f)
         ex = {}
-        for role, (r, c) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        for (role, (r, c)), rf in zip((("gate", (I, H)), ("up", (I, H)), ("down", (H, I))), per_role):
+            fmt, bits, group = rf[:3]
+            frac = rf[3] if len(rf) > 3 else 0.0
             W = (rng.standard_normal((r, c)) * 0.1).astype(np.float32)
-            ex[role] = synth.quantize_asym(W, bits, group) if fmt == FMT_ASYM else synth.quantize_e2m1(W, group)
+            ex[role] = (synth.quantize_asym(W, bits, group, frac) if fmt == FMT_ASYM
+                        else synth.quantize_e2m1(W, group, frac))
         experts.append(ex)
     return x, Wr, b, experts
 
@@ -261,7 +317,12 @@ def _torch_expert(xt, ex):
 
 
 FORMAT_SETS = [[(FMT_ASYM, 4, 32)], [(FMT_ASYM, 2, 16)], [(FMT_E2M1, 4, 16)],
-               [(FMT_ASYM, 4, 32), (FMT_ASYM, 2, 16)], [(FMT_ASYM, 4, 64), (FMT_E2M1, 4, 32)]]
+               [(FMT_ASYM, 4, 32), (FMT_ASYM, 2, 16)], [(FMT_ASYM, 4, 64), (FMT_E2M1, 4, 32)],
+               [(FMT_ASYM, 3, 32), (FMT_ASYM, 3, 16)],
+               # per-matrix formats: gate 3-bit, up 2-bit, down 4-bit
+               [((FMT_ASYM, 3, 32), (FMT_ASYM, 2, 16), (FMT_ASYM, 4, 32))],
+               # outlier side lists (2% here, so a 64x64 matrix has some)
+               [(FMT_ASYM, 4, 32, 0.02), (FMT_E2M1, 4, 16, 0.02)]]
 
 
 @pytest.mark.parametrize("fmts", FORMAT_SETS)
