@@ -40,7 +40,7 @@ PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA
 PEAK_INT8_TOPS = 5033.2     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["quantized_mixture_experts_router_amd/csrc/gemm.hip",
+KERNEL_SOURCES = ["quantized_mixture_experts_router_amd/csrc/gemm_impl.h",
                   "quantized_mixture_experts_router_amd/csrc/deq.h",
                   "quantized_mixture_experts_router_amd/csrc/common.h"]
 FMT_NAMES = {1: "asym", 2: "e2m1"}

@@ -56,10 +56,11 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Element formats of a weight block.
- * MOE_W_ASYM: w = s*q + m, q unsigned b-bit (b in {1,2,4}), fp16 s and m
+ * MOE_W_ASYM: w = s*q + m, q unsigned b-bit (b in {1,2,3,4}), fp16 s and m
  *             per group; decoded value rounded once to fp32. 1 bit is the
  *             sub-2-bit tier for the coldest experts (expert-aware
- *             quantisation digest, conclusion).
+ *             quantisation digest, conclusion); 3 bits the gate's width in
+ *             the per-matrix mix of the "AlphaQ" blog, section 2.2.
  * MOE_W_E2M1: w = e2m1(q) * s, 4-bit OCP-MX e2m1 element (bit 3 sign, two
  *             exponent bits with bias 1, one mantissa bit: magnitudes
  *             0, .5, 1, 1.5, 2, 3, 4, 6), fp16 s per group (the 4-bit
@@ -97,45 +98,73 @@ enum {
 /* One weight matrix W[rows, cols] in the canonical block format.
  * Groups of `group` consecutive elements along cols (the GEMM's K).
  * codes (device): uint8 [rows, row_bytes], row_bytes = cols*bits/8 rounded
- *   up to a multiple of 16 (padding bytes are ignored). 4-bit: element 2i in
- *   the low nibble of byte i, 2i+1 in the high nibble. 2-bit: element 4i+j in
- *   bits [2j, 2j+1] of byte i. 1-bit: element 8i+j in bit j of byte i.
+ *   up to a multiple of 16 (padding bytes are ignored). A row's codes are one
+ *   little-endian bit stream, element e at bits [b*e, b*e + b), bit i of the
+ *   stream being bit i % 8 of byte i / 8: 4-bit: element 2i in the low nibble
+ *   of byte i, 2i+1 in the high nibble; 2-bit: element 4i+j in bits
+ *   [2j, 2j+1] of byte i; 1-bit: element 8i+j in bit j of byte i; 3-bit:
+ *   elements 8i..8i+7 in the 24-bit little-endian word of bytes 3i..3i+2,
+ *   element 8i+j at bits [3j, 3j+2].
  * params (device): fp16 [rows, cols/group] scales for MOE_W_E2M1, or
  *   [rows, cols/group] (scale, min) pairs for MOE_W_ASYM, row-major.
- * Supported: ASYM with bits 1, 2 or 4 and group 16/32/64/128; E2M1 with bits 4
- * and group 16/32/64/128. rows % 32 == 0; cols % 128 == 0; codes 16-byte
- * aligned, params 4-byte aligned. */
+ * outliers (device, optional; MoE mixed-precision field notes, section 4.2:
+ *   the largest ~0.05% of the weights kept in fp16, the rest low-bit):
+ *   n_outliers records of 8 bytes {uint32 index = row * cols + col; uint16
+ *   fp16 value; uint16 0}, indices strictly ascending. Each listed element
+ *   takes its fp16 value instead of its block decode. n_outliers == 0: none
+ *   (outliers may be NULL).
+ * Supported: ASYM with bits 1, 2, 3 or 4 and group 16/32/64/128; E2M1 with
+ * bits 4 and group 16/32/64/128. rows % 32 == 0; cols % 128 == 0; codes
+ * 16-byte aligned, params 4-byte aligned, outliers 8-byte aligned. */
 typedef struct {
   uint8_t fmt;    /* moe_wfmt */
-  uint8_t bits;   /* 1, 2 or 4 */
+  uint8_t bits;   /* 1, 2, 3 or 4 */
   uint16_t group; /* 16, 32, 64 or 128 */
   uint32_t rows;
   uint32_t cols;
+  uint32_t n_outliers;
   const void* codes;
   const void* params;
+  const void* outliers;
 } moe_qmat;
 
-/* One expert: gate [I,H], up [I,H] (same format), down [H,I]. */
+/* One expert: gate [I,H], up [I,H], down [H,I], each with its own format
+ * (the per-expert, per-matrix bit widths of the "AlphaQ" blog, sections 2.2
+ * and 4.2). */
 typedef struct {
   moe_qmat gate, up, down;
 } moe_expert_canon;
 
+/* Layout bit of a packed expert: gate and up are separate streams (their
+ * formats differ); otherwise their 32-row tiles are interleaved in one. */
+#define MOE_PACK_SPLIT_GU 1u
+
 /* Device-layout descriptor of one packed expert, filled by moe_pack_expert.
  * The pointed-to layout is private to the library (32-row by 64- or 128-
- * column tiles in matrix-core fragment order, gate and up tiles interleaved).
- * An array of E of these, copied to device memory by the caller, is what the
- * FFN entry points take. 64 bytes. */
+ * column tiles in matrix-core fragment order; gate and up tiles interleaved
+ * when they share a format). An array of E of these, copied to device memory
+ * by the caller, is what the FFN entry points take. 128 bytes. */
 typedef struct {
-  uint8_t gu_fmt, gu_bits;
+  uint8_t gu_fmt, gu_bits; /* gate's format (and up's when interleaved) */
   uint16_t gu_group;
   uint8_t dn_fmt, dn_bits;
   uint16_t dn_group;
   uint32_t H, I;
-  uint32_t reserved0, reserved1, reserved2, reserved3;
-  const void* gu_codes;
+  uint8_t up_fmt, up_bits; /* up's format */
+  uint16_t up_group;
+  uint32_t layout;                 /* MOE_PACK_SPLIT_GU or 0 */
+  uint32_t n_out_gu, n_out_dn;     /* outliers of gate + up, of down */
+  const void* gu_codes;            /* gate (+ up interleaved) */
   const void* gu_params;
   const void* dn_codes;
   const void* dn_params;
+  const void* up_codes;            /* split layout only */
+  const void* up_params;
+  const void* out_gu_rowptr;       /* outlier lists (n_out_* > 0 only) */
+  const void* out_gu_entries;
+  const void* out_dn_rowptr;
+  const void* out_dn_entries;
+  uint64_t reserved[2];
 } moe_packed_expert;
 
 /* Bytes of device memory moe_pack_expert needs for this expert (0 if the
@@ -145,20 +174,27 @@ size_t moe_packed_expert_bytes(const moe_expert_canon* src);
 /* Repack one expert from the canonical format (device planes named in *src)
  * into the device layout at dst_dev (256-byte aligned, dst_bytes >=
  * moe_packed_expert_bytes(src)). Fills *out_desc (host). Enqueues the repack
- * on `stream`; the canonical planes must stay valid until it has run.
+ * on `stream`; the canonical planes and outlier lists must stay valid until
+ * it has run. Gate and up are interleaved when their formats agree, else
+ * stored as separate streams (MOE_PACK_SPLIT_GU). Outliers become per-row
+ * lists of (column, fp32 difference between the fp16 outlier and the fp16
+ * value the kernels decode there), added in the GEMM epilogues.
  * I * H <= 2^31 (else MOE_ERR_UNSUPPORTED: the kernels address a packed
- * matrix with 32-bit byte offsets). */
+ * matrix with 32-bit byte offsets); n_outliers <= rows * cols. */
 moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t dst_bytes,
                            moe_packed_expert* out_desc, void* stream);
 
 /* Bit mask of the block formats used by E packed experts (host array of the
- * descriptors moe_pack_expert filled): bit i is set when some gate/up or
+ * descriptors moe_pack_expert filled): bit i is set when some gate, up or
  * down matrix has format i, with i = 4*c + g, c = 0 asym 4-bit, 1 asym 2-bit,
- * 2 e2m1, 3 asym 1-bit, and g = 0,1,2,3 for group 16, 32, 64, 128. The FFN entry points
- * take this mask (fmt_mask) and run one kernel per format in it; 0 means
- * every supported format (correct for any expert set, but each absent format
- * still costs a launch). Experts whose format is missing from a non-zero mask
- * are skipped and flag MOE_FLAG_FORMAT_NOT_LAUNCHED. Host only. */
+ * 2 e2m1, 3 asym 1-bit, 4 asym 3-bit, and g = 0,1,2,3 for group 16, 32, 64,
+ * 128; bit 31 (MOE_MASK_SPLIT_GU) is set when some expert has the split
+ * gate/up layout. The FFN entry points take this mask (fmt_mask) and run one
+ * kernel per format (and role) in it; 0 means every supported format
+ * (correct for any expert set, but each absent format still costs launches).
+ * Experts whose format is missing from a non-zero mask are skipped and flag
+ * MOE_FLAG_FORMAT_NOT_LAUNCHED. Host only. */
+#define MOE_MASK_SPLIT_GU (1u << 31)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 
 /* Workspace bytes the layer entry points need for these sizes. Host only. */

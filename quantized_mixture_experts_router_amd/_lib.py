@@ -32,7 +32,9 @@ class MoeError(RuntimeError):
 class QMatC(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_uint8), ("bits", ctypes.c_uint8), ("group", ctypes.c_uint16),
                 ("rows", ctypes.c_uint32), ("cols", ctypes.c_uint32),
-                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
+                ("n_outliers", ctypes.c_uint32),
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p),
+                ("outliers", ctypes.c_void_p)]
 
 
 class ExpertCanonC(ctypes.Structure):
@@ -43,13 +45,21 @@ class PackedExpertC(ctypes.Structure):
     _fields_ = [("gu_fmt", ctypes.c_uint8), ("gu_bits", ctypes.c_uint8), ("gu_group", ctypes.c_uint16),
                 ("dn_fmt", ctypes.c_uint8), ("dn_bits", ctypes.c_uint8), ("dn_group", ctypes.c_uint16),
                 ("H", ctypes.c_uint32), ("I", ctypes.c_uint32),
-                ("reserved0", ctypes.c_uint32), ("reserved1", ctypes.c_uint32),
-                ("reserved2", ctypes.c_uint32), ("reserved3", ctypes.c_uint32),
+                ("up_fmt", ctypes.c_uint8), ("up_bits", ctypes.c_uint8), ("up_group", ctypes.c_uint16),
+                ("layout", ctypes.c_uint32), ("n_out_gu", ctypes.c_uint32), ("n_out_dn", ctypes.c_uint32),
                 ("gu_codes", ctypes.c_void_p), ("gu_params", ctypes.c_void_p),
-                ("dn_codes", ctypes.c_void_p), ("dn_params", ctypes.c_void_p)]
+                ("dn_codes", ctypes.c_void_p), ("dn_params", ctypes.c_void_p),
+                ("up_codes", ctypes.c_void_p), ("up_params", ctypes.c_void_p),
+                ("out_gu_rowptr", ctypes.c_void_p), ("out_gu_entries", ctypes.c_void_p),
+                ("out_dn_rowptr", ctypes.c_void_p), ("out_dn_entries", ctypes.c_void_p),
+                ("reserved", ctypes.c_uint64 * 2)]
 
 
-assert ctypes.sizeof(PackedExpertC) == 64
+assert ctypes.sizeof(QMatC) == 40
+assert ctypes.sizeof(PackedExpertC) == 128
+DESC_BYTES = 128
+PACK_SPLIT_GU = 1
+MASK_SPLIT_GU = 1 << 31
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
@@ -151,19 +161,27 @@ def read_flags(ws):
 class DeviceQMat:
     """A canonical block matrix whose planes live in device memory."""
 
-    def __init__(self, fmt, bits, group, rows, cols, codes, params):
+    def __init__(self, fmt, bits, group, rows, cols, codes, params, outliers=None):
         self.fmt, self.bits, self.group, self.rows, self.cols = fmt, bits, group, rows, cols
-        self.codes, self.params = codes, params
+        self.codes, self.params, self.outliers = codes, params, outliers
 
     @classmethod
     def from_host(cls, q, device="cuda"):
+        """From a host QMat (codes uint8, params uint16, optional outlier
+        records uint32 [n, 2] of (index, fp16 bits))."""
         codes = torch.from_numpy(np.ascontiguousarray(q.codes)).to(device)
         params = torch.from_numpy(np.ascontiguousarray(q.params).view(np.int16)).to(device)
-        return cls(q.fmt, q.bits, q.group, q.rows, q.cols, codes, params)
+        out = getattr(q, "outliers", None)
+        outliers = None
+        if out is not None and len(out):
+            outliers = torch.from_numpy(np.ascontiguousarray(out, dtype=np.uint32).view(np.int32)).to(device)
+        return cls(q.fmt, q.bits, q.group, q.rows, q.cols, codes, params, outliers)
 
     def c(self):
-        return QMatC(self.fmt, self.bits, self.group, self.rows, self.cols,
-                     self.codes.data_ptr(), self.params.data_ptr())
+        n = 0 if self.outliers is None else int(self.outliers.shape[0])
+        return QMatC(self.fmt, self.bits, self.group, self.rows, self.cols, n,
+                     self.codes.data_ptr(), self.params.data_ptr(),
+                     None if self.outliers is None else self.outliers.data_ptr())
 
 
 class PackedExperts:
@@ -173,9 +191,10 @@ class PackedExperts:
         self.buffers = buffers
         self.descs = descs
         self.H, self.I = H, I
-        raw = bytearray(ctypes.sizeof(PackedExpertC) * len(descs))
+        raw = bytearray(DESC_BYTES * len(descs))
         for i, d in enumerate(descs):
-            ctypes.memmove(ctypes.addressof(ctypes.c_char.from_buffer(raw, i * 64)), ctypes.addressof(d), 64)
+            ctypes.memmove(ctypes.addressof(ctypes.c_char.from_buffer(raw, i * DESC_BYTES)),
+                           ctypes.addressof(d), DESC_BYTES)
         self.dev = torch.frombuffer(raw, dtype=torch.uint8).to(device)
         arr = (PackedExpertC * len(descs))(*descs)
         self.fmt_mask = int(LIB.moe_format_mask(arr, len(descs)))

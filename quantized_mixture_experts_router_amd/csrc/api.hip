@@ -18,6 +18,10 @@ moe_status check_qmat(const moe_qmat& q, uint32_t rows, uint32_t cols) {
   if (fmt_id(q.fmt, q.bits, q.group) < 0) return MOE_ERR_UNSUPPORTED;
   if (rows % 32 != 0 || cols % 128 != 0 || cols % q.group != 0) return MOE_ERR_INVALID_ARG;
   if (!aligned(q.codes, 16) || !aligned(q.params, 4)) return MOE_ERR_ALIGNMENT;
+  if (q.n_outliers > 0) {
+    if (!q.outliers || (uint64_t)q.n_outliers > (uint64_t)rows * cols) return MOE_ERR_INVALID_ARG;
+    if (!aligned(q.outliers, 8)) return MOE_ERR_ALIGNMENT;
+  }
   return MOE_OK;
 }
 
@@ -31,24 +35,38 @@ moe_status check_canon(const moe_expert_canon* src) {
   if ((s = check_qmat(src->gate, I, H)) != MOE_OK) return s;
   if ((s = check_qmat(src->up, I, H)) != MOE_OK) return s;
   if ((s = check_qmat(src->down, H, I)) != MOE_OK) return s;
-  if (src->up.fmt != src->gate.fmt || src->up.bits != src->gate.bits ||
-      src->up.group != src->gate.group)
-    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
+inline bool split_gu(const moe_expert_canon* src) {
+  return src->up.fmt != src->gate.fmt || src->up.bits != src->gate.bits ||
+         src->up.group != src->gate.group;
+}
+
+// byte offsets of the parts of one packed expert (each 256-aligned)
 struct PackedSizes {
-  size_t gu_codes, gu_params, dn_codes, dn_params, total;
+  size_t gu_codes, gu_params, up_codes, up_params, dn_codes, dn_params;
+  size_t gu_rowptr, gu_ent, dn_rowptr, dn_ent, total;
 };
 
 PackedSizes packed_sizes(const moe_expert_canon* src) {
   PackedSizes p;
   const int I = (int)src->gate.rows, H = (int)src->gate.cols;
-  p.gu_codes = align256(packed_codes_bytes(2 * I, H, src->gate.bits));
-  p.gu_params = align256(packed_params_bytes(2 * I, H, src->gate.fmt, src->gate.bits, src->gate.group));
-  p.dn_codes = align256(packed_codes_bytes(H, I, src->down.bits));
-  p.dn_params = align256(packed_params_bytes(H, I, src->down.fmt, src->down.bits, src->down.group));
-  p.total = p.gu_codes + p.gu_params + p.dn_codes + p.dn_params;
+  const bool split = split_gu(src);
+  const moe_qmat &g = src->gate, &u = src->up, &d = src->down;
+  p.gu_codes = align256(packed_codes_bytes(split ? I : 2 * I, H, g.bits));
+  p.gu_params = align256(packed_params_bytes(split ? I : 2 * I, H, g.fmt, g.bits, g.group));
+  p.up_codes = split ? align256(packed_codes_bytes(I, H, u.bits)) : 0;
+  p.up_params = split ? align256(packed_params_bytes(I, H, u.fmt, u.bits, u.group)) : 0;
+  p.dn_codes = align256(packed_codes_bytes(H, I, d.bits));
+  p.dn_params = align256(packed_params_bytes(H, I, d.fmt, d.bits, d.group));
+  const uint64_t ngu = (uint64_t)g.n_outliers + u.n_outliers, ndn = d.n_outliers;
+  p.gu_rowptr = ngu ? align256(outlier_rowptr_bytes(2 * I)) : 0;
+  p.gu_ent = ngu ? align256(ngu * sizeof(OutEntry)) : 0;
+  p.dn_rowptr = ndn ? align256(outlier_rowptr_bytes(H)) : 0;
+  p.dn_ent = ndn ? align256(ndn * sizeof(OutEntry)) : 0;
+  p.total = p.gu_codes + p.gu_params + p.up_codes + p.up_params + p.dn_codes + p.dn_params +
+            p.gu_rowptr + p.gu_ent + p.dn_rowptr + p.dn_ent;
   return p;
 }
 
@@ -80,7 +98,9 @@ moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, 
   return MOE_OK;
 }
 
-inline uint32_t effective_mask(uint32_t m) { return m ? m : ((1u << F_COUNT) - 1u); }
+inline uint32_t effective_mask(uint32_t m) {
+  return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU);
+}
 
 moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
                        int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
@@ -190,7 +210,7 @@ moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, WsL
 
 extern "C" {
 
-int moe_version(void) { return 100; }
+int moe_version(void) { return 20000; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -218,27 +238,58 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
   PackedSizes p = packed_sizes(src);
   if (dst_bytes < p.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  char* base = (char*)dst_dev;
-  void* guc = base;
-  void* gup = base + p.gu_codes;
-  void* dnc = base + p.gu_codes + p.gu_params;
-  void* dnp = base + p.gu_codes + p.gu_params + p.dn_codes;
-  MOE_TRY(launch_pack_matrix(&src->gate, &src->up, guc, gup, s));
+  const bool split = split_gu(src);
+  char* at = (char*)dst_dev;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = bytes ? at : nullptr;
+    at += bytes;
+    return r;
+  };
+  void* guc = take(p.gu_codes);
+  void* gup = take(p.gu_params);
+  void* upc = take(p.up_codes);
+  void* upp = take(p.up_params);
+  void* dnc = take(p.dn_codes);
+  void* dnp = take(p.dn_params);
+  void* gur = take(p.gu_rowptr);
+  void* gue = take(p.gu_ent);
+  void* dnr = take(p.dn_rowptr);
+  void* dne = take(p.dn_ent);
+  if (split) {
+    MOE_TRY(launch_pack_matrix(&src->gate, nullptr, guc, gup, s));
+    MOE_TRY(launch_pack_matrix(&src->up, nullptr, upc, upp, s));
+  } else {
+    MOE_TRY(launch_pack_matrix(&src->gate, &src->up, guc, gup, s));
+  }
   MOE_TRY(launch_pack_matrix(&src->down, nullptr, dnc, dnp, s));
-  moe_packed_expert d;
+  const uint32_t ngu = src->gate.n_outliers + src->up.n_outliers, ndn = src->down.n_outliers;
+  if (ngu) MOE_TRY(launch_pack_outliers(&src->gate, &src->up, (uint32_t*)gur, (OutEntry*)gue, s));
+  if (ndn) MOE_TRY(launch_pack_outliers(&src->down, nullptr, (uint32_t*)dnr, (OutEntry*)dne, s));
+  moe_packed_expert d = {};
   d.gu_fmt = src->gate.fmt;
   d.gu_bits = src->gate.bits;
   d.gu_group = src->gate.group;
+  d.up_fmt = src->up.fmt;
+  d.up_bits = src->up.bits;
+  d.up_group = src->up.group;
   d.dn_fmt = src->down.fmt;
   d.dn_bits = src->down.bits;
   d.dn_group = src->down.group;
   d.H = src->gate.cols;
   d.I = src->gate.rows;
-  d.reserved0 = d.reserved1 = d.reserved2 = d.reserved3 = 0;
+  d.layout = split ? MOE_PACK_SPLIT_GU : 0u;
+  d.n_out_gu = ngu;
+  d.n_out_dn = ndn;
   d.gu_codes = guc;
   d.gu_params = gup;
+  d.up_codes = split ? upc : guc;
+  d.up_params = split ? upp : gup;
   d.dn_codes = dnc;
   d.dn_params = dnp;
+  d.out_gu_rowptr = gur;
+  d.out_gu_entries = gue;
+  d.out_dn_rowptr = dnr;
+  d.out_dn_entries = dne;
   *out_desc = d;
   return MOE_OK;
 }
@@ -247,10 +298,13 @@ uint32_t moe_format_mask(const moe_packed_expert* descs, int E) {
   if (!descs || E <= 0) return 0;
   uint32_t m = 0;
   for (int e = 0; e < E; ++e) {
-    int a = fmt_id(descs[e].gu_fmt, descs[e].gu_bits, descs[e].gu_group);
-    int b = fmt_id(descs[e].dn_fmt, descs[e].dn_bits, descs[e].dn_group);
+    const int a = fmt_id(descs[e].gu_fmt, descs[e].gu_bits, descs[e].gu_group);
+    const int u = fmt_id(descs[e].up_fmt, descs[e].up_bits, descs[e].up_group);
+    const int b = fmt_id(descs[e].dn_fmt, descs[e].dn_bits, descs[e].dn_group);
     if (a >= 0) m |= 1u << a;
+    if (u >= 0) m |= 1u << u;
     if (b >= 0) m |= 1u << b;
+    if (descs[e].layout & MOE_PACK_SPLIT_GU) m |= kMaskSplitGU;
   }
   return m;
 }

@@ -30,8 +30,13 @@ enum FmtId : int {
   F_A2G16, F_A2G32, F_A2G64, F_A2G128,
   F_E4G16, F_E4G32, F_E4G64, F_E4G128,
   F_A1G16, F_A1G32, F_A1G64, F_A1G128,
+  F_A3G16, F_A3G32, F_A3G64, F_A3G128,
   F_COUNT
 };
+// bit of a format mask: some expert stores gate and up as separate streams
+// (their formats differ), so the split gate and up passes run too
+constexpr uint32_t kMaskSplitGU = 1u << 31;
+static_assert(F_COUNT <= 31, "format mask bits");
 
 __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   int g = group == 16 ? 0 : group == 32 ? 1 : group == 64 ? 2 : group == 128 ? 3 : -1;
@@ -40,32 +45,50 @@ __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   if (fmt == MOE_W_ASYM && bits == 2) return F_A2G16 + g;
   if (fmt == MOE_W_E2M1 && bits == 4) return F_E4G16 + g;
   if (fmt == MOE_W_ASYM && bits == 1) return F_A1G16 + g;
+  if (fmt == MOE_W_ASYM && bits == 3) return F_A3G16 + g;
   return -1;
 }
 
+// Roles of a grouped GEMM launch. R_GU: gate and up row tiles interleaved in
+// one stream, SwiGLU in the epilogue (an expert whose gate and up share a
+// format). R_DN: the down projection. R_GATE / R_UP: gate and up as separate
+// streams of their own formats (an expert whose gate and up formats differ):
+// the gate pass leaves g in h's buffer, the up pass turns it into
+// h = silu(g) * u in place. A wavefront owns a gate/up row-tile pair (R_GU)
+// or two consecutive row tiles of one matrix (the other roles).
+enum Role : int { R_GU = 0, R_DN = 1, R_GATE = 2, R_UP = 3 };
+
 // Device layout of one packed matrix W[N, K] (N rows = GEMM output columns).
 //  - 32-row tiles; one tile spans KT = 2*SPAN columns; lane l = (n = l % 32,
-//    kh = l / 32) holds CB bytes = SPAN codes of row n, columns
-//    [kt*KT + kh*SPAN, +SPAN). 4- and 2-bit: CB = 16 (SPAN = 32, 64), a tile
-//    is 1 KiB. 1-bit: CB = 8 (SPAN = 64, KT = 128 like 2-bit, so the prefill
-//    token tile keeps its size), a tile is 512 B.
+//    kh = l / 32) holds SPAN codes of row n, columns [kt*KT + kh*SPAN, +SPAN).
+//    4- and 2-bit: 16 bytes per lane (SPAN = 32, 64), a tile is 1 KiB.
+//    1-bit: 8 bytes (SPAN = 64, KT = 128 like 2-bit, so the prefill token tile
+//    keeps its size), 512 B. 3-bit: two planes, the low two bits of each code
+//    laid out as a 2-bit tile (16 bytes per lane at 16 l) followed by the high
+//    bit laid out as a 1-bit tile (8 bytes per lane at 1024 + 8 l): 1536 B.
 //  - Inside each 32-bit word the codes are ordered so that (word >> b*i) &
 //    mask yields the pair (code 2i, code 2i+1) in the two 16-bit halves.
-//  - Tiles are stored row-tile major, then K-tile; gate/up are interleaved
-//    as row tiles (2j = gate rows 32j.., 2j+1 = up rows 32j..).
+//  - Tiles are stored row-tile major, then K-tile; interleaved gate/up have
+//    row tiles 2j = gate rows 32j.., 2j+1 = up rows 32j...
 //  - Params: one "entry" per (row, GE columns) with GE = max(group, SPAN),
 //    holding max(1, SPAN/group) params (ASYM: fp16 (s, m) = 4 B each; E2M1:
 //    fp16 s = 2 B each). Stored [row tile][entry][32 rows][EB bytes].
+struct Codes3 {
+  u32x4 lo;  // low two bits of the lane's 64 codes (2-bit layout)
+  u32x2 hi;  // their high bit (1-bit layout)
+};
 template <int FMT, int BITS, int GROUP>
 struct Fmt {
   static constexpr int ID = fmt_id(FMT, BITS, GROUP);
   static constexpr int kFmt = FMT;
   static constexpr int kBits = BITS;
   static constexpr int kGroup = GROUP;
-  static constexpr int SPAN = BITS == 1 ? 64 : 128 / BITS;  // codes per lane per tile
-  static constexpr int CB = SPAN * BITS / 8;                // code bytes per lane per tile
-  static constexpr int TB = 64 * CB;                        // code bytes per tile
-  using CodeT = typename std::conditional<CB == 16, u32x4, u32x2>::type;
+  static constexpr int SPAN = (BITS == 1 || BITS == 3) ? 64 : 128 / BITS;  // codes per lane
+  static constexpr int CB = BITS == 1 ? 8 : 16;           // bytes per lane, first plane
+  static constexpr int TB = BITS == 1 ? 512 : (BITS == 3 ? 1536 : 1024);  // bytes per tile
+  static constexpr int HOFF = 1024;                       // 3-bit: the high plane
+  using CodeT = typename std::conditional<
+      BITS == 3, Codes3, typename std::conditional<CB == 16, u32x4, u32x2>::type>::type;
   static constexpr int KT = 2 * SPAN;                      // K columns per tile
   static constexpr int STEPS = SPAN / 8;                   // 32x32x16 MFMA steps per tile
   static constexpr int GE = GROUP > SPAN ? GROUP : SPAN;   // K columns per param entry
@@ -74,12 +97,14 @@ struct Fmt {
   static constexpr int EB = NP * PSZ;                      // entry bytes
 };
 
-__host__ __device__ inline int fmt_span(int bits) { return bits == 1 ? 64 : 128 / bits; }
+__host__ __device__ inline int fmt_span(int bits) { return (bits == 1 || bits == 3) ? 64 : 128 / bits; }
 __host__ __device__ inline int fmt_kt(int bits) { return 2 * fmt_span(bits); }
-__host__ __device__ inline int fmt_cb(int bits) { return fmt_span(bits) * bits / 8; }
+__host__ __device__ inline int fmt_tile_bytes(int bits) {
+  return bits == 1 ? 512 : (bits == 3 ? 1536 : 1024);
+}
 
 inline size_t packed_codes_bytes(int N, int K, int bits) {
-  return (size_t)(N / 32) * (size_t)(K / fmt_kt(bits)) * 64 * fmt_cb(bits);
+  return (size_t)(N / 32) * (size_t)(K / fmt_kt(bits)) * fmt_tile_bytes(bits);
 }
 inline size_t packed_params_bytes(int N, int K, int fmt, int bits, int group) {
   int span = fmt_span(bits);
@@ -88,6 +113,17 @@ inline size_t packed_params_bytes(int N, int K, int fmt, int bits, int group) {
   int eb = np * (fmt == MOE_W_ASYM ? 4 : 2);
   return (size_t)(N / 32) * (size_t)(K / ge) * 32 * eb;
 }
+// Outlier side lists, per packed matrix group (gate/up: rows 0..I-1 gate,
+// I..2I-1 up; down: rows 0..H-1): rowptr [rows + 1] uint32, then entries
+// {uint32 k, float delta} by row, delta = the fp16 outlier value minus the
+// fp16 value the kernels decode from the block at (row, k).
+struct OutEntry {
+  uint32_t k;
+  float delta;
+};
+inline size_t outlier_rowptr_bytes(int rows) { return (size_t)(rows + 1) * 4; }
+static_assert(sizeof(moe_packed_expert) == 128, "descriptor size");
+static_assert(sizeof(moe_qmat) == 40, "canonical matrix size");
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
@@ -254,6 +290,10 @@ hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, ui
                               hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,
                               void* params, hipStream_t s);
+// outlier side lists of a (and, when b is given, of b as rows a.rows..) into
+// rowptr [rows(+b.rows) + 1] and entries (OutEntry, n_a + n_b)
+hipError_t launch_pack_outliers(const moe_qmat* a, const moe_qmat* b_or_null, uint32_t* rowptr,
+                                OutEntry* entries, hipStream_t s);
 
 // The whole layer on a validated workspace (api.hip); flags: where the flag
 // word goes (nullptr: the workspace's own). check_layer_sizes validates the

@@ -2,11 +2,13 @@
 //
 // Asymmetric blocks (w = s*q + m; AWQ-style zero point of the "sparse
 // activation" page, section 4.4; the per-expert bit widths of the AlphaQ blog,
-// section 4.2; 1-bit for the coldest experts, the sub-2-bit tier of the
-// expert-aware quantisation digest's conclusion): a pair of b-bit codes is
+// sections 2.2 and 4.2; 1-bit for the coldest experts, the sub-2-bit tier of
+// the expert-aware quantisation digest's conclusion): a pair of b-bit codes is
 // OR-ed into the mantissas of two fp16 numbers (exact), the fp16 offset is
 // subtracted (exact), and one packed fp16 fma applies the group scale and
-// minimum (one rounding to fp16).
+// minimum (one rounding to fp16). 3-bit codes come as a 2-bit plane and a
+// 1-bit plane: each gives an exact fp16 pair, and q = q2 + 4 q1 is formed
+// exactly before the same fma.
 // e2m1 blocks (the 4-bit floating-point weights of the quantized-MoE
 // article): the gfx950 fp4 converter yields the exact fp16 value of each code,
 // then one fp16 multiply by the group scale (one rounding).
@@ -54,6 +56,23 @@ __device__ inline T bload(rsrc_t r, uint32_t voff, uint32_t soff) {
   }
 }
 
+// One lane's codes of a tile: one load, or two for the 3-bit planes (v: the
+// lane's offset in the first plane, vh: in the high-bit plane).
+template <class F, int AUX = 0>
+__device__ inline typename F::CodeT load_codes(rsrc_t r, uint32_t v, uint32_t vh, uint32_t soff) {
+  if constexpr (F::kBits == 3) {
+    Codes3 c;
+    c.lo = bload<u32x4, AUX>(r, v, soff);
+    c.hi = bload<u32x2, AUX>(r, vh, soff);
+    return c;
+  } else {
+    return bload<typename F::CodeT, AUX>(r, v, soff);
+  }
+}
+// loads a load_codes call issues
+template <class F>
+constexpr int code_loads() { return F::kBits == 3 ? 2 : 1; }
+
 // Block parameters of one lane's codes (EB bytes: fp16 scale, or scale and
 // minimum, for one or two groups), zero-extended into 32-bit words.
 template <int EB>
@@ -95,25 +114,41 @@ __device__ inline uint32_t opaque(uint32_t v) {
 // of an fp16 number whose last mantissa bit weighs 2^-o, i.e. 2^(10-o), gives
 // exactly 2^(10-o) + q; subtracting 2^(10-o) leaves q.
 struct DeqConsts {
-  uint32_t mask[4];   // field masks for offsets 0, b, 2b, 3b (b = bits), both halves
-  uint32_t magic[4];  // fp16 pairs 2^(10 - offset)
+  uint32_t mask[4];    // field masks for offsets 0, b, 2b, 3b (b = bits), both halves
+  uint32_t magic[4];   // fp16 pairs 2^(10 - offset)
+  uint32_t mask_h[4];  // 3-bit: the high-bit plane's fields at offsets 0..3
+  uint32_t magic_h[4]; // 3-bit: fp16 pairs 2^(12 - offset), so a set bit adds 4
 };
 
 template <class F>
 __device__ inline DeqConsts make_deq_consts() {
   DeqConsts k;
-  const uint32_t fm = (1u << F::kBits) - 1u;
+  // 3-bit codes decode their low two bits as a 2-bit plane
+  constexpr int B = F::kBits == 3 ? 2 : F::kBits;
+  const uint32_t fm = (1u << B) - 1u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int off = F::kBits * j;
-    const bool used = F::kFmt == MOE_W_ASYM && (F::kBits <= 2 || j < 2);
+    const int off = B * j;
+    const bool used = F::kFmt == MOE_W_ASYM && (B <= 2 || j < 2);
     const uint32_t mk = ((fm << off) | (fm << (16 + off)));
     const uint32_t e = 25u - off;  // fp16 exponent field of 2^(10 - off)
     const uint32_t mg = (e << 10) | (e << 26);
     k.mask[j] = used ? opaque(mk) : 0u;
     k.magic[j] = used ? opaque(mg) : 0u;
+    // high bit of a 3-bit code at offset j of its plane: 2^(12 - j) + 4 q1
+    const uint32_t eh = 27u - j;
+    k.mask_h[j] = F::kBits == 3 ? opaque((1u << j) | (1u << (16 + j))) : 0u;
+    k.magic_h[j] = F::kBits == 3 ? opaque((eh << 10) | (eh << 26)) : 0u;
   }
   return k;
+}
+
+// -(2^(12 - j) + 2^(10 - 2j)) in both halves (exact in fp16: at most six
+// significant bits): subtracting it from the high-bit pair and adding the
+// low-two-bit pair leaves q = q2 + 4 q1 exactly
+__device__ inline f16x2 magic3_sub(int j) {
+  const f16 c = (f16)(-(float)((1 << (12 - j)) + (1 << (10 - 2 * j))));
+  return f16x2{c, c};
 }
 
 __device__ inline f16x2 magic_sub(int off) {
@@ -130,11 +165,11 @@ __device__ inline f16x8 dequant_step(const typename F::CodeT& c, const PBuf<F::E
   // parameter index inside the entry for lane-local codes [8s, 8s+8)
   const int p = F::kGroup < F::SPAN ? (8 * s) / F::kGroup : 0;
   f16x2 out[4];
-  if (F::kFmt == MOE_W_ASYM) {
+  if constexpr (F::kFmt == MOE_W_ASYM) {
     const uint32_t sm = pb.w[p];
     const f16x2 s2 = as_f16x2((sm & 0xffffu) * 0x10001u);
     const f16x2 m2 = as_f16x2((sm >> 16) * 0x10001u);
-    if (F::kBits == 4) {
+    if constexpr (F::kBits == 4) {
       // word s: pairs at offsets 0, 4 (low byte) and 0, 4 after >> 8
       const uint32_t d = c[s];
       const uint32_t e = d >> 8;
@@ -144,6 +179,19 @@ __device__ inline f16x8 dequant_step(const typename F::CodeT& c, const PBuf<F::E
         const int j = i & 1;
         const uint32_t t = (src & k.mask[j]) | k.magic[j];
         out[i] = __builtin_elementwise_fma(as_f16x2(t) + magic_sub(4 * j), s2, m2);
+      }
+    } else if constexpr (F::kBits == 3) {
+      // low two bits as in the 2-bit layout (word s/2, byte s & 1), the high
+      // bit as in the 1-bit layout (word s/4, bits 4(s & 3)..)
+      const uint32_t d = c.lo[s >> 1];
+      const uint32_t lo = (s & 1) ? d >> 8 : d;
+      const uint32_t hi = c.hi[s >> 2] >> (4 * (s & 3));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t tl = (lo & k.mask[j]) | k.magic[j];
+        const uint32_t th = (hi & k.mask_h[j]) | k.magic_h[j];
+        const f16x2 q = (as_f16x2(th) + magic3_sub(j)) + as_f16x2(tl);
+        out[j] = __builtin_elementwise_fma(q, s2, m2);
       }
     } else if (F::kBits == 1) {
       // word s/4 holds four steps; step s uses bits 4q..4q+3 of each 16-bit

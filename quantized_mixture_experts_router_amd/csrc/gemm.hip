@@ -1,1058 +1,41 @@
-// Grouped expert GEMMs: gate/up + SwiGLU and the down projection, on weights
-// decoded in registers from packed 4-/2-bit blocks.
-//
-// Expert FFN: three matrices per expert, gate/up/down ("AlphaQ" blog,
-// section 2.2; MoE mixed-precision notes, section 3.3), in the gated SwiGLU
-// form h = silu(a Wg^T) * (a Wu^T), y = h Wd^T. SwiGLU is fused into the
-// gate/up epilogue (the notes fuse the expert activation into the linear,
-// section 3.6). Only the experts a token was routed to are read ("Sparse
-// activation ... 2% activation", section 3.1: the saving is in bandwidth).
-//
-// Two kernel families share the tile layout and the in-register decoding:
-//  * decode (few rows per expert): a block is 4 wavefronts on the same 32-row
-//    token tile; they form 4/ksw row groups (64 weight rows each) whose ksw
-//    wavefronts split the K tiles, ksw chosen from K so every wavefront
-//    streams at least 16 tiles. Weights stream from HBM straight into
-//    registers (non-temporal 16-byte loads per lane, 1 KiB per wave and
-//    tile, two tiles ahead), are decoded to fp16 and fed to
-//    v_mfma_f32_32x32x16_f16 with the token rows padded to 32; partial sums
-//    meet in LDS. The down projection also splits K across blocks.
-//  * prefill (many rows per expert): a block owns 128 token rows and 4 x 64
-//    weight rows; the token tile reaches LDS by DMA (buffer loads with an
-//    LDS destination, rows swizzled for the 64-bank LDS, three buffers for
-//    4-bit tiles) and is shared by the 4 wavefronts, each of which streams
-//    its own weight rows into registers (buffer loads: scalar base and tile
-//    offset, so no vector address arithmetic) and decodes step s+1 while the
-//    MFMAs of step s run; two
-//    blocks share a CU so one block's decode overlaps the other's MFMAs. The
-//    pipeline is specialised on the number of 32-row sub-tiles holding rows,
-//    so a partial last m-tile costs only its own MFMAs, and each XCD runs
-//    its full m-tiles before its partial ones (longest first).
-// Every kernel is instantiated per block format; a launch handles the experts
-// of its format. Tasks are (expert, n-tile, m-tile), expert-major, so blocks
-// that share weight tiles run together; each block derives its task from the
-// segment offsets, so no host synchronisation is needed.
+// Dispatch of the grouped expert GEMMs: one launch per block format present
+// in the call's mask and per role (fused gate/up + SwiGLU for experts whose
+// gate and up share a format; split gate then up for the others; down).
+// The kernels live in gemm_impl.h, instantiated per format family.
 #include "common.h"
-#include "deq.h"
+#include "gemm_impl.h"
 
 namespace moeq {
 
+hipError_t launch_ffn_a4(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+hipError_t launch_ffn_a2(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+hipError_t launch_ffn_e4(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+hipError_t launch_ffn_a1(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+hipError_t launch_ffn_a3(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+
+hipError_t launch_ffn_fmt(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s) {
+  switch (fid / 4) {
+    case 0: return launch_ffn_a4(fid, role, a, decode, s);
+    case 1: return launch_ffn_a2(fid, role, a, decode, s);
+    case 2: return launch_ffn_e4(fid, role, a, decode, s);
+    case 3: return launch_ffn_a1(fid, role, a, decode, s);
+    case 4: return launch_ffn_a3(fid, role, a, decode, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 namespace {
 
-constexpr int kThreads = 256;
-
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
-template <int FID>
-struct FmtOf;
-template <> struct FmtOf<F_A4G16> { using T = Fmt<MOE_W_ASYM, 4, 16>; };
-template <> struct FmtOf<F_A4G32> { using T = Fmt<MOE_W_ASYM, 4, 32>; };
-template <> struct FmtOf<F_A4G64> { using T = Fmt<MOE_W_ASYM, 4, 64>; };
-template <> struct FmtOf<F_A4G128> { using T = Fmt<MOE_W_ASYM, 4, 128>; };
-template <> struct FmtOf<F_A2G16> { using T = Fmt<MOE_W_ASYM, 2, 16>; };
-template <> struct FmtOf<F_A2G32> { using T = Fmt<MOE_W_ASYM, 2, 32>; };
-template <> struct FmtOf<F_A2G64> { using T = Fmt<MOE_W_ASYM, 2, 64>; };
-template <> struct FmtOf<F_A2G128> { using T = Fmt<MOE_W_ASYM, 2, 128>; };
-template <> struct FmtOf<F_E4G16> { using T = Fmt<MOE_W_E2M1, 4, 16>; };
-template <> struct FmtOf<F_E4G32> { using T = Fmt<MOE_W_E2M1, 4, 32>; };
-template <> struct FmtOf<F_E4G64> { using T = Fmt<MOE_W_E2M1, 4, 64>; };
-template <> struct FmtOf<F_E4G128> { using T = Fmt<MOE_W_E2M1, 4, 128>; };
-template <> struct FmtOf<F_A1G16> { using T = Fmt<MOE_W_ASYM, 1, 16>; };
-template <> struct FmtOf<F_A1G32> { using T = Fmt<MOE_W_ASYM, 1, 32>; };
-template <> struct FmtOf<F_A1G64> { using T = Fmt<MOE_W_ASYM, 1, 64>; };
-template <> struct FmtOf<F_A1G128> { using T = Fmt<MOE_W_ASYM, 1, 128>; };
-
-__device__ inline f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// SiLU(g) * u; the reciprocal is the hardware one (~1 ulp in fp32), far
-// below the fp16 rounding of h that follows
-__device__ inline float silu_mul(float g, float u) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-}
-
-// Row of accumulator register r for lane `lane` in a 32x32 MFMA output tile.
-__device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-struct FfnArgs {
-  const moe_packed_expert* experts;
-  const int32_t* offsets;
-  uint32_t* flags;
-  uint32_t fmt_mask;
-  int E;
-  int K;          // reduction dim (H for gate/up, I for down)
-  int N;          // outputs per expert (I for gate/up, H for down)
-  const f16* a;   // [R, K] rows in sorted order
-  const float* ascale;  // per-row scale (int8 inputs) or null
-  void* out;      // gate/up: h [R, N] (f16 or f32); down: [splits][R][N] f32
-  int out_f32;
-  int R;
-  int splits;
-  int lpt;        // prefill task order: expert-major (0), longest first in 2 (1) or 4 (2) classes
-};
-
-struct Task {
-  int e, row0, mcount, nt;
-};
-
-// Rows and format of expert e as every task lookup sees them. The caller's
-// segment [offsets[e], offsets[e+1]) is clamped to [0, R) (bit
-// MOE_FLAG_BAD_SEGMENT in *bad when that changes it), so no row outside the
-// expert inputs, h or Y is ever addressed; an expert whose descriptor has
-// another H or I than the call gets no rows (MOE_FLAG_EXPERT_SHAPE), so its
-// packed matrices are never read with the call's sizes; an expert with rows
-// whose format is not in the launch mask is reported
-// (MOE_FLAG_FORMAT_NOT_LAUNCHED). Returns the format id of the expert's
-// gate/up (GU) or down matrices.
-template <bool GU>
-__device__ inline int expert_rows(const FfnArgs& a, int e, int& row0, int& count, uint32_t& bad) {
-  // fmt words, H and I: the descriptor's first 16 bytes
-  const u32x4 d = *reinterpret_cast<const u32x4*>(a.experts + e);
-  const int o0 = a.offsets[e], o1 = a.offsets[e + 1];
-  const int lo = min(max(o0, 0), a.R);
-  const int hi = min(max(o1, lo), a.R);
-  if (lo != o0 || hi != o1) bad |= MOE_FLAG_BAD_SEGMENT;
-  int c = hi - lo;
-  const uint32_t w = GU ? d[0] : d[1];
-  const int f = fmt_id(w & 0xff, (w >> 8) & 0xff, w >> 16);
-  if (c > 0 && (d[2] != (uint32_t)(GU ? a.K : a.N) || d[3] != (uint32_t)(GU ? a.N : a.K))) {
-    bad |= MOE_FLAG_EXPERT_SHAPE;
-    c = 0;
-  }
-  if (c > 0 && (f < 0 || !((a.fmt_mask >> f) & 1u))) bad |= MOE_FLAG_FORMAT_NOT_LAUNCHED;
-  row0 = lo;
-  count = c;
-  return f;
-}
-
-// Task lookup over the experts of format `fid` (decode): tasks of expert e
-// = ceil(count_e / BM) * NB, expert-major, then n-tile, then m-tile.
-// The first block also flags experts with rows whose format is not in the
-// launch mask (their rows would otherwise be left uncomputed).
-template <bool GU>
-__device__ bool find_task(const FfnArgs& a, int fid, int BM, int NB, int L, Task& task) {
-  __shared__ int s_wsum[16];  // up to 1024 threads
-  __shared__ int s_res[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_res[0] = -1;
-  int cnt[2], ntk[2], r0[2];
-  int local = 0;
-  uint32_t bad = 0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * tid + q;
-    int c = 0, f = -1, lo = 0;
-    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
-    cnt[q] = c;
-    r0[q] = lo;
-    ntk[q] = f == fid ? ((c + BM - 1) / BM) * NB : 0;
-    local += ntk[q];
-  }
-  if (bad && blockIdx.x == 0 && blockIdx.y == 0 && a.flags) atomicOr(a.flags, bad);
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  int start = incl - local;
-  for (int w = 0; w < wave; ++w) start += s_wsum[w];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (L >= start && L < start + ntk[q]) {
-      const int e = 2 * tid + q;
-      const int rel = L - start;
-      const int mt = (cnt[q] + BM - 1) / BM;
-      const int mi = rel % mt;
-      s_res[0] = e;
-      s_res[1] = r0[q] + mi * BM;
-      s_res[2] = min(BM, cnt[q] - mi * BM);
-      s_res[3] = rel / mt;
-    }
-    start += ntk[q];
-  }
-  __syncthreads();
-  // block-uniform: held in scalar registers, so what derives from them
-  // (weight addresses, buffer descriptors) is computed on the scalar unit
-  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
-  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
-  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
-  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
-  return task.e >= 0;
-}
-
-// Task lookup of the prefill kernel for block b. Tasks are full m-tiles
-// (count_e / BM per expert and n-tile) and partial last m-tiles (one per
-// expert and n-tile when count_e is not a multiple of BM). Blocks are dealt
-// round-robin to the 8 XCDs, and XCD x runs, in slot order, an equal
-// contiguous share of the tasks that exist (not of the grid, which is an
-// upper bound), in one of two orders:
-//  - expert-major (a.lpt == 0): expert, then n-tile, then m-tile, so the
-//    m-tiles sharing a weight tile run together and find it in L2;
-//  - longest first (a.lpt == 1): a share of all full m-tiles, then a share
-//    of the partial ones, so short blocks fill the tail of a launch that has
-//    few blocks per slot.
-// The grid needs 16 blocks more than there are tasks (spare blocks find
-// nothing and exit).
-template <bool GU>
-__device__ bool find_task_lpt(const FfnArgs& a, int fid, int BM, int NB, int b, Task& task) {
-  __shared__ int s_wsum[2][16];  // up to 1024 threads
-  __shared__ int s_res[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
-  if (tid == 0) s_res[0] = -1;
-  int cnt[2], nfu[2], npa[2], r0[2];
-  int lf = 0, lp = 0;
-  uint32_t bad = 0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * tid + q;
-    int c = 0, f = -1, lo = 0;
-    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
-    cnt[q] = c;
-    r0[q] = lo;
-    nfu[q] = f == fid ? (c / BM) * NB : 0;
-    npa[q] = f == fid && c % BM ? NB : 0;
-    lf += nfu[q];
-    lp += npa[q];
-  }
-  if (bad && blockIdx.x == 0 && a.flags) atomicOr(a.flags, bad);
-  int incf = lf, incp = lp;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int vf = __shfl_up(incf, off), vp = __shfl_up(incp, off);
-    if (lane >= off) {
-      incf += vf;
-      incp += vp;
-    }
-  }
-  if (lane == 63) {
-    s_wsum[0][wave] = incf;
-    s_wsum[1][wave] = incp;
-  }
-  __syncthreads();
-  int sf = incf - lf, sp = incp - lp, F = 0, P = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    if (w < wave) {
-      sf += s_wsum[0][w];
-      sp += s_wsum[1][w];
-    }
-    F += s_wsum[0][w];
-    P += s_wsum[1][w];
-  }
-  const int x = b & 7, slot = b >> 3;
-  if (!a.lpt) {
-    // one list, expert-major; XCD x takes tasks [x q8 + min(x, r8), + n8)
-    const int TOT = F + P;
-    const int q8 = TOT >> 3, r8 = TOT & 7;
-    const int n8 = q8 + (x < r8 ? 1 : 0);
-    const int L = x * q8 + min(x, r8) + slot;
-    if (slot < n8) {
-      int st = sf + sp;  // the thread's experts start here in the combined list
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int n = nfu[q] + npa[q];
-        if (L >= st && L < st + n) {
-          const int rel = L - st;
-          const int mt = (cnt[q] + BM - 1) / BM;
-          const int mi = rel % mt;
-          s_res[0] = 2 * tid + q;
-          s_res[1] = r0[q] + mi * BM;
-          s_res[2] = min(BM, cnt[q] - mi * BM);
-          s_res[3] = rel / mt;
-        }
-        st += n;
-      }
-    }
-  } else {
-    // the XCD's shares of the two lists
-    const int qf = F >> 3, rf = F & 7, qp = P >> 3, rp = P & 7;
-    const int nf = qf + (x < rf ? 1 : 0);
-    const int bf = x * qf + min(x, rf);
-    // the partial list's extras go to the last XCDs (the full list's to the
-    // first), so no XCD takes two
-    const int np = qp + (x >= 8 - rp ? 1 : 0);
-    const int bp = x * qp + max(0, x - (8 - rp));
-    const bool full = slot < nf;
-    const int L = full ? bf + slot : bp + (slot - nf);
-    if (full || slot - nf < np) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * tid + q;
-        const int st = full ? sf : sp;
-        const int n = full ? nfu[q] : npa[q];
-        if (L >= st && L < st + n) {
-          const int rel = L - st;
-          const int mf = cnt[q] / BM;  // full m-tiles of the expert
-          const int mi = full ? rel % mf : mf;
-          s_res[0] = e;
-          s_res[1] = r0[q] + mi * BM;
-          s_res[2] = min(BM, cnt[q] - mi * BM);
-          s_res[3] = full ? rel / mf : rel;
-        }
-        sf += nfu[q];
-        sp += npa[q];
-      }
-    }
-  }
-  __syncthreads();
-  // block-uniform: held in scalar registers, so what derives from them
-  // (weight addresses, buffer descriptors) is computed on the scalar unit
-  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
-  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
-  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
-  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
-  return task.e >= 0;
-}
-
-// Task lookup of the prefill kernel for a launch of less than two rounds of
-// block slots: longest first in four classes. The tiles with 4 filled 32-row
-// sub-tiles (full m-tiles, and partial ones of more than 3 BM / 4 rows) come
-// first, then the partial tiles with 3, 2 and 1, so the shortest blocks make
-// the tail. XCD x runs an equal contiguous share of each class in turn; a
-// class's remainder goes to the XCDs after the previous class's, so no XCD
-// takes more than one task above the others. (find_task_lpt holds the other
-// orders; this one pays for four prefix sums instead of two.)
-template <bool GU>
-__device__ bool find_task_lpt4(const FfnArgs& a, int fid, int BM, int NB, int b, Task& task) {
-  constexpr int NC = 4;  // longest-first classes: 4, 3, 2, 1 filled sub-tiles
-  __shared__ int s_wsum[NC][16];  // up to 1024 threads
-  __shared__ int s_res[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
-  if (tid == 0) s_res[0] = -1;
-  const int SUB = BM / 4;  // rows of a sub-tile class step
-  int cnt[2], ncl[2][NC], cls[2], r0[2];
-  int lsum[NC] = {0, 0, 0, 0};
-  uint32_t bad = 0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * tid + q;
-    int c = 0, f = -1, lo = 0;
-    if (e < a.E) f = expert_rows<GU>(a, e, lo, c, bad);
-    cnt[q] = c;
-    r0[q] = lo;
-    const bool mine = f == fid;
-    const int rem = c % BM;
-    // class of the partial tile: 0 (as long as a full one) .. 3 (shortest)
-    cls[q] = rem ? NC - (rem + SUB - 1) / SUB : 0;
-#pragma unroll
-    for (int k = 0; k < NC; ++k) ncl[q][k] = 0;
-    if (mine) {
-      ncl[q][0] = (c / BM) * NB;
-      if (rem) ncl[q][cls[q]] += NB;
-    }
-#pragma unroll
-    for (int k = 0; k < NC; ++k) lsum[k] += ncl[q][k];
-  }
-  if (bad && blockIdx.x == 0 && a.flags) atomicOr(a.flags, bad);
-  int inc[NC];
-#pragma unroll
-  for (int k = 0; k < NC; ++k) inc[k] = lsum[k];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int v = __shfl_up(inc[k], off);
-      if (lane >= off) inc[k] += v;
-    }
-  }
-  if (lane == 63) {
-#pragma unroll
-    for (int k = 0; k < NC; ++k) s_wsum[k][wave] = inc[k];
-  }
-  __syncthreads();
-  int st[NC], tot[NC];  // the thread's experts' first task in each list; list sizes
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    st[k] = inc[k] - lsum[k];
-    tot[k] = 0;
-  }
-  for (int w = 0; w < nwaves; ++w) {
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      if (w < wave) st[k] += s_wsum[k][w];
-      tot[k] += s_wsum[k][w];
-    }
-  }
-  const int x = b & 7, slot = b >> 3;
-  {
-    // XCD x's share of list k: q + 1 tasks on the r XCDs starting at `rot`
-    // (the XCD after the previous list's extras), q on the others
-    int rot = 0, before = 0;
-    int k_sel = -1, L = 0;
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int q = tot[k] >> 3, r = tot[k] & 7;
-      const int d = (x - rot + 8) & 7;  // x's position counted from rot
-      const int n = q + (d < r ? 1 : 0);
-      // extras of the XCDs below x: those at positions < r among x' < x
-      int ex = 0;
-      for (int y = 0; y < x; ++y) ex += ((y - rot + 8) & 7) < r ? 1 : 0;
-      if (k_sel < 0 && slot - before < n) {
-        k_sel = k;
-        L = x * q + ex + (slot - before);
-      }
-      before += n;
-      rot = (rot + r) & 7;
-    }
-    if (k_sel >= 0) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * tid + q;
-        int s0 = 0, n = 0;
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-          if (k == k_sel) {
-            s0 = st[k];
-            n = ncl[q][k];
-          }
-        }
-        if (L >= s0 && L < s0 + n) {
-          const int rel = L - s0;
-          const int mf = cnt[q] / BM;  // full m-tiles of the expert
-          int mi, nt;
-          if (k_sel == 0) {
-            // the expert's class-0 tiles: its full m-tiles, plus the partial
-            // one when that is class 0 too
-            const int mt = mf + ((cnt[q] % BM) && cls[q] == 0 ? 1 : 0);
-            mi = rel % mt;
-            nt = rel / mt;
-          } else {
-            mi = mf;
-            nt = rel;
-          }
-          s_res[0] = e;
-          s_res[1] = r0[q] + mi * BM;
-          s_res[2] = min(BM, cnt[q] - mi * BM);
-          s_res[3] = nt;
-        }
-        if (k_sel >= 0) {
-#pragma unroll
-          for (int k = 0; k < NC; ++k) st[k] += ncl[q][k];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // block-uniform: held in scalar registers, so what derives from them
-  // (weight addresses, buffer descriptors) is computed on the scalar unit
-  task.e = __builtin_amdgcn_readfirstlane(s_res[0]);
-  task.row0 = __builtin_amdgcn_readfirstlane(s_res[1]);
-  task.mcount = __builtin_amdgcn_readfirstlane(s_res[2]);
-  task.nt = __builtin_amdgcn_readfirstlane(s_res[3]);
-  return task.e >= 0;
-}
-
-// fp16 holds |v| <= 65504; beyond, the stored h is +-inf
-constexpr float kF16Max = 65504.0f;
-
-// stores h = silu(g) * u; true when h is stored as fp16 and overflows it
-__device__ inline bool store_gu(const FfnArgs& a, int row, int col, float g, float u) {
-  const float sc = a.ascale ? a.ascale[row] : 1.0f;
-  const float h = silu_mul(g * sc, u * sc);
-  if (a.out_f32) {
-    reinterpret_cast<float*>(a.out)[(size_t)row * a.N + col] = h;
-    return false;
-  }
-  reinterpret_cast<f16*>(a.out)[(size_t)row * a.N + col] = (f16)h;
-  return fabsf(h) > kF16Max;
-}
-
-__device__ inline void store_dn(const FfnArgs& a, int split, int row, int col, float y) {
-  const float sc = a.ascale ? a.ascale[row] : 1.0f;
-  reinterpret_cast<float*>(a.out)[((size_t)split * a.R + row) * a.N + col] = y * sc;
-}
-
-template <class F>
-struct BTile {
-  typename F::CodeT w0, w1;
-  PBuf<F::EB> q0, q1;
-};
-
-// 16 bytes per lane from r at voff + soff into LDS at lds + 16 lane
-__device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-
-// ===========================================================================
-// Decode family
-// ===========================================================================
-template <class F, bool GU>
-__global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
-  // The 4 wavefronts of a block form 4/ksw row groups of ksw wavefronts; the
-  // ksw wavefronts of a group split the K tiles of the block's K range and
-  // meet in LDS. A row group is the gate/up pair (output tile j: row tiles
-  // 2j, 2j+1) or the down row-tile pair (2j, 2j+1).
-  __shared__ float red[4 * 2 * 16 * 64];
-  const int G = 4 / ksw;
-  const int NRG = GU ? a.N / 32 : a.N / 64;
-  const int NB = (NRG + G - 1) / G;
-  Task t;
-  if (!find_task<GU>(a, F::ID, 32, NB, blockIdx.x, t)) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, kh = lane >> 5;
-  const int grp = wave / ksw, ks = wave % ksw;
-  const int rg = t.nt * G + grp;
-  const bool on = rg < NRG;
-  const int KTn = a.K / F::KT;
-  const int NE = a.K / F::GE;
-  const moe_packed_expert* ex = a.experts + t.e;
-  const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
-  const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
-  const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
-  // 32-row weight tiles of the matrix (2I rows of interleaved gate/up, or H)
-  const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
-  const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
-  const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
-  const uint32_t vc0 = (uint32_t)rt0 * KTn * F::TB + lane * F::CB;
-  const uint32_t vc1 = vc0 + (uint32_t)KTn * F::TB;
-  // group of the lane's first element in tile kt: kt KT / GE, plus kh SPAN / GE
-  // when groups are no longer than a tile
-  const uint32_t vp0 =
-      ((uint32_t)rt0 * NE * 32 + n + (F::GE <= F::KT ? kh * (F::SPAN / F::GE) : 0) * 32) * F::EB;
-  const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
-
-  const DeqConsts dk = make_deq_consts<F>();
-  const int split = blockIdx.y;
-  const int per = (KTn + a.splits - 1) / a.splits;
-  const int kb = split * per, ke = min(KTn, kb + per);
-
-  const bool arow = n < t.mcount;
-  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
-  const uint32_t va = ((uint32_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN) * 2;
-
-  struct AFrag {
-    f16x8 v[F::STEPS];
-  };
-  // tiles of this wavefront: kt_i = kb + ks + ksw i, i < nt. Prefetches past
-  // the last tile re-read a valid tile (result unused) so that the loop body
-  // has no conditional loads and exact wait counts.
-  const int nt = ke > kb + ks ? (ke - kb - ks + ksw - 1) / ksw : 0;
-  auto tile_of = [&](int i) { return min(kb + ks + ksw * i, KTn - 1); };
-  auto load_b = [&](int i, BTile<F>& b) {
-    const int kt = tile_of(i);
-    b.w0 = bload<typename F::CodeT, kNT>(rC, vc0, (uint32_t)kt * F::TB);
-    b.w1 = bload<typename F::CodeT, kNT>(rC, vc1, (uint32_t)kt * F::TB);
-    const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
-    b.q0.template load<kNT>(rP, vp0, sp);
-    b.q1.template load<kNT>(rP, vp1, sp);
-  };
-  auto load_a = [&](int i, AFrag& af) {
-    const int kt = tile_of(i);
-    // every lane loads: rows past the tile read the tile's first row, and
-    // their outputs (MFMA rows of their own) are never stored
-#pragma unroll
-    for (int s = 0; s < F::STEPS; ++s)
-      af.v[s] = bload<f16x8>(rA, va, (uint32_t)(kt * F::KT + 8 * s) * 2);
-  };
-  f32x16 acc0 = {}, acc1 = {};
-  auto compute = [&](const BTile<F>& b, const AFrag& af) {
-#pragma unroll
-    for (int s = 0; s < F::STEPS; ++s) {
-      const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s, dk);
-      const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s, dk);
-      acc0 = mfma32(af.v[s], b0, acc0);
-      acc1 = mfma32(af.v[s], b1, acc1);
-    }
-  };
-  // weights and token fragments two tiles ahead (three slots each)
-  BTile<F> B0, B1, B2;
-  AFrag A0, A1, A2;
-  load_b(0, B0);
-  load_a(0, A0);
-  load_b(1, B1);
-  load_a(1, A1);
-  for (int i = 0; i < nt; i += 3) {
-    load_b(i + 2, B2); load_a(i + 2, A2); compute(B0, A0);
-    load_b(i + 3, B0); load_a(i + 3, A0); if (i + 1 < nt) compute(B1, A1);
-    load_b(i + 4, B1); load_a(i + 4, A1); if (i + 2 < nt) compute(B2, A2);
-  }
-
-  // reduce the ksw partial sums of each row group: red[w][m][r][lane];
-  // wavefront ks of a group finalises registers r = (16/ksw) ks .. +16/ksw.
-  // Register r holds token rows 8(r/4) + (r%4) and that + 4 of the tile:
-  // registers whose rows all lie past the segment are neither reduced nor
-  // stored (at one token per expert only register 0 carries a row).
-  const int mrows = __builtin_amdgcn_readfirstlane(t.mcount);
-  auto live = [&](int r) { return 8 * (r >> 2) + (r & 3) < mrows; };
-  if (ksw > 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (!live(r)) continue;
-      red[((wave * 2 + 0) * 16 + r) * 64 + lane] = acc0[r];
-      red[((wave * 2 + 1) * 16 + r) * 64 + lane] = acc1[r];
-    }
-    __syncthreads();
-  }
-  if (!on) return;
-  const int RPW = 16 / ksw;
-  const int w0 = grp * ksw;
-  bool over = false;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r / RPW != ks || !live(r)) continue;
-    float v0 = acc0[r], v1 = acc1[r];
-    if (ksw > 1) {
-      v0 = 0.f;
-      v1 = 0.f;
-      for (int w = 0; w < ksw; ++w) {
-        v0 += red[(((w0 + w) * 2 + 0) * 16 + r) * 64 + lane];
-        v1 += red[(((w0 + w) * 2 + 1) * 16 + r) * 64 + lane];
-      }
-    }
-    const int i = acc_row(r, lane);
-    if (i < t.mcount) {
-      const int row = t.row0 + i;
-      if (GU) {
-        over |= store_gu(a, row, 32 * rg + n, v0, v1);
-      } else {
-        store_dn(a, split, row, 64 * rg + n, v0);
-        store_dn(a, split, row, 64 * rg + 32 + n, v1);
-      }
-    }
-  }
-  if (over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
-}
-
-// decode: fewest K tiles a wavefront of a K-split group streams
-#ifndef MOEQ_DEC_MINT
-#define MOEQ_DEC_MINT 16
-#endif
-
-// ===========================================================================
-// Prefill family
-// ===========================================================================
-// Prefill tuning knobs (defaults measured best on MI355X): the three-buffer
-// pipeline for 16 KiB token tiles, wavefronts per block. Weight loads are
-// cached: the m-tiles of an expert re-read each weight tile.
-#ifndef MOEQ_PF_DEEP
-#define MOEQ_PF_DEEP 1
-#endif
-#ifndef MOEQ_PF_WAVES
-#define MOEQ_PF_WAVES 4
-#endif
-// MOEQ_PF_BM: token rows per block (256 puts one wavefront on each SIMD and
-// measured ~20% slower; 64 spills at four blocks per CU)
-#ifndef MOEQ_PF_BM
-#define MOEQ_PF_BM 128
-#endif
-constexpr int kBM = MOEQ_PF_BM;
-constexpr int kMT = kBM / 32;  // 32-row sub-tiles per block tile
-// wavefronts per prefill block: they share one token tile in LDS, each
-// streaming its own 64 weight rows (one block per CU at 8)
-constexpr int kPW = MOEQ_PF_WAVES;
-constexpr int kBPC = (8 / kPW) * 128 / kBM;  // blocks per CU
-// bytes of LDS a prefill wavefront stages its output through: 16 rows of 64
-// fp32 at a pitch of 72
-constexpr int kStageB = 16 * 72 * 4;
-
-// LPT4: the four-class longest-first lookup (down launches of less than two
-// rounds); a separate instantiation, so the other launches keep the kernel
-// that the lighter lookup compiles to
-template <class F, bool GU, bool LPT4 = false>
-__global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) {
-  // Token tile in LDS: kBM rows x KT halves, rows packed (KT*2 bytes) with the
-  // 16-byte chunks of row r stored at chunk ^ swz(r). The LDS serves a 16-byte
-  // read of 16 lanes (16 consecutive rows, one logical chunk) per cycle from
-  // 64 banks; swz makes those 16 reads land on 16 different 4-bank groups.
-  constexpr int ROWB = F::KT * 2;
-  constexpr int TILEB = kBM * ROWB;           // 16 KiB (4-bit) or 32 KiB (2-bit)
-  constexpr int CPR = F::KT / 8;              // 16-byte chunks per row
-  constexpr int NI = TILEB / (kPW * 64 * 16);  // LDS-DMA instructions per wave and tile
-  // two separate arrays: the compiler can then tell that a DMA into one
-  // buffer does not feed reads of the other, and waits only where needed
-  // 16 KiB tiles (4-bit) get three buffers and a deeper pipeline
-  constexpr bool DEEP = MOEQ_PF_DEEP && 3 * TILEB * kBPC <= 160 * 1024;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[DEEP ? TILEB : 16];
-  // unit of one wavefront: gate/up output tile j (row tiles 2j, 2j+1), or
-  // the down row-tile pair (2j, 2j+1); a block covers kPW consecutive units
-  const int NU = a.N / (GU ? 32 : 64);
-  const int NB = (NU + kPW - 1) / kPW;
-  Task t;
-  bool found;
-  if constexpr (LPT4)
-    found = find_task_lpt4<GU>(a, F::ID, kBM, NB, blockIdx.x, t);
-  else
-    found = find_task_lpt<GU>(a, F::ID, kBM, NB, blockIdx.x, t);
-  if (!found) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, kh = lane >> 5;
-  const int KTn = a.K / F::KT;
-  const int NE = a.K / F::GE;
-  const moe_packed_expert* ex = a.experts + t.e;
-  const uint8_t* codes = (const uint8_t*)(GU ? ex->gu_codes : ex->dn_codes);
-  const uint8_t* params = (const uint8_t*)(GU ? ex->gu_params : ex->dn_params);
-  const int unit = kPW * t.nt + wave;
-  const bool on = unit < NU;
-  // a wavefront past the last unit streams a valid tile and discards it, so
-  // every wavefront runs the same straight-line loop
-  const int rt0 = 2 * unit;
-  const int rtl = 2 * min(unit, NU - 1);
-  // 32-row weight tiles of the matrix (2I rows of interleaved gate/up, or H);
-  // the descriptors span the whole matrix
-  const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
-  const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
-  const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
-  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
-  const uint32_t vc0 = (uint32_t)rtl * KTn * F::TB + lane * F::CB;
-  const uint32_t vc1 = vc0 + (uint32_t)KTn * F::TB;
-  // the group of a lane's first element in tile kt is kt KT / GE plus, when
-  // groups are no longer than a tile, its half's kh SPAN / GE
-  const uint32_t vp0 =
-      ((uint32_t)rtl * NE * 32 + n + (F::GE <= F::KT ? kh * (F::SPAN / F::GE) : 0) * 32) * F::EB;
-  const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
-
-  const DeqConsts dk = make_deq_consts<F>();
-  // Token tile DMA: instruction j of wavefront w fills LDS slots
-  // [(w NI + j) 64, +64) of the buffer, one 16-byte slot per lane. Slot ->
-  // (row, stored chunk) -> logical chunk; rows past the segment repeat its
-  // last row (their outputs are never stored). Offsets are in bytes from
-  // the start of K tile kt of the token matrix.
-  // 128-byte rows: two rows per 64 banks, so rows 2i and 2i+1 share a chunk
-  // pattern and differ in bank half; 256-byte rows fill all banks each.
-  auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
-  uint32_t doff[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int slot = (wave * NI + j) * 64 + lane;
-    const int r = slot / CPR, pc = slot % CPR;
-    const int c = pc ^ swz(r);
-    doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
-  }
-  auto dma_a = [&](int kt, uint8_t* buf) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16(rA, buf + (wave * NI + j) * 1024, doff[j], (uint32_t)kt * ROWB);
-  };
-  auto load_b = [&](int kt, BTile<F>& b) {
-    b.w0 = bload<typename F::CodeT>(rC, vc0, (uint32_t)kt * F::TB);
-    b.w1 = bload<typename F::CodeT>(rC, vc1, (uint32_t)kt * F::TB);
-    const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
-    b.q0.load(rP, vp0, sp);
-    b.q1.load(rP, vp1, sp);
-  };
-  // The block's pipeline, specialised on the number of 32-row sub-tiles
-  // that hold rows (the last m-tile of an expert is usually partial): empty
-  // sub-tiles cost no MFMAs and no LDS reads. amt is block-uniform, taken
-  // through a scalar register so every wavefront branches the same way.
-  const int amt = __builtin_amdgcn_readfirstlane((t.mcount + 31) / 32);
-  auto run = [&](auto amt_c) {
-    constexpr int AMT = decltype(amt_c)::value;
-    f32x16 acc[AMT][2];
-#pragma unroll
-    for (int mi = 0; mi < AMT; ++mi) {
-      acc[mi][0] = f32x16{};
-      acc[mi][1] = f32x16{};
-    }
-    // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
-    // kh*SPAN/8 + s; swz(mi*32 + n) == swz(n)
-    auto afrag = [&](const uint8_t* buf, int mi, int s) {
-      const int c = (kh * (F::SPAN / 8) + s) ^ swz(n);
-      return *reinterpret_cast<const f16x8*>(buf + (mi * 32 + n) * ROWB + c * 16);
-    };
-
-    // Pipeline, one barrier per K tile. At the start of tile kt the wavefront
-    // waits for its own DMA of token tile kt and its weight codes of tile kt
-    // (everything but the 4 weight loads of tile kt+1 issued at the end of
-    // tile kt-1), then the barrier makes every wavefront's DMA visible and
-    // frees the other buffer; the DMA of tile kt+1 goes out, tile kt is
-    // computed (codes of MFMA step s+1 decoded while the MFMAs of step s run),
-    // and the weight codes of tile kt+2 are fetched into the slot just used.
-    // Prefetches past the last tile re-read the last tile (unused).
-    BTile<F> R0, R1;  // raw weight codes (tile parity)
-    auto mma_jit = [&](const uint8_t* buf, const BTile<F>& raw) {
-      f16x8 av[AMT];
-#pragma unroll
-      for (int mi = 0; mi < AMT; ++mi) av[mi] = afrag(buf, mi, 0);
-      f16x8 d0 = dequant_step<F>(raw.w0, raw.q0, 0, dk);
-      f16x8 d1 = dequant_step<F>(raw.w1, raw.q1, 0, dk);
-#pragma unroll
-      for (int s = 0; s < F::STEPS; ++s) {
-        f16x8 an[AMT];
-        f16x8 n0 = d0, n1 = d1;
-        if (s + 1 < F::STEPS) {
-#pragma unroll
-          for (int mi = 0; mi < AMT; ++mi) an[mi] = afrag(buf, mi, s + 1);
-          n0 = dequant_step<F>(raw.w0, raw.q0, s + 1, dk);
-          n1 = dequant_step<F>(raw.w1, raw.q1, s + 1, dk);
-        }
-        // (a wavefront with no row tile of its own computes on the clamped
-        // tile and stores nothing: no branch around the matrix-core chain)
-#pragma unroll
-        for (int mi = 0; mi < AMT; ++mi) {
-          acc[mi][0] = mfma32(av[mi], d0, acc[mi][0]);
-          acc[mi][1] = mfma32(av[mi], d1, acc[mi][1]);
-        }
-        if (s + 1 < F::STEPS) {
-#pragma unroll
-          for (int mi = 0; mi < AMT; ++mi) av[mi] = an[mi];
-        }
-        d0 = n0;
-        d1 = n1;
-        // one scheduling region per step: each MFMA of step s is followed by
-        // a share of step s+1's decode, so a lone wavefront keeps the matrix
-        // core fed while it decodes (about 2/3 of the decode is pinned behind
-        // the MFMAs; the scheduler places the rest and the LDS reads, which
-        // measured 1-4% faster than pinning all of them)
-        constexpr int NM = 2 * AMT;
-        constexpr int VPM = (24 + NM - 1) / NM;
-        constexpr int VG = VPM > 2 ? VPM - 1 : VPM;
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    if constexpr (DEEP) {
-      // Three token buffers, three weight slots: the DMA of token tile kt+2
-      // goes out at the start of tile kt (into the buffer tile kt-1 used) and
-      // the weight codes of tile kt+3 at its end, so both are fetched two full
-      // tiles ahead. At the start of tile kt everything but the last 8 + NI
-      // memory operations (weights kt+1, DMA kt+1, weights kt+2) has landed.
-      BTile<F> R2;
-      constexpr int VM = 8 + NI;
-      auto tile = [&](int kt, uint8_t* cur, uint8_t* next2, BTile<F>& slot) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        dma_a(min(kt + 2, KTn - 1), next2);
-        mma_jit(cur, slot);
-        load_b(min(kt + 3, KTn - 1), slot);
-      };
-      load_b(0, R0);
-      dma_a(0, lds0);
-      load_b(min(1, KTn - 1), R1);
-      dma_a(min(1, KTn - 1), lds1);
-      load_b(min(2, KTn - 1), R2);
-      int kt = 0;
-      for (; kt + 2 < KTn; kt += 3) {
-        tile(kt, lds0, lds2, R0);
-        tile(kt + 1, lds1, lds0, R1);
-        tile(kt + 2, lds2, lds1, R2);
-      }
-      if (kt < KTn) tile(kt, lds0, lds2, R0);
-      if (kt + 1 < KTn) tile(kt + 1, lds1, lds0, R1);
-    } else {
-      // Two token buffers: the DMA of token tile kt+1 goes out at the start of
-      // tile kt, the weight codes of tile kt+2 at its end.
-      auto tile_start = [&](int kt, uint8_t* next) {
-        // vmcnt(4): the 4 weight loads of tile kt+1 may stay in flight
-        __builtin_amdgcn_s_waitcnt(0x0F74);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        // past the last tile this re-fills the idle buffer (no branch in the loop)
-        dma_a(min(kt + 1, KTn - 1), next);
-      };
-      dma_a(0, lds0);
-      load_b(0, R0);
-      load_b(min(1, KTn - 1), R1);
-      int kt = 0;
-      for (; kt + 1 < KTn; kt += 2) {
-        tile_start(kt, lds1);
-        mma_jit(lds0, R0);
-        load_b(min(kt + 2, KTn - 1), R0);
-        tile_start(kt + 1, lds0);
-        mma_jit(lds1, R1);
-        load_b(min(kt + 3, KTn - 1), R1);
-      }
-      if (kt < KTn) {
-        tile_start(kt, lds1);
-        mma_jit(lds0, R0);
-      }
-    }
-    // no LDS DMA may still be in flight when the block's LDS is released
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-
-    // Epilogue, staged through LDS 16 rows at a time so each lane stores 16
-    // bytes of a row instead of one element: a wavefront's output rows are 64
-    // fp32 (down) or 32 fp16/fp32 (gate/up) values held one column per lane,
-    // and one-element stores made the end of a block slow (20% of the
-    // short-K down launches). Each wavefront writes its own 4.5 KiB of the
-    // token buffers (wavefronts 0/1 in lds0, 2/3 in lds1) once every
-    // wavefront is past its last token tile. Row pitches are padded so rows
-    // r and r+4, written by the two lane halves, fall on different banks.
-    static_assert(kPW <= 4 && 2 * kStageB <= TILEB, "epilogue staging exceeds the token buffers");
-    __syncthreads();
-    if (!on) return;
-    uint8_t* stg = (wave >> 1 ? lds1 : lds0) + (wave & 1) * kStageB;
-    bool over = false;  // an fp16 h out of range (rows past the segment
-                        // repeat its last row, so they add no false report)
-#pragma unroll
-    for (int mi = 0; mi < AMT; ++mi) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int i0 = mi * 32 + 16 * hh;  // first tile row of this half
-        // a wavefront's LDS operations run in order: the fences only keep
-        // the compiler from moving reads of other lanes' values across writes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
-        for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
-          const int lr = 8 * ((r >> 2) & 1) + 4 * kh + (r & 3);  // == acc_row(r) - 16 hh
-          if constexpr (GU) {
-            const float sc = (a.ascale && i0 + lr < t.mcount) ? a.ascale[t.row0 + i0 + lr] : 1.0f;
-            const float h = silu_mul(acc[mi][0][r] * sc, acc[mi][1][r] * sc);
-            if (a.out_f32) {
-              reinterpret_cast<float*>(stg)[lr * 36 + n] = h;
-            } else {
-              reinterpret_cast<f16*>(stg)[lr * 40 + n] = (f16)h;
-              over |= fabsf(h) > kF16Max;
-            }
-          } else {
-            reinterpret_cast<float*>(stg)[lr * 72 + n] = acc[mi][0][r];
-            reinterpret_cast<float*>(stg)[lr * 72 + 32 + n] = acc[mi][1][r];
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if constexpr (GU) {
-          if (a.out_f32) {
-            // 16 rows x 32 fp32: 8 lanes per row, two stores
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int lr = 8 * j + (lane >> 3), c4 = lane & 7;
-              const float4 v = *reinterpret_cast<const float4*>(stg + (lr * 36 + 4 * c4) * 4);
-              if (i0 + lr < t.mcount)
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
-                                           (size_t)(t.row0 + i0 + lr) * a.N + 32 * unit + 4 * c4) = v;
-            }
-          } else {
-            // 16 rows x 32 fp16: 4 lanes per row, one store
-            const int lr = lane >> 2, c8 = lane & 3;
-            const uint4 v = *reinterpret_cast<const uint4*>(stg + (lr * 40 + 8 * c8) * 2);
-            if (i0 + lr < t.mcount)
-              *reinterpret_cast<uint4*>(reinterpret_cast<f16*>(a.out) +
-                                        (size_t)(t.row0 + i0 + lr) * a.N + 32 * unit + 8 * c8) = v;
-          }
-        } else {
-          // 16 rows x 64 fp32: 16 lanes per row, four stores
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int lr = 4 * j + (lane >> 4), c4 = lane & 15;
-            float4 v = *reinterpret_cast<const float4*>(stg + (lr * 72 + 4 * c4) * 4);
-            if (i0 + lr < t.mcount) {
-              const float sc = a.ascale ? a.ascale[t.row0 + i0 + lr] : 1.0f;
-              v.x *= sc;
-              v.y *= sc;
-              v.z *= sc;
-              v.w *= sc;
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
-                                         (size_t)(t.row0 + i0 + lr) * a.N + 32 * rt0 + 4 * c4) = v;
-            }
-          }
-        }
-      }
-    }
-    if (GU && over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
-  };
-  if (amt > 3 * kMT / 4)
-    run(IntC<kMT>{});
-  else if (amt > kMT / 2)
-    run(IntC<(3 * kMT / 4 > 1 ? 3 * kMT / 4 : 1)>{});
-  else if (amt > kMT / 4)
-    run(IntC<(kMT / 2 > 1 ? kMT / 2 : 1)>{});
-  else
-    run(IntC<(kMT / 4 > 1 ? kMT / 4 : 1)>{});
-}
-
-inline int max_tiles(int R, int E, int BM) { return (R + BM - 1) / BM + (R < E ? R : E); }
-
-// compute units of the current device
-inline int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
-template <int FID, bool GU>
-hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
-  using F = typename FmtOf<FID>::T;
-  if (decode) {
-    // wavefronts splitting K inside a block: as many as keep >= 16 K tiles
-    // (per split) on each; when few weight rows are in flight (a handful of
-    // tokens on small experts) streams of >= 8 tiles on more wavefronts
-    const int KTn = a.K / F::KT / (GU ? 1 : a.splits);
-    const int NRG = GU ? a.N / 32 : a.N / 64;
-    int ksw = KTn >= 4 * MOEQ_DEC_MINT ? 4 : (KTn >= 2 * MOEQ_DEC_MINT ? 2 : 1);
-    const long groups = (long)(a.R < a.E ? a.R : a.E) * NRG * (GU ? 1 : a.splits);
-    while (ksw < 4 && groups * ksw < 2048 && KTn >= 2 * ksw * (MOEQ_DEC_MINT / 2)) ksw *= 2;
-    // blocks (one per touched expert and row-group set, as when each touched
-    // expert has at most 32 rows) that would spill a little past one round
-    // of the device's block slots: half as many, on twice longer K streams,
-    // so the launch ends after one round (one token: 1.5 us of 37)
-    if (ksw > 1) {
-      const long blocks = groups / (4 / ksw);
-      int bpc = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void*)ffn_decode_kernel<F, GU>,
-                                                       kThreads, 0) != hipSuccess || bpc <= 0)
-        bpc = 1;
-      const long slots = (long)device_cus() * bpc;
-      if (blocks > slots && blocks <= 2 * slots) ksw /= 2;
-    }
-    const int NB = (NRG + 4 / ksw - 1) / (4 / ksw);
-    dim3 grid(max_tiles(a.R, a.E, 32) * NB, GU ? 1 : a.splits);
-    hipLaunchKernelGGL((ffn_decode_kernel<F, GU>), grid, dim3(kThreads), 0, s, a, ksw);
-  } else {
-    const int NU = a.N / (GU ? 32 : 64);
-    const int NB = (NU + kPW - 1) / kPW;
-    // longest-first order when the launch has fewer than 4 blocks per block
-    // slot of the device (its tail is then a large share of its time); for
-    // the down projection in four classes below 2 blocks per slot
-    const long nblk = (long)max_tiles(a.R, a.E, kBM) * NB;
-    FfnArgs b = a;
-    const long slots = (long)device_cus() * kBPC;
-    b.lpt = nblk < 2 * slots ? 2 : (nblk < 4 * slots ? 1 : 0);
-    // 16 spare blocks: the per-XCD task shares may round up (find_task_lpt)
-    dim3 grid(nblk + 16);
-    if (!GU && b.lpt == 2) {
-      hipLaunchKernelGGL((ffn_prefill_kernel<F, false, true>), grid, dim3(64 * kPW), 0, s, b);
-    } else {
-      if (b.lpt == 2) b.lpt = 1;  // gate/up: the two-class order
-      hipLaunchKernelGGL((ffn_prefill_kernel<F, GU, false>), grid, dim3(64 * kPW), 0, s, b);
-    }
-  }
-  return hipGetLastError();
-}
-
-template <bool GU>
-hipError_t launch_all(const FfnArgs& a, bool decode, hipStream_t s) {
+// one launch per format of the mask
+hipError_t launch_all(int role, const FfnArgs& a, bool decode, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  const uint32_t mask = a.fmt_mask;
-  hipError_t e = hipSuccess;
-#define MOEQ_LAUNCH(FID)                                              \
-  if (e == hipSuccess && ((mask >> FID) & 1u)) e = launch_one<FID, GU>(a, decode, s);
-  MOEQ_LAUNCH(F_A4G16)
-  MOEQ_LAUNCH(F_A4G32)
-  MOEQ_LAUNCH(F_A4G64)
-  MOEQ_LAUNCH(F_A4G128)
-  MOEQ_LAUNCH(F_A2G16)
-  MOEQ_LAUNCH(F_A2G32)
-  MOEQ_LAUNCH(F_A2G64)
-  MOEQ_LAUNCH(F_A2G128)
-  MOEQ_LAUNCH(F_E4G16)
-  MOEQ_LAUNCH(F_E4G32)
-  MOEQ_LAUNCH(F_E4G64)
-  MOEQ_LAUNCH(F_E4G128)
-  MOEQ_LAUNCH(F_A1G16)
-  MOEQ_LAUNCH(F_A1G32)
-  MOEQ_LAUNCH(F_A1G64)
-  MOEQ_LAUNCH(F_A1G128)
-#undef MOEQ_LAUNCH
-  return e;
+  for (int f = 0; f < F_COUNT; ++f) {
+    if ((a.fmt_mask >> f) & 1u) {
+      const hipError_t e = launch_ffn_fmt(f, role, a, decode, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1076,7 +59,13 @@ hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* o
   a.R = T * k;
   a.splits = 1;
   a.lpt = 0;
-  return launch_all<true>(a, decode, s);
+  hipError_t e = launch_all(R_GU, a, decode, s);
+  if (e == hipSuccess && (fmt_mask & kMaskSplitGU)) {
+    // experts with separate gate and up streams: g first, then h in place
+    e = launch_all(R_GATE, a, decode, s);
+    if (e == hipSuccess) e = launch_all(R_UP, a, decode, s);
+  }
+  return e;
 }
 
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
@@ -1098,7 +87,7 @@ hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offs
   a.R = T * k;
   a.splits = decode ? splits : 1;
   a.lpt = 0;
-  return launch_all<false>(a, decode, s);
+  return launch_all(R_DN, a, decode, s);
 }
 
 }  // namespace moeq

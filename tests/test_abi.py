@@ -101,17 +101,22 @@ def test_permute_workspace_size():
     assert L.moe_permute(p, 1 << 20, 1 << 11, 256, p, p, p, p, p, 1 << 30, None) == -1
 
 
-def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bits=None):
-    q = lambda r, c, b: _lib.QMatC(fmt, b, group, r, c, codes, params)
-    return _lib.ExpertCanonC(q(I, H, bits), q(I, H, bits), q(H, I, down_bits or bits))
+def _canon(fmt=1, bits=4, group=32, I=256, H=256, codes=256, params=256, down_bits=None,
+           up_bits=None, n_out=0, outliers=0):
+    q = lambda r, c, b: _lib.QMatC(fmt, b, group, r, c, n_out, codes, params, outliers or None)
+    return _lib.ExpertCanonC(q(I, H, bits), q(I, H, up_bits or bits), q(H, I, down_bits or bits))
 
 
 @pytest.mark.parametrize("kw,ok", [
-    (dict(), True), (dict(bits=3), False), (dict(group=48), False), (dict(fmt=3), False),
+    (dict(), True), (dict(bits=3), True), (dict(bits=5), False), (dict(group=48), False),
+    (dict(fmt=3), False),
     (dict(fmt=2, bits=2), False), (dict(I=100), False), (dict(codes=8), False),
     (dict(params=2), False), (dict(codes=0), False), (dict(fmt=2, group=16), True),
-    (dict(bits=2, group=16), True), (dict(down_bits=2), True),
+    (dict(bits=2, group=16), True), (dict(down_bits=2), True), (dict(up_bits=3), True),
     (dict(I=65536, H=65536), False),  # beyond 32-bit offsets into a packed matrix
+    (dict(n_out=10, outliers=256), True), (dict(n_out=10), False),  # outlier list missing
+    (dict(n_out=10, outliers=260), False),                          # misaligned list
+    (dict(n_out=256 * 256 + 1, outliers=256), False),               # more than the matrix
 ])
 def test_packed_bytes_validation(kw, ok):
     ec = _canon(**kw)
@@ -125,6 +130,35 @@ def test_packed_bytes_value():
     n = _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec))
     w = 3 * 512 * 256
     assert n == w // 2 + w // 32 * 4
+    # 3-bit g32: 3/8 B/weight of codes, the same params
+    ec = _canon(I=512, H=256, bits=3)
+    assert _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec)) == w * 3 // 8 + w // 32 * 4
+    # gate 3-bit, up 2-bit, down 4-bit: separate gate and up streams
+    ec = _canon(I=512, H=256, bits=3, up_bits=2, down_bits=4)
+    m = 512 * 256
+    assert _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec)) == \
+        m * 3 // 8 + m * 2 // 8 + m * 4 // 8 + 3 * (m // 32 * 4)
+    # outliers: per matrix group a row-pointer array and 8-byte entries (each
+    # part 256-byte aligned)
+    al = lambda v: (v + 255) // 256 * 256
+    ec = _canon(I=512, H=256, n_out=100, outliers=256)
+    assert _lib.LIB.moe_packed_expert_bytes(ctypes.byref(ec)) == \
+        w // 2 + w // 32 * 4 + al((2 * 512 + 1) * 4) + al(200 * 8) + al((256 + 1) * 4) + al(100 * 8)
+
+
+def test_format_mask_split_bit():
+    d = (_lib.PackedExpertC * 2)()
+    d[0].gu_fmt, d[0].gu_bits, d[0].gu_group = 1, 3, 32
+    d[0].up_fmt, d[0].up_bits, d[0].up_group = 1, 2, 16
+    d[0].dn_fmt, d[0].dn_bits, d[0].dn_group = 1, 4, 32
+    d[0].layout = _lib.PACK_SPLIT_GU
+    for x in (d[1],):
+        x.gu_fmt, x.gu_bits, x.gu_group = 2, 4, 16
+        x.up_fmt, x.up_bits, x.up_group = 2, 4, 16
+        x.dn_fmt, x.dn_bits, x.dn_group = 2, 4, 16
+    m = _lib.LIB.moe_format_mask(d, 2)
+    # ids 4c+g: asym 3-bit c=4 g32 -> 17; asym 2-bit g16 -> 4; asym 4-bit g32 -> 1; e2m1 g16 -> 8
+    assert m == (1 << 17) | (1 << 4) | (1 << 1) | (1 << 8) | _lib.MASK_SPLIT_GU
 
 
 def test_ffn_rejects_small_workspace():

@@ -630,3 +630,74 @@ def test_expert_shape_mismatch_is_skipped(moeq):
     torch.cuda.synchronize()
     assert moeq.read_flags(ws) & moeq.FLAG_EXPERT_SHAPE
     assert (Yb == canary).all()
+
+
+# ------------------------------------------- per-matrix formats, 3-bit, outliers
+def _fmt_plan(kind, E):
+    """Per-expert (gate, up, down) formats of a parity case."""
+    from synth import FMT_ASYM, FMT_E2M1
+    A = lambda b, g: (FMT_ASYM, b, g)
+    if kind == "three_bit":
+        cyc = [(A(3, g),) * 3 for g in (16, 32, 64, 128)]
+    elif kind == "split":
+        # the "AlphaQ" mix (gate 3-bit, up 2-bit, down 4-bit) and others whose
+        # gate and up formats differ, next to experts that keep them equal
+        cyc = [(A(3, 32), A(2, 16), A(4, 32)), (A(4, 32), A(3, 64), A(2, 16)),
+               (A(2, 16), A(4, 64), A(3, 32)), ((FMT_E2M1, 4, 16), A(4, 32), A(1, 32)),
+               (A(4, 32), A(4, 32), A(4, 32))]
+    else:
+        cyc = [(A(4, 32),) * 3, ((FMT_E2M1, 4, 16),) * 3, (A(2, 16),) * 3, (A(3, 32),) * 3]
+    return tuple(cyc[e % len(cyc)] for e in range(E))
+
+
+NEXT_CASES = [
+    # name, T, H, I, E, k, kind, outlier share
+    ("mixtral", 40, 512, 512, 8, 2, "three_bit", 0.0),     # decode GEMV
+    ("mixtral", 600, 512, 512, 8, 2, "three_bit", 0.0),    # prefill GEMM
+    ("mixtral", 40, 512, 512, 8, 2, "split", 0.0),
+    ("mixtral", 600, 512, 512, 8, 2, "split", 0.0),
+    ("hotcold", 1, 1024, 256, 32, 4, "split", 0.0),        # one token, fused front
+    ("mixtral", 40, 512, 512, 8, 2, "mixed", 0.005),       # outliers, decode
+    ("mixtral", 600, 512, 512, 8, 2, "mixed", 0.005),      # outliers, prefill
+    ("mixtral", 600, 512, 384, 8, 2, "mixed", 0.0005),     # 0.05%: the field notes' share
+    ("w4a8", 300, 512, 512, 8, 2, "split", 0.005),         # int8 x and h, split, outliers
+    ("w4a8", 16, 512, 512, 8, 2, "split", 0.005),
+    ("fine_e2m1", 70, 256, 256, 64, 6, "split", 0.005),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,kind,frac", NEXT_CASES)
+def test_layer_parity_matrix_formats_and_outliers(moeq, name, T, H, I, E, k, kind, frac):
+    from dataclasses import replace
+    cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode="quantize",
+                              n_hot=min(64, E // 4) if name == "hotcold" else None)
+    cfg = replace(cfg, matrix_fmts=_fmt_plan(kind, E), weight_outlier_frac=frac)
+    _say(f"[formats] {name} T={T} H={H} I={I} E={E} k={k} {kind} outliers={frac} act={cfg.act} "
+         f"({prefill_order(T, H, I, E, k)})")
+    wl = Workload(cfg)
+    if kind == "split":
+        assert wl.packed.fmt_mask & (1 << 31)
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+    out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) == 0
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, wl.b_np if cfg.zipf_alpha > 0 else None,
+                           wl.expert, cfg.E, cfg.k, act=cfg.act)
+    ok = ~ref["flagged"]
+    np.testing.assert_array_equal(ids.cpu().numpy()[ok], ref["ids"][ok])
+    err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
+    _say(f"    max row rel-L2 {err.max():.3e}")
+    assert err.max() <= tolerance(cfg), err.max()
+    if frac > 0:
+        # the side lists matter: the same layer without them is further away
+        # same blocks, lists dropped: repack from the workload's own blobs
+        def bare(e):
+            ex = wl.expert(e)
+            return {r: synth.QMat(q.fmt, q.bits, q.group, q.rows, q.cols, q.codes, q.params)
+                    for r, q in ex.items()}
+        packed0 = moeq.pack_experts(bare, cfg.E)
+        out0, _, _ = moeq.layer_forward(wl.x, wl.Wr, wl.b, packed0, cfg.k, act=cfg.act)
+        torch.cuda.synchronize()
+        err0 = rel_l2_rows(out0.cpu().numpy()[ok], ref["out"][ok])
+        _say(f"    without the side lists: max row rel-L2 {err0.max():.3e}")
+        assert err0.max() > 4 * err.max()
