@@ -345,6 +345,30 @@ class Bench:
             f"route_i8 {r8['route_i8_ms'] * 1e3:.1f} us")
         return r8
 
+    def outliers(self, wl, T, flush):
+        """Cost of fp16 outlier side lists (0.05% of each expert matrix, the
+        field notes' share): the same layer packed with them, prefill and
+        decode times against the plain layer's."""
+        from dataclasses import replace
+        from layer_cases import Workload
+        cfg = wl.cfg
+        frac = 0.0005
+        wl2 = Workload(replace(cfg, weight_outlier_frac=frac), device=self.dev)
+        d, _, _ = self.prefill(wl2, T)
+        res = {"share": frac, "outliers_per_expert": int(round(frac * 3 * cfg.H * cfg.I)),
+               "prefill_ms": d["ms_per_step"], "prefill_gate_up_ms": d["gate_up_ms"],
+               "prefill_down_ms": d["down_ms"]}
+        if cfg.decode_T:
+            dd = []
+            for Td in cfg.decode_T:
+                r, _, _ = self.decode(wl2, Td, flush, False)
+                dd.append({"tokens": Td, "layer_ms": r["layer_ms"], "gate_up_ms": r["gate_up_ms"],
+                           "down_ms": r["down_ms"]})
+            res["decode"] = dd
+        del wl2
+        log(f"[bench] {cfg.name} with 0.05% outliers: prefill {res['prefill_ms']:.3f} ms")
+        return res
+
     def tiers(self, wl, T, ids_own):
         """Expert-aware precision from a routing profile of T held-out tokens:
         the tier plan within the byte budget of the workload's bias-ranked hot
@@ -395,6 +419,11 @@ class Bench:
         tiers3, used3 = moeq.plan_tiers(counts_cal, sizes3, budget)
         fm3 = (cfg.fmt, cfg.cold_fmt, one)
         ms_3 = timed(fm3[t] for t in tiers3)
+        # four tiers, a bit apart each (4-, 3-, 2-, 1-bit, group 32)
+        fm4 = ((1, 4, 32), (1, 3, 32), (1, 2, 32), (1, 1, 32))
+        sizes4 = [expert_bytes(f) for f in fm4]
+        tiers4, used4 = moeq.plan_tiers(counts_cal, sizes4, budget)
+        ms_4 = timed(fm4[t] for t in tiers4)
         res = {"calibration_tokens": T, "hot_experts": int(hot.sum()),
                "tier_bytes": sizes, "budget_bytes": int(budget), "used_bytes": int(used),
                "histogram_ms": h0.elapsed_time(h1), "plan_us": plan_us,
@@ -406,10 +435,18 @@ class Bench:
                               "experts_per_tier": [int((tiers3 == t).sum()) for t in range(3)],
                               "slot_share_per_tier": [float(own[tiers3 == t].sum() / own.sum())
                                                       for t in range(3)],
-                              "prefill_ms": ms_3}}
+                              "prefill_ms": ms_3},
+               "four_tier": {"formats": ["asym 4-bit g32", "asym 3-bit g32", "asym 2-bit g32",
+                                         "asym 1-bit g32"],
+                             "tier_bytes": sizes4, "used_bytes": int(used4),
+                             "experts_per_tier": [int((tiers4 == t).sum()) for t in range(4)],
+                             "slot_share_per_tier": [float(own[tiers4 == t].sum() / own.sum())
+                                                     for t in range(4)],
+                             "prefill_ms": ms_4}}
         log(f"[bench] {cfg.name} tiers: profiled hot set shares {res['hot_share_profiled']:.3f} "
             f"of the slots (bias-ranked {res['hot_share_bias_ranked']:.3f}), prefill {ms_p:.3f} ms; "
-            f"three tiers {res['three_tier']['experts_per_tier']}, prefill {ms_3:.3f} ms")
+            f"three tiers {res['three_tier']['experts_per_tier']}, prefill {ms_3:.3f} ms; "
+            f"four tiers {res['four_tier']['experts_per_tier']}, prefill {ms_4:.3f} ms")
         return res
 
 
@@ -573,6 +610,8 @@ def main():
                 d, od, idd = bench.decode(wl, Td, flush, extras and name == "mixtral")
                 ent["decode"].append(d)
                 outs[Td] = (od.cpu().numpy(), idd.cpu().numpy())
+        if extras and name == "mixtral" and not args.no_prefill and flush is not None:
+            ent["outliers"] = bench.outliers(wl, cfg.T, flush)
         if not args.no_cpu_baseline and outs:
             if name == HEADLINE:
                 cpu_headline, par = headline_oracle_sample(cfg, wl, outs)

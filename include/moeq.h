@@ -189,12 +189,16 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
  * down matrix has format i, with i = 4*c + g, c = 0 asym 4-bit, 1 asym 2-bit,
  * 2 e2m1, 3 asym 1-bit, 4 asym 3-bit, and g = 0,1,2,3 for group 16, 32, 64,
  * 128; bit 31 (MOE_MASK_SPLIT_GU) is set when some expert has the split
- * gate/up layout. The FFN entry points take this mask (fmt_mask) and run one
+ * gate/up layout, bit 30 (MOE_MASK_NO_FUSE) when some expert has the split
+ * layout, outlier lists or a down format other than its gate/up format (the
+ * fused decode kernel of moe_layer_forward then stays unused). The FFN entry
+ * points take this mask (fmt_mask) and run one
  * kernel per format (and role) in it; 0 means every supported format
  * (correct for any expert set, but each absent format still costs launches).
  * Experts whose format is missing from a non-zero mask are skipped and flag
  * MOE_FLAG_FORMAT_NOT_LAUNCHED. Host only. */
 #define MOE_MASK_SPLIT_GU (1u << 31)
+#define MOE_MASK_NO_FUSE (1u << 30)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 
 /* Workspace bytes the layer entry points need for these sizes. Host only. */

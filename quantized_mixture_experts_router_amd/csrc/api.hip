@@ -99,7 +99,7 @@ moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, 
 }
 
 inline uint32_t effective_mask(uint32_t m) {
-  return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU);
+  return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU | kMaskNoFuse);
 }
 
 moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
@@ -190,6 +190,22 @@ moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const
                            ws_at(ws, L.pscratch), s));
     MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
                             (float*)ws_at(ws, L.ascale), flags, s));
+  }
+  const FusedPlan fp = fused_plan(T, H, I, E, k, aq);
+  const uint32_t mask = effective_mask(fmt_mask);
+  if (fp.use && !(mask & kMaskNoFuse)) {
+    // small decode batch: gate/up, SwiGLU and down in one launch per format,
+    // then the sum of its partial planes
+    int ns = 0;
+    const hipError_t e = launch_ffn_fused(experts, offsets, mask, flags, T, H, I, E, k,
+                                          (const f16*)ws_at(ws, L.a16),
+                                          aq != MOE_ACT_NONE ? (const float*)ws_at(ws, L.ascale)
+                                                             : nullptr,
+                                          yp, fp.S, fp.ns, &ns, s);
+    if (e == hipSuccess)
+      return hip_status(launch_combine_slices(yp, ns, w, inv, T, H, k, out, out_dt, s));
+    if (e != hipErrorNotSupported) return MOE_ERR_HIP;
+    // no slice width fits these formats: the two-launch path below
   }
   st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, s);
   if (st != MOE_OK) return st;
@@ -305,6 +321,8 @@ uint32_t moe_format_mask(const moe_packed_expert* descs, int E) {
     if (u >= 0) m |= 1u << u;
     if (b >= 0) m |= 1u << b;
     if (descs[e].layout & MOE_PACK_SPLIT_GU) m |= kMaskSplitGU;
+    if ((descs[e].layout & MOE_PACK_SPLIT_GU) || descs[e].n_out_gu || descs[e].n_out_dn || a != b)
+      m |= kMaskNoFuse;
   }
   return m;
 }

@@ -208,8 +208,58 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
+// out[t] = sum_j w[t,j] * sum_s yp[s][inv[t*k+j]] over ns partial planes:
+// block (token t, 16 columns), wavefront q the 4 columns 4q..4q+3 of them,
+// lane l the planes l, l + 64, ...; then a butterfly over the 64 lanes.
+// The order of every sum is fixed, so results are the same run to run.
+__global__ __launch_bounds__(kThreads) void combine_slices_kernel(const float* __restrict__ yp,
+                                                                int ns, size_t plane,
+                                                                const float* __restrict__ w,
+                                                                const int32_t* __restrict__ inv,
+                                                                int H, int k, void* __restrict__ out,
+                                                                int out_dt) {
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 16 + 4 * q;
+  const int R = (int)(plane / H);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(size_t)t * k + j];
+    if (r < 0 || r >= R) continue;
+    const float wt = w[(size_t)t * k + j];
+    const float* src = yp + (size_t)r * H + c;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int s = lane; s < ns; s += 64) y += *reinterpret_cast<const f32x4*>(src + s * plane);
+    acc += wt * y;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+  }
+  if (lane != 0) return;
+  if (out_dt == MOE_F32) {
+    *reinterpret_cast<f32x4*>((float*)out + (size_t)t * H + c) = acc;
+  } else {
+    uint16_t* o = (uint16_t*)out + (size_t)t * H + c;
+    o[0] = f32_to_bf16_rne(acc[0]);
+    o[1] = f32_to_bf16_rne(acc[1]);
+    o[2] = f32_to_bf16_rne(acc[2]);
+    o[3] = f32_to_bf16_rne(acc[3]);
+  }
+}
 
 }  // namespace
+
+hipError_t launch_combine_slices(const float* yp, int ns, const float* w, const int32_t* inv,
+                                 int T, int H, int k, void* out, int out_dt, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const size_t plane = (size_t)T * k * H;
+  dim3 grid(H / 16, T);
+  hipLaunchKernelGGL(combine_slices_kernel, grid, dim3(kThreads), 0, s, yp, ns, plane, w, inv, H,
+                     k, out, out_dt);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
                            int quant, f16* a16, float* ascale, uint32_t* flags, hipStream_t s) {

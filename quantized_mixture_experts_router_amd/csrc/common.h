@@ -35,8 +35,11 @@ enum FmtId : int {
 };
 // bit of a format mask: some expert stores gate and up as separate streams
 // (their formats differ), so the split gate and up passes run too
-constexpr uint32_t kMaskSplitGU = 1u << 31;
-static_assert(F_COUNT <= 31, "format mask bits");
+constexpr uint32_t kMaskSplitGU = MOE_MASK_SPLIT_GU;
+// bit of a format mask: some expert cannot take the fused decode kernel
+// (split gate/up, outlier lists, or a down format other than its gate/up's)
+constexpr uint32_t kMaskNoFuse = MOE_MASK_NO_FUSE;
+static_assert(F_COUNT <= 30, "format mask bits");
 
 __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   int g = group == 16 ? 0 : group == 32 ? 1 : group == 64 ? 2 : group == 128 ? 3 : -1;
@@ -172,6 +175,49 @@ inline int down_splits(int T, int H, int I, int E, int k) {
   return s < 1 ? 1 : (int)s;
 }
 
+// Fused decode FFN plan (host-known sizes only): used for decode batches of
+// at most 32 tokens (one 32-row tile per expert) with one row per touched
+// expert on average (MOEQ_FUSED_MAXROWS; with more, the partial planes cost
+// more than the second launch saves: measured slower at 2 and 8 rows per
+// expert), when the (touched expert, slice) blocks fill the device (at
+// least 256; the 256-expert layer's 512-wide experts give too few slices at
+// one token and measured slower), and without int8 h (its per-row scale
+// needs the whole row of h). The slice width S is the smallest of 64 and the
+// multiples of 128 dividing I whose ns = I / S partial planes [ns][T*k][H]
+// fp32 stay within ~6% of the touched experts' weight bytes at 0.625 B per
+// weight (ns <= 0.028 I / rows), and at most 512 (the h slice stays in 33
+// KiB of LDS). A launch may widen S for its formats' K tiles and parameter
+// groups (fewer planes, within the workspace).
+#ifndef MOEQ_FUSED_MAXROWS
+#define MOEQ_FUSED_MAXROWS 1
+#endif
+#ifndef MOEQ_FUSED_MINBLOCKS
+#define MOEQ_FUSED_MINBLOCKS 256
+#endif
+struct FusedPlan {
+  bool use;
+  int S, ns;
+};
+inline FusedPlan fused_plan(int T, int H, int I, int E, int k, int aq) {
+  FusedPlan p = {false, 0, 0};
+  (void)H;
+  if (!use_decode_path(T, k, E) || T > 32 || T <= 0 || aq == MOE_ACT_I8_XH) return p;
+  const long R = (long)T * k, te = R < E ? R : E;
+  const double rows = (double)R / (double)te;
+  if (rows > MOEQ_FUSED_MAXROWS) return p;
+  const double nsmax = 0.028125 * I / rows;
+  for (int S = 64; S <= I && S <= 512; S = S == 64 ? 128 : S + 128) {
+    if (I % S == 0 && I / S <= nsmax) {
+      if (te * (I / S) < MOEQ_FUSED_MINBLOCKS) return p;
+      p.use = true;
+      p.S = S;
+      p.ns = I / S;
+      return p;
+    }
+  }
+  return p;
+}
+
 // Router plan (host-known sizes only). The fp64 logits kernel runs one
 // block per (16-token tile, group of ntw 16-expert tiles, K block); the
 // block's ks wavefronts split the K block's 16-column chunks, cpw chunks
@@ -234,7 +280,9 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   L.hscale = take(R * 4);
   L.splits = down_splits(T, H, I, E, k);
   L.decode = use_decode_path(T, k, E);
-  const size_t yp_bytes = (size_t)L.splits * R * H * 4;
+  const FusedPlan fp = fused_plan(T, H, I, E, k, aq);
+  const int planes = fp.use && fp.ns > L.splits ? fp.ns : L.splits;
+  const size_t yp_bytes = (size_t)planes * R * H * 4;
   const size_t rp_bytes = route_plan(T, H, E).part_bytes;
   const size_t ps_bytes = permute_plan((int)R, E).scratch_bytes;
   size_t big = yp_bytes > rp_bytes ? yp_bytes : rp_bytes;
@@ -286,6 +334,16 @@ hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offs
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);
+// combine of many partial planes (the fused decode FFN's slices)
+hipError_t launch_combine_slices(const float* yp, int ns, const float* w, const int32_t* inv,
+                                 int T, int H, int k, void* out, int out_dt, hipStream_t s);
+// fused decode FFN over the experts of the mask's formats; S is widened to
+// the formats' K tiles and groups (returns hipErrorNotSupported when no
+// admissible S fits the plan, before launching anything)
+hipError_t launch_ffn_fused(const moe_packed_expert* experts, const int32_t* offsets,
+                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
+                            const f16* a16, const float* ascale, float* yp, int S_plan,
+                            int ns_plan, int* ns_used, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                               hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,

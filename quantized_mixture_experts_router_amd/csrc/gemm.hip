@@ -3,7 +3,7 @@
 // gate and up share a format; split gate then up for the others; down).
 // The kernels live in gemm_impl.h, instantiated per format family.
 #include "common.h"
-#include "gemm_impl.h"
+#include "fused_impl.h"
 
 namespace moeq {
 
@@ -12,6 +12,12 @@ hipError_t launch_ffn_a2(int fid, int role, const FfnArgs& a, bool decode, hipSt
 hipError_t launch_ffn_e4(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
 hipError_t launch_ffn_a1(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
 hipError_t launch_ffn_a3(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s);
+
+hipError_t launch_fused_a4(int fid, const FusedArgs& fa, hipStream_t s);
+hipError_t launch_fused_a2(int fid, const FusedArgs& fa, hipStream_t s);
+hipError_t launch_fused_e4(int fid, const FusedArgs& fa, hipStream_t s);
+hipError_t launch_fused_a1(int fid, const FusedArgs& fa, hipStream_t s);
+hipError_t launch_fused_a3(int fid, const FusedArgs& fa, hipStream_t s);
 
 hipError_t launch_ffn_fmt(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s) {
   switch (fid / 4) {
@@ -66,6 +72,67 @@ hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* o
     if (e == hipSuccess) e = launch_all(R_UP, a, decode, s);
   }
   return e;
+}
+
+// K tile and parameter entry widths of format id f (host)
+static void fmt_tile(int f, int& kt, int& ge) {
+  const int fam = f / 4, group = 16 << (f % 4);
+  const int span = (fam == 0 || fam == 2) ? 32 : 64;  // 4-bit and e2m1 : 2-, 1-, 3-bit
+  kt = 2 * span;
+  ge = group > span ? group : span;
+}
+
+hipError_t launch_ffn_fused(const moe_packed_expert* experts, const int32_t* offsets,
+                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
+                            const f16* a16, const float* ascale, float* yp, int S_plan,
+                            int ns_plan, int* ns_used, hipStream_t s) {
+  // the smallest admissible S >= the plan's for every format present
+  int S = 0;
+  for (int c = S_plan; c <= I && c <= 512 && !S; c = c == 64 ? 128 : c + 128) {
+    if (I % c != 0) continue;
+    bool ok = true;
+    for (int f = 0; f < F_COUNT && ok; ++f) {
+      if (!((fmt_mask >> f) & 1u)) continue;
+      int kt, ge;
+      fmt_tile(f, kt, ge);
+      ok = c % kt == 0 && c % ge == 0;
+    }
+    if (ok) S = c;
+  }
+  if (!S || I / S > ns_plan) return hipErrorNotSupported;
+  FusedArgs fa;
+  FfnArgs& a = fa.g;
+  a.experts = experts;
+  a.offsets = offsets;
+  a.flags = flags;
+  a.fmt_mask = fmt_mask;
+  a.E = E;
+  a.K = H;
+  a.N = I;
+  a.a = a16;
+  a.ascale = ascale;
+  a.out = nullptr;
+  a.out_f32 = 0;
+  a.R = T * k;
+  a.splits = 1;
+  a.lpt = 0;
+  fa.yp = yp;
+  fa.S = S;
+  fa.ns = I / S;
+  *ns_used = fa.ns;
+  for (int f = 0; f < F_COUNT; ++f) {
+    if (!((fmt_mask >> f) & 1u)) continue;
+    hipError_t e;
+    switch (f / 4) {
+      case 0: e = launch_fused_a4(f, fa, s); break;
+      case 1: e = launch_fused_a2(f, fa, s); break;
+      case 2: e = launch_fused_e4(f, fa, s); break;
+      case 3: e = launch_fused_a1(f, fa, s); break;
+      default: e = launch_fused_a3(f, fa, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,

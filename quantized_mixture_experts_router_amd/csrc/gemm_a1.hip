@@ -1,5 +1,5 @@
 // Grouped expert GEMMs of the asymmetric 1-bit block formats (groups 16, 32, 64, 128).
-#include "gemm_impl.h"
+#include "fused_impl.h"
 
 namespace moeq {
 
@@ -9,6 +9,16 @@ hipError_t launch_ffn_a1(int fid, int role, const FfnArgs& a, bool decode, hipSt
     case F_A1G32: return launch_roles<F_A1G32>(role, a, decode, s);
     case F_A1G64: return launch_roles<F_A1G64>(role, a, decode, s);
     case F_A1G128: return launch_roles<F_A1G128>(role, a, decode, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_a1(int fid, const FusedArgs& fa, hipStream_t s) {
+  switch (fid) {
+    case F_A1G16: return launch_fused_one<F_A1G16>(fa, s);
+    case F_A1G32: return launch_fused_one<F_A1G32>(fa, s);
+    case F_A1G64: return launch_fused_one<F_A1G64>(fa, s);
+    case F_A1G128: return launch_fused_one<F_A1G128>(fa, s);
   }
   return hipErrorInvalidValue;
 }

@@ -61,6 +61,9 @@ def prefill_order(T, H, I, E, k, bm=128, blocks_per_cu=2):
     classes below 2 blocks per slot, lpt 2)."""
     R = T * k
     if R < 48 * E:
+        te = min(R, E)
+        if T <= 32 and R <= te and te * (I // 64) >= 256:
+            return "fused decode kernel (one row per expert)"
         return "decode GEMV"
     cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
     slots = cus * blocks_per_cu

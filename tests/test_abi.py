@@ -158,7 +158,9 @@ def test_format_mask_split_bit():
         x.dn_fmt, x.dn_bits, x.dn_group = 2, 4, 16
     m = _lib.LIB.moe_format_mask(d, 2)
     # ids 4c+g: asym 3-bit c=4 g32 -> 17; asym 2-bit g16 -> 4; asym 4-bit g32 -> 1; e2m1 g16 -> 8
-    assert m == (1 << 17) | (1 << 4) | (1 << 1) | (1 << 8) | _lib.MASK_SPLIT_GU
+    assert m == (1 << 17) | (1 << 4) | (1 << 1) | (1 << 8) | _lib.MASK_SPLIT_GU | _lib.MASK_NO_FUSE
+    # without the split expert: no layout bits
+    assert _lib.LIB.moe_format_mask(ctypes.byref(d[1]), 1) == 1 << 8
 
 
 def test_ffn_rejects_small_workspace():
