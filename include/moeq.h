@@ -191,17 +191,27 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
  * 128; bit 31 (MOE_MASK_SPLIT_GU) is set when some expert has the split
  * gate/up layout, bit 30 (MOE_MASK_NO_FUSE) when some expert has the split
  * layout, outlier lists or a down format other than its gate/up format (the
- * fused decode kernel of moe_layer_forward then stays unused). The FFN entry
- * points take this mask (fmt_mask) and run one
+ * fused decode kernel of moe_layer_forward then stays unused), bit 29
+ * (MOE_MASK_OUTLIERS) when some matrix carries an outlier list (prefill-sized
+ * calls then copy each GEMM's input rows into a transposed workspace buffer
+ * that the outlier corrections read; without the bit, experts with outlier
+ * lists flag MOE_FLAG_FORMAT_NOT_LAUNCHED at prefill sizes and their outputs
+ * lack the corrections). The FFN entry points take this mask (fmt_mask) and
+ * run one
  * kernel per format (and role) in it; 0 means every supported format
  * (correct for any expert set, but each absent format still costs launches).
  * Experts whose format is missing from a non-zero mask are skipped and flag
  * MOE_FLAG_FORMAT_NOT_LAUNCHED. Host only. */
 #define MOE_MASK_SPLIT_GU (1u << 31)
 #define MOE_MASK_NO_FUSE (1u << 30)
+#define MOE_MASK_OUTLIERS (1u << 29)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 
-/* Workspace bytes the layer entry points need for these sizes. Host only. */
+/* Workspace bytes the layer entry points need for these sizes, with any
+ * fmt_mask (a mask without MOE_MASK_OUTLIERS needs less: at prefill sizes the
+ * transposed copy of the GEMM inputs, up to max(H, I) * (T*k + 31*min(T*k, E))
+ * fp16 values, is left out; moe_layer_forward_noalloc uses the smaller size).
+ * Host only. */
 size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq);
 
 /* Workspace bytes moe_route needs for these sizes (fp64 partial logits of
@@ -306,10 +316,12 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
  * caller buffer. Each GPU the library runs on holds one such array of
  * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) from the first call made with that GPU
  * current until the process ends; the call itself allocates nothing.
- * Sizes whose workspace (moe_workspace_size) exceeds it return
- * MOE_ERR_WORKSPACE before anything is enqueued: decode-size batches fit
- * (the Mixtral-shaped layer up to 314 tokens, the H=8192, I=16384 W4A8 one
- * up to 113).
+ * Sizes whose workspace exceeds it return MOE_ERR_WORKSPACE before
+ * anything is enqueued (the workspace moe_layer_forward needs with this
+ * fmt_mask: moe_workspace_size, less the transposed input copies when the
+ * mask lacks MOE_MASK_OUTLIERS). Decode-size batches fit: the
+ * Mixtral-shaped layer up to 314 tokens (191 with outlier lists), the
+ * H=8192, I=16384 W4A8 one up to 113.
  * Every call on a GPU shares that GPU's array, which keeps the last call's
  * contents: calls that overlap on one GPU (two streams, two host threads)
  * race and must be ordered by the caller. Nothing in the array needs to

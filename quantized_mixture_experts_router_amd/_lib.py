@@ -61,6 +61,7 @@ DESC_BYTES = 128
 PACK_SPLIT_GU = 1
 MASK_SPLIT_GU = 1 << 31
 MASK_NO_FUSE = 1 << 30
+MASK_OUTLIERS = 1 << 29
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {

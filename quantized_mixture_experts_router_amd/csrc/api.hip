@@ -7,7 +7,6 @@ using namespace moeq;
 
 namespace {
 
-constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -99,16 +98,33 @@ moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, 
 }
 
 inline uint32_t effective_mask(uint32_t m) {
-  return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU | kMaskNoFuse);
+  return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU | kMaskNoFuse | kMaskOutliers);
+}
+
+// the transposed copy of a prefill GEMM's input (K columns) for its outlier
+// corrections, when the layout has room for it (mask with the outlier bit)
+moe_status outlier_inputs(const f16* a, int R, int K, const int32_t* offsets, int E,
+                          const WsLayout& L, size_t at_off, void* ws, OutlierInputs& oi,
+                          hipStream_t s) {
+  oi = OutlierInputs{nullptr, 0, nullptr};
+  if (!L.rp) return MOE_OK;
+  f16* at = (f16*)ws_at(ws, at_off);
+  int32_t* poff = (int32_t*)ws_at(ws, L.poff);
+  MOE_TRY(launch_transpose_pad(a, R, K, offsets, E, at, L.rp, poff, s));
+  oi = OutlierInputs{at, L.rp, poff};
+  return MOE_OK;
 }
 
 moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const int32_t* offsets,
                        int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
                        uint32_t* flags, hipStream_t s) {
-  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), flags,
-                             T, H, I, E, k, (const f16*)ws_at(ws, L.a16),
+  const f16* a16 = (const f16*)ws_at(ws, L.a16);
+  OutlierInputs oi;
+  moe_status st = outlier_inputs(a16, T * k, H, offsets, E, L, L.at_gu, ws, oi, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), flags, T, H, I, E, k, a16,
                              aq != MOE_ACT_NONE ? (const float*)ws_at(ws, L.ascale) : nullptr,
-                             ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, s));
+                             ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, oi, s));
   return MOE_OK;
 }
 
@@ -125,19 +141,32 @@ moe_status run_down(const moe_packed_expert* experts, uint32_t mask, const int32
     ain = h16;
     sc = hs;
   }
+  OutlierInputs oi;
+  moe_status st = outlier_inputs(ain, R, I, offsets, E, L, L.at_dn, ws, oi, s);
+  if (st != MOE_OK) return st;
   MOE_TRY(launch_ffn_down(experts, offsets, effective_mask(mask), flags, T, H, I, E, k, ain, sc,
-                          yp, L.splits, L.decode, s));
+                          yp, L.splits, L.decode, oi, s));
   return MOE_OK;
 }
 
-moe_status check_ws(int T, int H, int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
-                    WsLayout& L) {
+// layout for a call with format mask `mask`; the transposed copies are
+// addressed with 32-bit byte offsets too
+moe_status layout_for(int T, int H, int I, int E, int k, moe_actq aq, uint32_t mask,
+                      WsLayout& L) {
+  L = ws_layout(T, H, I, E, k, aq, (effective_mask(mask) & kMaskOutliers) != 0);
+  if (L.rp && (uint64_t)(H > I ? H : I) * (uint64_t)L.rp * 2 > 0xFFFFFFFFull)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ws(int T, int H, int I, int E, int k, moe_actq aq, uint32_t mask, void* ws,
+                    size_t ws_bytes, WsLayout& L) {
   moe_status st = check_sizes(T, H, I, E, k);
   if (st != MOE_OK) return st;
   if (aq < MOE_ACT_NONE || aq > MOE_ACT_I8_XH) return MOE_ERR_INVALID_ARG;
   if (!ws) return MOE_ERR_INVALID_ARG;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  L = ws_layout(T, H, I, E, k, aq);
+  if ((st = layout_for(T, H, I, E, k, aq, mask, L)) != MOE_OK) return st;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
@@ -214,19 +243,19 @@ moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const
   return hip_status(launch_combine(yp, L.decode ? L.splits : 1, w, inv, T, H, k, out, out_dt, s));
 }
 
-moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, WsLayout& L) {
+moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, uint32_t fmt_mask,
+                             WsLayout& L) {
   moe_status st = check_sizes(T, H, I, E, k);
   if (st != MOE_OK) return st;
   if (aq < MOE_ACT_NONE || aq > MOE_ACT_I8_XH) return MOE_ERR_INVALID_ARG;
-  L = ws_layout(T, H, I, E, k, aq);
-  return MOE_OK;
+  return layout_for(T, H, I, E, k, aq, fmt_mask, L);
 }
 
 }  // namespace moeq
 
 extern "C" {
 
-int moe_version(void) { return 20000; }
+int moe_version(void) { return 20100; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -323,6 +352,7 @@ uint32_t moe_format_mask(const moe_packed_expert* descs, int E) {
     if (descs[e].layout & MOE_PACK_SPLIT_GU) m |= kMaskSplitGU;
     if ((descs[e].layout & MOE_PACK_SPLIT_GU) || descs[e].n_out_gu || descs[e].n_out_dn || a != b)
       m |= kMaskNoFuse;
+    if (descs[e].n_out_gu || descs[e].n_out_dn) m |= kMaskOutliers;
   }
   return m;
 }
@@ -436,7 +466,8 @@ moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_toke
                           int I, int E, int k, moe_actq aq, void* ws, size_t ws_bytes,
                           void* stream) {
   WsLayout L;
-  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  // the gather's regions do not depend on the format mask
+  moe_status st = check_ws(T, H, I, E, k, aq, 1u, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -449,7 +480,7 @@ moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
                            const int32_t* offsets, int T, int H, int I, int E, int k, moe_actq aq,
                            void* ws, size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, fmt_mask, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -461,7 +492,7 @@ moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
                         const int32_t* offsets, int T, int H, int I, int E, int k, moe_actq aq,
                         float* Y, void* ws, size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, fmt_mask, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T > 0 && !Y) return MOE_ERR_INVALID_ARG;
@@ -485,7 +516,7 @@ moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expe
                              int T, int H, int I, int E, int k, moe_actq aq, float* Y, void* ws,
                              size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, fmt_mask, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -514,7 +545,7 @@ moe_status moe_layer_forward(const void* x, moe_dtype xdt, const float* Wr, cons
                              int32_t* topk_ids,
                              float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   WsLayout L;
-  moe_status st = check_ws(T, H, I, E, k, aq, ws, ws_bytes, L);
+  moe_status st = check_ws(T, H, I, E, k, aq, fmt_mask, ws, ws_bytes, L);
   if (st != MOE_OK) return st;
   return layer_forward_ws(x, xdt, Wr, b, experts, fmt_mask, T, H, I, E, k, aq, out, out_dt,
                           topk_ids, topk_w, ws, L, nullptr, (hipStream_t)stream);

@@ -249,7 +249,90 @@ __global__ __launch_bounds__(kThreads) void combine_slices_kernel(const float* _
   }
 }
 
+
+// ===========================================================================
+// Transposed expert inputs for the prefill outlier corrections
+// ===========================================================================
+// Block (bx, by) copies padded columns [64 bx, +64) x input columns
+// [64 by, +64) through a 64 x 64 LDS tile: 16-byte loads along the input
+// rows, 16-byte stores along the output rows. Every block scans the E padded
+// segment sizes itself (E <= 256, one per thread); block (0, 0) stores them.
+// Within a 32-column group, slot 16 h + 4 g + i holds padded row 8 g + 4 h + i,
+// the order in which lane half h of a 32 x 32 MFMA holds its rows.
+__global__ __launch_bounds__(kThreads) void transpose_pad_kernel(
+    const f16* __restrict__ a, int R, int K, const int32_t* __restrict__ offsets, int E,
+    f16* __restrict__ at, int rp, int32_t* __restrict__ poff) {
+  static_assert(kMaxE <= kThreads, "one expert per thread");
+  __shared__ int s_po[kMaxE + 1], s_lo[kMaxE], s_cnt[kMaxE];
+  __shared__ int s_ws[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) f16 tile[64][72];  // [column][slot]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c32 = 0;
+  if (tid < E) {
+    const int o0 = offsets[tid], o1 = offsets[tid + 1];
+    const int lo = min(max(o0, 0), R);
+    const int hi = min(max(o1, lo), R);
+    s_lo[tid] = lo;
+    s_cnt[tid] = hi - lo;
+    c32 = (hi - lo + 31) & ~31;
+  }
+  int incl = c32;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_ws[wave] = incl;
+  __syncthreads();
+  int ex = incl - c32;
+  for (int w = 0; w < wave; ++w) ex += s_ws[w];
+  if (tid < E) s_po[tid] = ex;
+  if (tid == E - 1) s_po[E] = ex + c32;
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i <= E; i += kThreads) poff[i] = s_po[i];
+  const int total = s_po[E];
+  const int p0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y;
+  if (p0 >= total) return;  // block-uniform
+  for (int q = tid; q < 512; q += kThreads) {
+    const int j = q >> 3, c8 = q & 7;  // padded row p0 + j, input columns k0 + 8 c8
+    const int p = p0 + j;
+    if (p < total) {
+      int lo = 0, hi = E;  // s_po[lo] <= p < s_po[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_po[mid] <= p) lo = mid;
+        else hi = mid;
+      }
+      const int row = s_lo[lo] + min(p - s_po[lo], s_cnt[lo] - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(a + (size_t)row * K + k0 + 8 * c8);
+      const int rho = j & 31;
+      const int slot = (j & 32) | (16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        tile[8 * c8 + 2 * t][slot] = __builtin_bit_cast(f16, (uint16_t)(v[t] & 0xffffu));
+        tile[8 * c8 + 2 * t + 1][slot] = __builtin_bit_cast(f16, (uint16_t)(v[t] >> 16));
+      }
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < 512; q += kThreads) {
+    const int kk = q >> 3, c = q & 7;  // input column k0 + kk, slots [8 c, +8)
+    if (p0 + 8 * c < total)
+      *reinterpret_cast<u32x4*>(at + (size_t)(k0 + kk) * rp + p0 + 8 * c) =
+          *reinterpret_cast<const u32x4*>(&tile[kk][8 * c]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose_pad(const f16* a, int R, int K, const int32_t* offsets, int E,
+                                f16* at, int rp, int32_t* poff, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(rp / 64, K / 64), dim3(kThreads), 0, s, a, R, K,
+                     offsets, E, at, rp, poff);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine_slices(const float* yp, int ns, const float* w, const int32_t* inv,
                                  int T, int H, int k, void* out, int out_dt, hipStream_t s) {

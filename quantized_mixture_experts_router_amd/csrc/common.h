@@ -39,6 +39,8 @@ constexpr uint32_t kMaskSplitGU = MOE_MASK_SPLIT_GU;
 // bit of a format mask: some expert cannot take the fused decode kernel
 // (split gate/up, outlier lists, or a down format other than its gate/up's)
 constexpr uint32_t kMaskNoFuse = MOE_MASK_NO_FUSE;
+constexpr uint32_t kMaskOutliers = MOE_MASK_OUTLIERS;
+constexpr int kMaxE = 256;  // experts per layer
 static_assert(F_COUNT <= 30, "format mask bits");
 
 __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
@@ -150,6 +152,15 @@ struct WsLayout {
                    // before the down projection writes it)
   size_t pscratch; // permutation scratch; aliases yp too (the top-k has read the
                    // partial logits before the permutation runs)
+  size_t poff;     // int32 [E+1] padded segment starts of the transposed inputs
+  // Transposed expert inputs for the prefill outlier corrections (prefill
+  // sizes with outliers only): f16 [K][rp], column p of expert e's padded
+  // segment at poff[e] + p. The gate/up copy (K = H) takes yp's place when
+  // it fits (yp is written only by the down projection); the down copy
+  // (K = I) takes the fp32 h of MOE_ACT_I8_XH when it fits (free once its
+  // int8 codes are made), else both go to a region at the end.
+  size_t at_gu, at_dn;
+  int rp;          // row pitch of the transposed copies, 0 when there are none
   size_t total;
   int splits;
   bool decode;
@@ -261,7 +272,16 @@ struct PermutePlan {
 };
 PermutePlan permute_plan(int R, int E);
 
-inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
+// Columns of the transposed input copies: every expert's segment padded to
+// a multiple of 32 rows, rounded up to 64.
+inline size_t outlier_pitch(size_t R, int E) {
+  const size_t ne = R < (size_t)E ? R : (size_t)E;
+  return (R + 31 * ne + 63) / 64 * 64;
+}
+
+// outl: room for the transposed input copies of prefill outlier corrections.
+// Every offset but at_gu/at_dn and total is the same either way.
+inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq, bool outl = true) {
   WsLayout L;
   size_t R = (size_t)T * k;
   size_t o = 0;
@@ -278,6 +298,7 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   L.h = take(R * I * (aq == MOE_ACT_I8_XH ? 4 : 2));
   L.h16 = take(aq == MOE_ACT_I8_XH ? R * I * 2 : 0);
   L.hscale = take(R * 4);
+  L.poff = take((size_t)(E + 1) * 4);
   L.splits = down_splits(T, H, I, E, k);
   L.decode = use_decode_path(T, k, E);
   const FusedPlan fp = fused_plan(T, H, I, E, k, aq);
@@ -290,6 +311,19 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq) {
   L.yp = take(big);
   L.rpart = L.yp;
   L.pscratch = L.yp;
+  L.at_gu = L.at_dn = 0;
+  L.rp = 0;
+  if (outl && !L.decode && R > 0) {
+    const size_t rp = outlier_pitch(R, E);
+    const size_t gu = (size_t)H * rp * 2, dn = (size_t)I * rp * 2;
+    const bool gu_in = gu <= big;
+    const bool dn_in = aq == MOE_ACT_I8_XH && dn <= R * I * 4;
+    const size_t extra = (gu_in ? 0 : gu) > (dn_in ? 0 : dn) ? gu : (dn_in ? 0 : dn);
+    const size_t at = take(extra);
+    L.at_gu = gu_in ? L.yp : at;
+    L.at_dn = dn_in ? L.h : at;
+    L.rp = (int)rp;
+  }
   L.total = o;
   return L;
 }
@@ -323,14 +357,29 @@ hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* 
                                  hipStream_t s);
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
                                hipStream_t s);
+// The transposed copy of a prefill GEMM's input rows that its outlier
+// corrections read (at == nullptr: none made; experts with outlier lists
+// then flag MOE_FLAG_FORMAT_NOT_LAUNCHED at prefill sizes).
+struct OutlierInputs {
+  const f16* at;        // [K][rp]
+  int rp;
+  const int32_t* poff;  // [E+1] padded segment starts
+};
+// at[k][poff[e] + p] = a[lo_e + min(p, count_e - 1)][k] for p < the segment's
+// count rounded up to 32, each 32-column group stored in the order the MFMA
+// accumulators hold rows: slot 16 h + 4 g + i holds row 8 g + 4 h + i.
+// Segments are the clamped [offsets[e], offsets[e+1]) of the GEMMs; poff is
+// written too.
+hipError_t launch_transpose_pad(const f16* a, int R, int K, const int32_t* offsets, int E,
+                                f16* at, int rp, int32_t* poff, hipStream_t s);
 hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
                               uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
                               int k, const f16* a16, const float* ascale, void* h, int h_f32,
-                              bool decode, hipStream_t s);
+                              bool decode, const OutlierInputs& oi, hipStream_t s);
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
                            const f16* ain, const float* ascale, float* yp, int splits,
-                           bool decode, hipStream_t s);
+                           bool decode, const OutlierInputs& oi, hipStream_t s);
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);
@@ -361,6 +410,7 @@ moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const
                             int I, int E, int k, moe_actq aq, void* out, moe_dtype out_dt,
                             int32_t* topk_ids, float* topk_w, void* ws, const WsLayout& L,
                             uint32_t* flags, hipStream_t s);
-moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, WsLayout& L);
+moe_status check_layer_sizes(int T, int H, int I, int E, int k, moe_actq aq, uint32_t fmt_mask,
+                             WsLayout& L);
 
 }  // namespace moeq

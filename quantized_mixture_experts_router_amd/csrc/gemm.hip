@@ -49,8 +49,11 @@ hipError_t launch_all(int role, const FfnArgs& a, bool decode, hipStream_t s) {
 hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
                               uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
                               int k, const f16* a16, const float* ascale, void* h, int h_f32,
-                              bool decode, hipStream_t s) {
+                              bool decode, const OutlierInputs& oi, hipStream_t s) {
   FfnArgs a;
+  a.at = oi.at;
+  a.rp = oi.rp;
+  a.poff = oi.poff;
   a.experts = experts;
   a.offsets = offsets;
   a.flags = flags;
@@ -138,8 +141,11 @@ hipError_t launch_ffn_fused(const moe_packed_expert* experts, const int32_t* off
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
                            const f16* ain, const float* ascale, float* yp, int splits,
-                           bool decode, hipStream_t s) {
+                           bool decode, const OutlierInputs& oi, hipStream_t s) {
   FfnArgs a;
+  a.at = oi.at;
+  a.rp = oi.rp;
+  a.poff = oi.poff;
   a.experts = experts;
   a.offsets = offsets;
   a.flags = flags;

@@ -57,6 +57,10 @@ struct FfnArgs {
   int R;
   int splits;
   int lpt;        // prefill task order: expert-major (0), longest first in 2 (1) or 4 (2) classes
+  // prefill outlier corrections: the transposed inputs (see OutlierInputs)
+  const f16* at = nullptr;
+  int rp = 0;
+  const int32_t* poff = nullptr;
 };
 
 // Launches the grouped GEMM of format `fid` in role `role` (one unit per
@@ -183,18 +187,6 @@ __device__ inline int outlier_row(int N, int unit, int t, int n) {
   if constexpr (ROLE == R_GU) return (t ? N : 0) + 32 * unit + n;
   else return (ROLE == R_UP ? N : 0) + 64 * unit + 32 * t + n;
 }
-// sum over list row lr of delta * a_row[k]: the weights the outliers replace,
-// corrected on one token row (a_row: its expert inputs as the GEMM used them)
-__device__ inline float outlier_dot(const uint32_t* rp, const OutEntry* en, int lr,
-                                    const f16* a_row) {
-  float s = 0.f;
-  for (uint32_t e = rp[lr], e1 = rp[lr + 1]; e < e1; ++e) {
-    const OutEntry o = en[e];
-    s += o.delta * (float)a_row[o.k];
-  }
-  return s;
-}
-
 // Task lookup over the experts of format `fid` (decode): tasks of expert e
 // = ceil(count_e / BM) * NB, expert-major, then n-tile, then m-tile.
 // The first block also flags experts with rows whose format is not in the
@@ -574,6 +566,12 @@ __device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t sof
 // ===========================================================================
 // Decode family
 // ===========================================================================
+// decode: outlier entries per batch (three keep the 4-bit kernels at three
+// wavefronts per SIMD)
+#ifndef MOEQ_DEC_OUTB
+#define MOEQ_DEC_OUTB 3
+#endif
+
 template <class F, int ROLE>
 __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
   constexpr bool GU = ROLE == R_GU;
@@ -690,39 +688,80 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const int RPW = 16 / ksw;
   const int w0 = grp * ksw;
   bool over = false;
-  // outliers of the matrix: added once, by the K split that starts at 0
-  const uint32_t* orp;
-  const OutEntry* oen;
-  const bool has_out = role_outliers<ROLE>(ex, orp, oen) && split == 0;
-  const int ol0 = outlier_row<ROLE>(a.N, rg, 0, n), ol1 = outlier_row<ROLE>(a.N, rg, 1, n);
+  // this wavefront's rows: registers r of its K-split share that hold rows
+  auto mine = [&](int r) { return r / RPW == ks && live(r); };
+  float v0[16], v1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (r / RPW != ks || !live(r)) continue;
-    float v0 = acc0[r], v1 = acc1[r];
-    if (ksw > 1) {
-      v0 = 0.f;
-      v1 = 0.f;
-      for (int w = 0; w < ksw; ++w) {
-        v0 += red[(((w0 + w) * 2 + 0) * 16 + r) * 64 + lane];
-        v1 += red[(((w0 + w) * 2 + 1) * 16 + r) * 64 + lane];
+    v0[r] = acc0[r];
+    v1[r] = acc1[r];
+    if (!mine(r) || ksw == 1) continue;
+    v0[r] = 0.f;
+    v1[r] = 0.f;
+    for (int w = 0; w < ksw; ++w) {
+      v0[r] += red[(((w0 + w) * 2 + 0) * 16 + r) * 64 + lane];
+      v1[r] += red[(((w0 + w) * 2 + 1) * 16 + r) * 64 + lane];
+    }
+  }
+  // Outliers of the matrix, added once (by the K split that starts at 0):
+  // per output column, each listed weight's correction times the rows'
+  // inputs at its column. Entries go four at a time: their loads, then all
+  // the rows' input loads of the four, then the products, so a list costs
+  // a quarter as many memory round trips as its length.
+  const uint32_t* orp;
+  const OutEntry* oen;
+  if (role_outliers<ROLE>(ex, orp, oen) && split == 0) {
+    constexpr int B = MOEQ_DEC_OUTB;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int lr = outlier_row<ROLE>(a.N, rg, tt, n);
+      const int b0 = (int)orp[lr], c = (int)orp[lr + 1] - b0;
+      const OutEntry* en = oen + b0;
+      for (int j = 0; j < c; j += B) {
+        uint32_t kk[B];
+        float dd[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int e = min(j + u, c - 1);
+          kk[u] = en[e].k;
+          dd[u] = en[e].delta;
+        }
+        f16 x[B][16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!mine(r)) continue;
+          const uint32_t ro = (uint32_t)(t.row0 + min(acc_row(r, lane), t.mcount - 1)) * a.K;
+#pragma unroll
+          for (int u = 0; u < B; ++u)
+            x[u][r] = __builtin_bit_cast(f16, bload<uint16_t>(rA, (ro + kk[u]) * 2, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          if (j + u >= c) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (!mine(r)) continue;
+            if (tt) v1[r] = fmaf(dd[u], (float)x[u][r], v1[r]);
+            else v0[r] = fmaf(dd[u], (float)x[u][r], v0[r]);
+          }
+        }
       }
     }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (!mine(r)) continue;
     const int i = acc_row(r, lane);
     if (i < t.mcount) {
       const int row = t.row0 + i;
-      if (has_out) {
-        const f16* arow = a.a + (size_t)row * a.K;
-        v0 += outlier_dot(orp, oen, ol0, arow);
-        v1 += outlier_dot(orp, oen, ol1, arow);
-      }
       if constexpr (ROLE == R_GU) {
-        over |= store_gu(a, row, 32 * rg + n, v0, v1);
+        over |= store_gu(a, row, 32 * rg + n, v0[r], v1[r]);
       } else if constexpr (ROLE == R_DN) {
-        store_dn(a, split, row, 64 * rg + n, v0);
-        store_dn(a, split, row, 64 * rg + 32 + n, v1);
+        store_dn(a, split, row, 64 * rg + n, v0[r]);
+        store_dn(a, split, row, 64 * rg + 32 + n, v1[r]);
       } else {
-        over |= store_split<ROLE>(a, row, 64 * rg + n, v0);
-        over |= store_split<ROLE>(a, row, 64 * rg + 32 + n, v1);
+        over |= store_split<ROLE>(a, row, 64 * rg + n, v0[r]);
+        over |= store_split<ROLE>(a, row, 64 * rg + 32 + n, v1[r]);
       }
     }
   }
@@ -866,6 +905,61 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
       acc[mi][0] = f32x16{};
       acc[mi][1] = f32x16{};
     }
+    // Outliers of the matrix, before the K loop (the accumulators start from
+    // the corrections, while few other registers are live): each listed
+    // weight's correction (delta = its fp16 value - the decoded weight)
+    // times the token rows' inputs at its column. The inputs come from the transposed copy, where the block's
+    // rows of one column are contiguous and in accumulator order: lane
+    // (n, kh) reads its 16 rows of sub-tile mi as 32 bytes, so one entry
+    // costs 2 AMT 16-byte loads that touch two cache lines per lane pair
+    // (row-major inputs cost one line per row). Each output column's list
+    // is walked with the next entry loaded while the current one's inputs
+    // are in flight. Rows past the segment read the last row's inputs, as
+    // the token tile does.
+    {
+      const uint32_t* orp;
+      const OutEntry* oen;
+      if (on && role_outliers<ROLE>(ex, orp, oen)) {
+        if (!a.at) {
+          if (tid == 0 && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FORMAT_NOT_LAUNCHED);
+        } else {
+          const int lo = min(max(a.offsets[t.e], 0), a.R);
+          const rsrc_t rT = make_rsrc(a.at, (uint32_t)((size_t)a.K * a.rp * 2));
+          const uint32_t pb = (uint32_t)(a.poff[t.e] + (t.row0 - lo) + 16 * kh) * 2;
+          const uint32_t rowT = (uint32_t)a.rp * 2;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int lr = outlier_row<ROLE>(a.N, unit, tt, n);
+            const int b0 = (int)orp[lr], c = (int)orp[lr + 1] - b0;
+            // the entries' columns and deltas as separate scalars, so they
+            // stay in registers
+            const OutEntry* en = oen + b0;
+            uint32_t qk = c > 0 ? en[0].k : 0u;
+            float qd = c > 0 ? en[0].delta : 0.f;
+            for (int j = 0; j < c; ++j) {
+              f16x8 v[AMT][2];
+#pragma unroll
+              for (int mi = 0; mi < AMT; ++mi) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                  v[mi][hf] = bload<f16x8>(rT, qk * rowT + pb, (uint32_t)(32 * mi + 8 * hf) * 2);
+              }
+              const bool more = j + 1 < c;
+              const uint32_t nk = more ? en[j + 1].k : qk;
+              const float nd = more ? en[j + 1].delta : qd;
+#pragma unroll
+              for (int mi = 0; mi < AMT; ++mi) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  acc[mi][tt][r] = fmaf(qd, (float)v[mi][r >> 3][r & 7], acc[mi][tt][r]);
+              }
+              qk = nk;
+              qd = nd;
+            }
+          }
+        }
+      }
+    }
     // fragment (mi, step s) of lane (n, kh): row mi*32 + n, logical chunk
     // kh*SPAN/8 + s; swz(mi*32 + n) == swz(n)
     auto afrag = [&](const uint8_t* buf, int mi, int s) {
@@ -1003,38 +1097,6 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
     static_assert(kPW <= 4 && 2 * kStageB <= TILEB, "epilogue staging exceeds the token buffers");
     __syncthreads();
     if (!on) return;
-    // outliers of the matrix: each listed weight's correction times the
-    // token rows' inputs at its column, read through the bounded token
-    // descriptor (rows past the segment are not stored; past the buffer they
-    // read 0). The row offsets pass through an empty asm inside the loop, so
-    // the compiler recomputes them per entry instead of holding 64 of them
-    // live beside the accumulators.
-    {
-      const uint32_t* orp;
-      const OutEntry* oen;
-      if (role_outliers<ROLE>(ex, orp, oen)) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int lr = outlier_row<ROLE>(a.N, unit, tt, n);
-          for (uint32_t e = orp[lr], e1 = orp[lr + 1]; e < e1; ++e) {
-            const OutEntry o = oen[e];
-            uint32_t vb = ((uint32_t)(t.row0 + 4 * kh) * a.K + o.k) * 2;
-            uint32_t rowb = (uint32_t)a.K * 2;
-            asm volatile("" : "+v"(vb), "+s"(rowb));
-#pragma unroll
-            for (int mi = 0; mi < AMT; ++mi) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                // token row mi*32 + acc_row(r, lane) = (4 kh) + this
-                const uint32_t so = (uint32_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * rowb;
-                const f16 v = __builtin_bit_cast(f16, bload<uint16_t>(rA, vb, so));
-                acc[mi][tt][r] += o.delta * (float)v;
-              }
-            }
-          }
-        }
-      }
-    }
     uint8_t* stg = (wave >> 1 ? lds1 : lds0) + (wave & 1) * kStageB;
     bool over = false;  // an fp16 h out of range (rows past the segment
                         // repeat its last row, so they add no false report)

@@ -54,7 +54,7 @@ moe_status moe_layer_forward_noalloc(const void* x, moe_dtype xdt, const float* 
                                      moe_dtype out_dt, int32_t* topk_ids, float* topk_w,
                                      uint32_t* flags, void* stream) {
   WsLayout L;
-  moe_status st = check_layer_sizes(T, H, I, E, k, aq, L);
+  moe_status st = check_layer_sizes(T, H, I, E, k, aq, fmt_mask, L);
   if (st != MOE_OK) return st;
   if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   if (flags && ((uintptr_t)flags % 4) != 0) return MOE_ERR_ALIGNMENT;

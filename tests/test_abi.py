@@ -161,6 +161,14 @@ def test_format_mask_split_bit():
     assert m == (1 << 17) | (1 << 4) | (1 << 1) | (1 << 8) | _lib.MASK_SPLIT_GU | _lib.MASK_NO_FUSE
     # without the split expert: no layout bits
     assert _lib.LIB.moe_format_mask(ctypes.byref(d[1]), 1) == 1 << 8
+    # an outlier list (either group) sets the outlier bit and keeps the
+    # fused decode kernel away
+    d[1].n_out_dn = 3
+    assert _lib.LIB.moe_format_mask(ctypes.byref(d[1]), 1) == \
+        (1 << 8) | _lib.MASK_OUTLIERS | _lib.MASK_NO_FUSE
+    d[1].n_out_dn, d[1].n_out_gu = 0, 7
+    assert _lib.LIB.moe_format_mask(ctypes.byref(d[1]), 1) == \
+        (1 << 8) | _lib.MASK_OUTLIERS | _lib.MASK_NO_FUSE
 
 
 def test_ffn_rejects_small_workspace():

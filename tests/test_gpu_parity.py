@@ -718,6 +718,41 @@ def test_layer_parity_matrix_formats_and_outliers(moeq, name, T, H, I, E, k, kin
         assert err0.max() > 4 * err.max()
 
 
+@pytest.mark.parametrize("T", [40, 600])
+def test_outliers_need_mask_bit_at_prefill(moeq, T):
+    """Experts with outlier lists and a mask without MOE_MASK_OUTLIERS: at
+    prefill sizes the transposed input copy is not made, the flag says so and
+    the corrections are missing; decode sizes need no copy and stay exact.
+    Mask 0 stands for every bit and matches the oracle."""
+    from dataclasses import replace
+    cfg = synth.scaled_config("mixtral", T=T, H=512, I=512, E=8, k=2, weight_mode="quantize")
+    cfg = replace(cfg, matrix_fmts=_fmt_plan("mixed", 8), weight_outlier_frac=0.005)
+    prefill = "GEMV" not in prefill_order(T, cfg.H, cfg.I, cfg.E, cfg.k)
+    _say(f"[outlier bit] T={T} prefill={prefill}")
+    wl = Workload(cfg)
+    full = wl.packed.fmt_mask
+    assert full & moeq.MASK_OUTLIERS
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, None, wl.expert, cfg.E, cfg.k,
+                           act=cfg.act)
+    ok = ~ref["flagged"]
+    try:
+        for mask, bit in ((0, True), (full & ~moeq.MASK_OUTLIERS, False)):
+            wl.packed.fmt_mask = mask
+            ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+            out, _, _ = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+            torch.cuda.synchronize()
+            flags = moeq.read_flags(ws)
+            err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok]).max()
+            _say(f"    mask bit {bit}: flags {flags}, max row rel-L2 {err:.3e}")
+            if bit or not prefill:
+                assert flags == 0 and err <= tolerance(cfg), (flags, err)
+            else:
+                assert flags == moeq.FLAG_FORMAT_NOT_LAUNCHED
+                assert err > tolerance(cfg)
+    finally:
+        wl.packed.fmt_mask = full
+
+
 @pytest.mark.parametrize("T", [1, 3, 8])
 def test_layer_parity_int8_x_fused(moeq, T):
     """int8 x only (MOE_ACT_I8_X): one or three tokens take the fused decode
