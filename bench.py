@@ -94,7 +94,8 @@ def payload_bytes(cfg, e):
 def kernel_names(cfg, gu=True):
     import synth
     fmts = sorted({synth.expert_format(cfg, e) for e in range(cfg.E)})
-    return [f"ffn_prefill_kernel<moeq::Fmt<{f}, {b}, {g}>, {'true' if gu else 'false'}, *>"
+    # template arguments: block format, role (0 fused gate/up, 1 down), four-class order
+    return [f"ffn_prefill_kernel<moeq::Fmt<{f}, {b}, {g}>, {0 if gu else 1}, *>"
             for f, b, g in fmts]
 
 
