@@ -370,6 +370,42 @@ class Bench:
         log(f"[bench] {cfg.name} with 0.05% outliers: prefill {res['prefill_ms']:.3f} ms")
         return res
 
+    def int8_gemm(self, wl, T):
+        """The opt-in int8 MFMA GEMMs (MOE_MASK_INT8_GEMM) against the default
+        fp16 kernels on the same W4A8 batch: whole-layer calls
+        (moe_layer_forward), args.steps timed after args.warmup."""
+        import numpy as np
+        import quantized_mixture_experts_router_amd as moeq
+        torch, args, cfg = self.torch, self.args, wl.cfg
+        x = wl.x[:T].contiguous()
+        ws = moeq.workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act, self.dev)
+        full = wl.packed.fmt_mask
+        res = {}
+        try:
+            outs = {}
+            for label, mask in (("fp16_kernels", full), ("int8_kernels", full | moeq.MASK_INT8_GEMM)):
+                wl.packed.fmt_mask = mask
+                for _ in range(args.warmup):
+                    moeq.layer_forward(x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    o, _, _ = moeq.layer_forward(x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1e3 / args.steps
+                outs[label] = o.float().cpu().numpy()
+                res[label] = {"layer_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                              "flags": moeq.read_flags(ws)}
+        finally:
+            wl.packed.fmt_mask = full
+        a, b = outs["int8_kernels"], outs["fp16_kernels"]
+        res["max_row_rel_l2_between"] = float(np.max(np.linalg.norm(a - b, axis=1) /
+                                                     np.maximum(np.linalg.norm(b, axis=1), 1e-30)))
+        log(f"[bench] {cfg.name} T={T} whole layer: fp16 kernels {res['fp16_kernels']['layer_ms']:.3f} ms, "
+            f"int8 kernels {res['int8_kernels']['layer_ms']:.3f} ms "
+            f"(outputs differ by {res['max_row_rel_l2_between']:.2e})")
+        return res
+
     def tiers(self, wl, T, ids_own):
         """Expert-aware precision from a routing profile of T held-out tokens:
         the tier plan within the byte budget of the workload's bias-ranked hot
@@ -613,6 +649,8 @@ def main():
                 outs[Td] = (od.cpu().numpy(), idd.cpu().numpy())
         if extras and name == "mixtral" and not args.no_prefill and flush is not None:
             ent["outliers"] = bench.outliers(wl, cfg.T, flush)
+        if extras and name == "w4a8" and not args.no_prefill:
+            ent["int8_gemm"] = bench.int8_gemm(wl, cfg.T)
         if not args.no_cpu_baseline and outs:
             if name == HEADLINE:
                 cpu_headline, par = headline_oracle_sample(cfg, wl, outs)

@@ -205,6 +205,15 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
 #define MOE_MASK_SPLIT_GU (1u << 31)
 #define MOE_MASK_NO_FUSE (1u << 30)
 #define MOE_MASK_OUTLIERS (1u << 29)
+/* Bit 28 (MOE_MASK_INT8_GEMM), never set by moe_format_mask: a caller that
+ * sets it asks moe_layer_forward, moe_layer_forward_noalloc and
+ * moe_grouped_ffn_q to run the prefill GEMMs of asymmetric 4-bit group-128
+ * experts on the int8 matrix cores when the activations are int8 (integer
+ * group sums scaled into fp32 per group: the same result up to fp32
+ * rounding), unless some expert needs the split roles or outlier lists.
+ * Measured slower than the default fp16 kernels on this GPU; kept for
+ * comparison. The phase entry points (moe_ffn_*) ignore it. */
+#define MOE_MASK_INT8_GEMM (1u << 28)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 
 /* Workspace bytes the layer entry points need for these sizes, with any

@@ -90,15 +90,32 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 inline char* ws_at(void* ws, size_t off) { return (char*)ws + off; }
 
 // phases of the grouped FFN (workspace already validated)
-moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, int H, int k,
-                      moe_actq aq, const WsLayout& L, void* ws, hipStream_t s) {
-  MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
-                          (float*)ws_at(ws, L.ascale), (uint32_t*)ws_at(ws, L.flags), s));
-  return MOE_OK;
-}
-
 inline uint32_t effective_mask(uint32_t m) {
   return m ? m : (((1u << F_COUNT) - 1u) | kMaskSplitGU | kMaskNoFuse | kMaskOutliers);
+}
+
+// The int8 prefill GEMMs take the W4A8 format (4-bit, groups of 128) when
+// the caller asks for them (MOE_MASK_INT8_GEMM), the layout holds their
+// operands (int8 activations at prefill sizes) and no expert needs the split
+// roles or outlier corrections; the fp16-held codes are still made when
+// another format is present.
+inline bool use_i8(const WsLayout& L, uint32_t m) {
+  return L.i8 && (m & kMaskInt8) && (m & kI8Formats) && !(m & (kMaskSplitGU | kMaskOutliers));
+}
+inline bool need16(const WsLayout& L, uint32_t m) {
+  return !use_i8(L, m) || (m & ((1u << F_COUNT) - 1u) & ~kI8Formats);
+}
+
+// the expert inputs: fp16 (or fp16-held int8 codes) when need16, the int8
+// GEMMs' operands when i8
+moe_status run_gather(const void* x, moe_dtype xdt, const int32_t* perm, int T, int H, int k,
+                      moe_actq aq, const WsLayout& L, void* ws, bool want16, bool i8,
+                      uint32_t* flags, hipStream_t s) {
+  MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE,
+                          want16 ? (f16*)ws_at(ws, L.a16) : nullptr, (float*)ws_at(ws, L.ascale),
+                          i8 ? (int8_t*)ws_at(ws, L.a8) : nullptr,
+                          i8 ? (float*)ws_at(ws, L.asum) : nullptr, flags, s));
+  return MOE_OK;
 }
 
 // the transposed copy of a prefill GEMM's input (K columns) for its outlier
@@ -122,9 +139,13 @@ moe_status run_gate_up(const moe_packed_expert* experts, uint32_t mask, const in
   OutlierInputs oi;
   moe_status st = outlier_inputs(a16, T * k, H, offsets, E, L, L.at_gu, ws, oi, s);
   if (st != MOE_OK) return st;
-  MOE_TRY(launch_ffn_gate_up(experts, offsets, effective_mask(mask), flags, T, H, I, E, k, a16,
+  const uint32_t m = effective_mask(mask);
+  const I8Inputs i8 = use_i8(L, m) ? I8Inputs{(const int8_t*)ws_at(ws, L.a8),
+                                               (const float*)ws_at(ws, L.asum)}
+                                    : I8Inputs{nullptr, nullptr};
+  MOE_TRY(launch_ffn_gate_up(experts, offsets, m, flags, T, H, I, E, k, a16,
                              aq != MOE_ACT_NONE ? (const float*)ws_at(ws, L.ascale) : nullptr,
-                             ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, oi, s));
+                             ws_at(ws, L.h), aq == MOE_ACT_I8_XH, L.decode, oi, i8, s));
   return MOE_OK;
 }
 
@@ -132,20 +153,30 @@ moe_status run_down(const moe_packed_expert* experts, uint32_t mask, const int32
                     int T, int H, int I, int E, int k, moe_actq aq, const WsLayout& L, void* ws,
                     uint32_t* flags, float* yp, hipStream_t s) {
   const int R = T * k;
+  const uint32_t m = effective_mask(mask);
   const f16* ain = (const f16*)ws_at(ws, L.h);
   const float* sc = nullptr;
+  I8Inputs i8{nullptr, nullptr};
   if (aq == MOE_ACT_I8_XH) {
+    // int8 codes of h: fp16-held for the fp16 kernels, bytes and sums for
+    // the int8 ones
+    const bool q8 = use_i8(L, m);
     f16* h16 = (f16*)ws_at(ws, L.h16);
     float* hs = (float*)ws_at(ws, L.hscale);
-    MOE_TRY(launch_quant_rows_f32((const float*)ws_at(ws, L.h), R, I, h16, hs, s));
+    int8_t* h8 = (int8_t*)ws_at(ws, L.h8);
+    float* hsum = (float*)ws_at(ws, L.hsum);
+    MOE_TRY(launch_quant_rows_f32((const float*)ws_at(ws, L.h), R, I,
+                                  need16(L, m) ? h16 : nullptr, hs, q8 ? h8 : nullptr,
+                                  q8 ? hsum : nullptr, s));
     ain = h16;
     sc = hs;
+    if (q8) i8 = I8Inputs{h8, hsum};
   }
   OutlierInputs oi;
   moe_status st = outlier_inputs(ain, R, I, offsets, E, L, L.at_dn, ws, oi, s);
   if (st != MOE_OK) return st;
-  MOE_TRY(launch_ffn_down(experts, offsets, effective_mask(mask), flags, T, H, I, E, k, ain, sc,
-                          yp, L.splits, L.decode, oi, s));
+  MOE_TRY(launch_ffn_down(experts, offsets, m, flags, T, H, I, E, k, ain, sc, yp, L.splits,
+                          L.decode, oi, i8, s));
   return MOE_OK;
 }
 
@@ -217,8 +248,10 @@ moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const
     MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
     MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags,
                            ws_at(ws, L.pscratch), s));
-    MOE_TRY(launch_gather_a(x, xdt, perm, T, k, H, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
-                            (float*)ws_at(ws, L.ascale), flags, s));
+    const uint32_t m = effective_mask(fmt_mask);
+    const moe_status sg = run_gather(x, xdt, perm, T, H, k, aq, L, ws, need16(L, m), use_i8(L, m),
+                                     flags, s);
+    if (sg != MOE_OK) return sg;
   }
   const FusedPlan fp = fused_plan(T, H, I, E, k, aq);
   const uint32_t mask = effective_mask(fmt_mask);
@@ -473,7 +506,8 @@ moe_status moe_ffn_gather(const void* x, moe_dtype xdt, const int32_t* perm_toke
   if (T == 0) return MOE_OK;
   if (!x || !perm_token) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16)) return MOE_ERR_ALIGNMENT;
-  return run_gather(x, xdt, perm_token, T, H, k, aq, L, ws, (hipStream_t)stream);
+  return run_gather(x, xdt, perm_token, T, H, k, aq, L, ws, true, false,
+                    (uint32_t*)ws_at(ws, L.flags), (hipStream_t)stream);
 }
 
 moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
@@ -484,7 +518,9 @@ moe_status moe_ffn_gate_up(const moe_packed_expert* experts, uint32_t fmt_mask,
   if (st != MOE_OK) return st;
   if ((st = check_experts(experts, offsets)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  return run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+  // the phase entry points keep the fp16 kernels (the gather made no int8
+  // operands for them)
+  return run_gate_up(experts, fmt_mask & ~kMaskInt8, offsets, T, H, I, E, k, aq, L, ws,
                      (uint32_t*)ws_at(ws, L.flags), (hipStream_t)stream);
 }
 
@@ -502,12 +538,12 @@ moe_status moe_ffn_down(const moe_packed_expert* experts, uint32_t fmt_mask,
   const size_t n = (size_t)T * k * H;
   if (L.decode && L.splits > 1) {
     float* yp = (float*)ws_at(ws, L.yp);
-    st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+    st = run_down(experts, fmt_mask & ~kMaskInt8, offsets, T, H, I, E, k, aq, L, ws,
                   (uint32_t*)ws_at(ws, L.flags), yp, s);
     if (st != MOE_OK) return st;
     return hip_status(launch_reduce_splits(yp, L.splits, n, Y, s));
   }
-  return run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws,
+  return run_down(experts, fmt_mask & ~kMaskInt8, offsets, T, H, I, E, k, aq, L, ws,
                   (uint32_t*)ws_at(ws, L.flags), Y, s);
 }
 
@@ -522,11 +558,21 @@ moe_status moe_grouped_ffn_q(const void* x, moe_dtype xdt, const moe_packed_expe
   if (xdt != MOE_F32 && xdt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm_token || !Y) return MOE_ERR_INVALID_ARG;
-  st = moe_ffn_gather(x, xdt, perm_token, T, H, I, E, k, aq, ws, ws_bytes, stream);
+  if (!aligned(x, 16) || !aligned(Y, 16)) return MOE_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flags = (uint32_t*)ws_at(ws, L.flags);
+  const uint32_t m = effective_mask(fmt_mask);
+  st = run_gather(x, xdt, perm_token, T, H, k, aq, L, ws, need16(L, m), use_i8(L, m), flags, s);
   if (st != MOE_OK) return st;
-  st = moe_ffn_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, ws, ws_bytes, stream);
+  st = run_gate_up(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, s);
   if (st != MOE_OK) return st;
-  return moe_ffn_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, Y, ws, ws_bytes, stream);
+  if (L.decode && L.splits > 1) {
+    float* yp = (float*)ws_at(ws, L.yp);
+    st = run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, yp, s);
+    if (st != MOE_OK) return st;
+    return hip_status(launch_reduce_splits(yp, L.splits, (size_t)T * k * H, Y, s));
+  }
+  return run_down(experts, fmt_mask, offsets, T, H, I, E, k, aq, L, ws, flags, Y, s);
 }
 
 moe_status moe_combine(const float* Y, const float* topk_w, const int32_t* inv, int T, int H,

@@ -34,22 +34,29 @@ __device__ inline float row_absmax(const void* x, int dt, size_t base, int cols)
   return r;
 }
 
-// one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes;
-// each thread moves 8 columns at a time (H % 8 == 0, x 16-byte aligned)
+// one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes
+// held as fp16 (a16) and/or as bytes with their 64-column sums (a8, asum:
+// the int8 GEMM's operands; R rows); each thread moves 8 columns at a time
+// (H % 8 == 0, x 16-byte aligned)
 __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restrict__ x, int dt,
                                                           const int32_t* __restrict__ perm, int T,
                                                           int H,
                                                           int quant, f16* __restrict__ a16,
                                                           float* __restrict__ ascale,
+                                                          int8_t* __restrict__ a8,
+                                                          float* __restrict__ asum, int R,
                                                           uint32_t* __restrict__ flags) {
   __shared__ float s_red[kThreads / 64];
   const int r = blockIdx.x;
   const int t = perm[r];
-  f16* dst = a16 + (size_t)r * H;
+  f16* dst = a16 ? a16 + (size_t)r * H : nullptr;
   if ((unsigned)t >= (unsigned)T) {
     // a slot the permutation left unused (dropped assignments): never read x
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) store8_f16(dst + c, z);
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
+      if (dst) store8_f16(dst + c, z);
+      if (a8) store_sum64(asum, R, r, c, store8_i8p(a8 + (size_t)r * H + c, z));
+    }
     if (quant && threadIdx.x == 0) ascale[r] = 0.f;
     return;
   }
@@ -73,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restri
       load8(x, dt, base + c, v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
-      store8_f16(dst + c, v);
+      if (dst) store8_f16(dst + c, v);
+      if (a8) store_sum64(asum, R, r, c, store8_i8p(a8 + (size_t)r * H + c, v));
     }
     if (threadIdx.x == 0) ascale[r] = s;
   } else {
@@ -104,10 +112,13 @@ __device__ inline float row_absmax8(const void* x, int dt, size_t base, int cols
   return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 }
 
-// h (fp32 [R, I], I % 8 == 0) -> int8 codes held as fp16, per-row scales
+// h (fp32 [R, I], I % 8 == 0) -> int8 codes held as fp16 (h16) and/or as
+// bytes with their 64-column sums (h8, hsum), per-row scales
 __global__ __launch_bounds__(kThreads) void quant_rows_f32_kernel(const float* __restrict__ h,
                                                                 int I, f16* __restrict__ h16,
-                                                                float* __restrict__ hscale) {
+                                                                float* __restrict__ hscale,
+                                                                int8_t* __restrict__ h8,
+                                                                float* __restrict__ hsum, int R) {
   const int r = blockIdx.x;
   const size_t base = (size_t)r * I;
   const float s = __fdiv_rn(row_absmax8(h, MOE_F32, base, I), 127.f);
@@ -116,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_f32_kernel(const float* _
     load8(h, MOE_F32, base + c, v);
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
-    store8_f16(h16 + base + c, v);
+    if (h16) store8_f16(h16 + base + c, v);
+    if (h8) store_sum64(hsum, R, r, c, store8_i8p(h8 + base + c, v));
   }
   if (threadIdx.x == 0) hscale[r] = s;
 }
@@ -345,18 +357,20 @@ hipError_t launch_combine_slices(const float* yp, int ns, const float* w, const 
 }
 
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
-                           int quant, f16* a16, float* ascale, uint32_t* flags, hipStream_t s) {
+                           int quant, f16* a16, float* ascale, int8_t* a8, float* asum,
+                           uint32_t* flags, hipStream_t s) {
   const int R = T * k;
   if (R == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_a_kernel, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, T, H, quant,
-                     a16, ascale, flags);
+                     a16, ascale, quant ? a8 : nullptr, asum, R, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
-                                 hipStream_t s) {
+                                 int8_t* h8, float* hsum, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_f32_kernel, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale);
+  hipLaunchKernelGGL(quant_rows_f32_kernel, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale, h8,
+                     hsum, R);
   return hipGetLastError();
 }
 

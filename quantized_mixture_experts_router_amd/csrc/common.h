@@ -40,8 +40,9 @@ constexpr uint32_t kMaskSplitGU = MOE_MASK_SPLIT_GU;
 // (split gate/up, outlier lists, or a down format other than its gate/up's)
 constexpr uint32_t kMaskNoFuse = MOE_MASK_NO_FUSE;
 constexpr uint32_t kMaskOutliers = MOE_MASK_OUTLIERS;
+constexpr uint32_t kMaskInt8 = MOE_MASK_INT8_GEMM;
 constexpr int kMaxE = 256;  // experts per layer
-static_assert(F_COUNT <= 30, "format mask bits");
+static_assert(F_COUNT <= 28, "format mask bits");
 
 __host__ __device__ constexpr int fmt_id(int fmt, int bits, int group) {
   int g = group == 16 ? 0 : group == 32 ? 1 : group == 64 ? 2 : group == 128 ? 3 : -1;
@@ -147,6 +148,10 @@ struct WsLayout {
   size_t h;        // f16 [T*k, I]  or f32 [T*k, I] under MOE_ACT_I8_XH
   size_t h16;      // f16 [T*k, I] int8 codes of h (MOE_ACT_I8_XH)
   size_t hscale;   // f32 [T*k]
+  // int8 prefill GEMM operands (int8 activation modes at prefill sizes):
+  // codes in perm8 byte order and tile-major 64-column sums [K/128][T*k][2]
+  size_t a8, asum;  // x: int8 [T*k, H], f32 [T*k * H/64]
+  size_t h8, hsum;  // h (MOE_ACT_I8_XH): int8 [T*k, I], f32 [T*k * I/64]
   size_t yp;       // f32 [splits, T*k, H] down-projection (partial) sums
   size_t rpart;    // f64 [kb, T, E] router partial logits; aliases yp (routing ends
                    // before the down projection writes it)
@@ -164,6 +169,7 @@ struct WsLayout {
   size_t total;
   int splits;
   bool decode;
+  bool i8;         // the int8 operand regions exist
 };
 
 // Choice of kernel family and split-K factor from host-known sizes only.
@@ -298,6 +304,12 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq, bool outl =
   L.h = take(R * I * (aq == MOE_ACT_I8_XH ? 4 : 2));
   L.h16 = take(aq == MOE_ACT_I8_XH ? R * I * 2 : 0);
   L.hscale = take(R * 4);
+  const bool i8 = aq != MOE_ACT_NONE && !use_decode_path(T, k, E);
+  L.a8 = take(i8 ? R * H : 0);
+  L.asum = take(i8 ? R * (H / 64) * 4 : 0);
+  L.h8 = take(i8 && aq == MOE_ACT_I8_XH ? R * I : 0);
+  L.hsum = take(i8 && aq == MOE_ACT_I8_XH ? R * (I / 64) * 4 : 0);
+  L.i8 = i8;
   L.poff = take((size_t)(E + 1) * 4);
   L.splits = down_splits(T, H, I, E, k);
   L.decode = use_decode_path(T, k, E);
@@ -351,10 +363,14 @@ hipError_t launch_front(const double* P, int KB, const void* x, int xdt, const f
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, uint32_t* flags,
                           void* scratch, hipStream_t s);
+// a16 and a8/asum (h16 and h8/hsum) are each optional: the fp16-held codes
+// feed the fp16 GEMMs, the byte codes (perm8 order) and their 64-column sums
+// (tile-major [K/128][R][2]) the int8 ones
 hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, int k, int H,
-                           int quant, f16* a16, float* ascale, uint32_t* flags, hipStream_t s);
+                           int quant, f16* a16, float* ascale, int8_t* a8, float* asum,
+                           uint32_t* flags, hipStream_t s);
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
-                                 hipStream_t s);
+                                 int8_t* h8, float* hsum, hipStream_t s);
 hipError_t launch_act_quant_i8(const void* v, int dt, int rows, int cols, int8_t* q, float* sc,
                                hipStream_t s);
 // The transposed copy of a prefill GEMM's input rows that its outlier
@@ -372,14 +388,24 @@ struct OutlierInputs {
 // written too.
 hipError_t launch_transpose_pad(const f16* a, int R, int K, const int32_t* offsets, int E,
                                 f16* at, int rp, int32_t* poff, hipStream_t s);
+// The int8 codes (perm8 byte order) and 64-column sums a prefill GEMM reads
+// for the experts of format F_A4G128 (a8 == nullptr: the fp16 kernels take
+// every format).
+struct I8Inputs {
+  const int8_t* a8;
+  const float* asum;
+};
+constexpr uint32_t kI8Formats = 1u << F_A4G128;
 hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
                               uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
                               int k, const f16* a16, const float* ascale, void* h, int h_f32,
-                              bool decode, const OutlierInputs& oi, hipStream_t s);
+                              bool decode, const OutlierInputs& oi, const I8Inputs& i8,
+                              hipStream_t s);
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
                            const f16* ain, const float* ascale, float* yp, int splits,
-                           bool decode, const OutlierInputs& oi, hipStream_t s);
+                           bool decode, const OutlierInputs& oi, const I8Inputs& i8,
+                           hipStream_t s);
 hipError_t launch_reduce_splits(const float* yp, int splits, size_t n, float* Y, hipStream_t s);
 hipError_t launch_combine(const float* yp, int splits, const float* w, const int32_t* inv, int T,
                           int H, int k, void* out, int out_dt, hipStream_t s);

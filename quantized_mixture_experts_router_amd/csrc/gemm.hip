@@ -19,6 +19,8 @@ hipError_t launch_fused_e4(int fid, const FusedArgs& fa, hipStream_t s);
 hipError_t launch_fused_a1(int fid, const FusedArgs& fa, hipStream_t s);
 hipError_t launch_fused_a3(int fid, const FusedArgs& fa, hipStream_t s);
 
+hipError_t launch_ffn_i8(int fid, int role, const FfnArgs& a, hipStream_t s);
+
 hipError_t launch_ffn_fmt(int fid, int role, const FfnArgs& a, bool decode, hipStream_t s) {
   switch (fid / 4) {
     case 0: return launch_ffn_a4(fid, role, a, decode, s);
@@ -32,12 +34,14 @@ hipError_t launch_ffn_fmt(int fid, int role, const FfnArgs& a, bool decode, hipS
 
 namespace {
 
-// one launch per format of the mask
+// one launch per format of the mask; with int8 operands, the int8 kernels
+// take the W4A8 formats of the fused gate/up and down roles at prefill
 hipError_t launch_all(int role, const FfnArgs& a, bool decode, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
   for (int f = 0; f < F_COUNT; ++f) {
     if ((a.fmt_mask >> f) & 1u) {
-      const hipError_t e = launch_ffn_fmt(f, role, a, decode, s);
+      const bool i8 = !decode && a.a8 && ((kI8Formats >> f) & 1u) && (role == R_GU || role == R_DN);
+      const hipError_t e = i8 ? launch_ffn_i8(f, role, a, s) : launch_ffn_fmt(f, role, a, decode, s);
       if (e != hipSuccess) return e;
     }
   }
@@ -49,8 +53,11 @@ hipError_t launch_all(int role, const FfnArgs& a, bool decode, hipStream_t s) {
 hipError_t launch_ffn_gate_up(const moe_packed_expert* experts, const int32_t* offsets,
                               uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E,
                               int k, const f16* a16, const float* ascale, void* h, int h_f32,
-                              bool decode, const OutlierInputs& oi, hipStream_t s) {
+                              bool decode, const OutlierInputs& oi, const I8Inputs& i8,
+                              hipStream_t s) {
   FfnArgs a;
+  a.a8 = i8.a8;
+  a.asum = i8.asum;
   a.at = oi.at;
   a.rp = oi.rp;
   a.poff = oi.poff;
@@ -141,8 +148,11 @@ hipError_t launch_ffn_fused(const moe_packed_expert* experts, const int32_t* off
 hipError_t launch_ffn_down(const moe_packed_expert* experts, const int32_t* offsets,
                            uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
                            const f16* ain, const float* ascale, float* yp, int splits,
-                           bool decode, const OutlierInputs& oi, hipStream_t s) {
+                           bool decode, const OutlierInputs& oi, const I8Inputs& i8,
+                           hipStream_t s) {
   FfnArgs a;
+  a.a8 = i8.a8;
+  a.asum = i8.asum;
   a.at = oi.at;
   a.rp = oi.rp;
   a.poff = oi.poff;

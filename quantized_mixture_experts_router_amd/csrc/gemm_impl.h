@@ -61,6 +61,10 @@ struct FfnArgs {
   const f16* at = nullptr;
   int rp = 0;
   const int32_t* poff = nullptr;
+  // int8 prefill GEMMs (format F_A4G128): the codes in perm8 order and
+  // their 64-column sums (nullptr: the fp16 kernels run)
+  const int8_t* a8 = nullptr;
+  const float* asum = nullptr;
 };
 
 // Launches the grouped GEMM of format `fid` in role `role` (one unit per

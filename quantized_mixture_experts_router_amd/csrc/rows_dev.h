@@ -43,6 +43,33 @@ __device__ inline void load8(const void* x, int dt, size_t idx, float* v) {
 
 // stores 8 values as fp16; true when one of them is beyond the fp16 range
 // (|v| > 65504: stored as +-inf)
+// 8 int8 codes (integral fp32 values in [-127, 127]) in the byte order of
+// the int8 GEMM's operands: byte p holds code perm8(p), perm8 = 0,4,1,5,2,6,3,7,
+// the order in which a 4-bit weight word's nibbles unpack to bytes. Returns
+// their sum.
+__device__ inline float store8_i8p(int8_t* dst, const float* q) {
+  const int b[8] = {(int)q[0], (int)q[4], (int)q[1], (int)q[5],
+                    (int)q[2], (int)q[6], (int)q[3], (int)q[7]};
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    lo |= (uint32_t)(b[p] & 0xff) << (8 * p);
+    hi |= (uint32_t)(b[p + 4] & 0xff) << (8 * p);
+  }
+  *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+  return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+}
+
+// Sum of one 64-column block over the 8 lanes holding it (lanes 8j..8j+7 of
+// a wavefront, 8 columns each); stored by the first of them into the int8
+// GEMM's tile-major sums: sums[(c / 128) R + r][(c / 64) % 2].
+__device__ inline void store_sum64(float* sums, int R, int r, int c, float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  if ((threadIdx.x & 7) == 0) sums[((size_t)(c >> 7) * R + r) * 2 + ((c >> 6) & 1)] = v;
+}
+
 __device__ inline bool store8_f16(f16* dst, const float* v) {
   f16x8 h;
   bool over = false;

@@ -771,3 +771,67 @@ def test_layer_parity_int8_x_fused(moeq, T):
     err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
     _say(f"    max row rel-L2 {err.max():.3e}")
     assert err.max() <= tolerance(cfg), err.max()
+
+
+I8_CASES = [
+    # name, T, H, I, E, k, activation mode, expert formats
+    ("w4a8", 300, 512, 512, 8, 2, 2, None),      # ~75 rows per expert: one partial m-tile each
+    ("w4a8", 1100, 512, 1024, 8, 2, 2, None),    # ~275 rows: full and partial m-tiles
+    ("w4a8", 600, 1024, 512, 8, 2, 1, None),     # int8 x only: int8 gate/up, fp16 down
+    ("w4a8", 600, 512, 512, 8, 2, 2, "mixed"),   # beside 2-bit and e2m1 experts: both kernels
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,act,kind", I8_CASES)
+def test_int8_gemm_path(moeq, name, T, H, I, E, k, act, kind):
+    """Prefill with int8 activations on 4-bit group-128 experts, with the
+    caller's MOE_MASK_INT8_GEMM bit, runs the int8 MFMA GEMMs (integer group
+    sums, scaled in fp32 per group), through moe_layer_forward and
+    moe_grouped_ffn_q. They match the oracle, and the default fp16 kernels
+    on the same layer."""
+    from dataclasses import replace
+    from synth import FMT_ASYM, FMT_E2M1
+    cfg = replace(synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode="quantize"),
+                  act=act)
+    if kind == "mixed":
+        cyc = [(FMT_ASYM, 4, 128), (FMT_ASYM, 2, 16), (FMT_E2M1, 4, 16)]
+        cfg = replace(cfg, expert_fmts=tuple(cyc[e % 3] for e in range(E)))
+    _say(f"[int8 gemm] T={T} H={H} I={I} E={E} k={k} act={act} {kind} "
+         f"({prefill_order(T, H, I, E, k)})")
+    wl = Workload(cfg)
+    full = wl.packed.fmt_mask
+    assert full & (1 << 3) and not full & (moeq.MASK_SPLIT_GU | moeq.MASK_OUTLIERS)
+    assert not full & moeq.MASK_INT8_GEMM  # never set by moe_format_mask
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, None, wl.expert, cfg.E, cfg.k, act=act)
+    ok = ~ref["flagged"]
+    outs = {}
+    try:
+        for label, mask in (("int8", full | moeq.MASK_INT8_GEMM), ("fp16", full)):
+            wl.packed.fmt_mask = mask
+            ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, act)
+            out, ids, _ = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=act, ws=ws)
+            torch.cuda.synchronize()
+            assert moeq.read_flags(ws) == 0
+            np.testing.assert_array_equal(ids.cpu().numpy()[ok], ref["ids"][ok])
+            outs[label] = out.cpu().numpy()
+            err = rel_l2_rows(outs[label][ok], ref["out"][ok])
+            _say(f"    {label} kernels: max row rel-L2 {err.max():.3e}")
+            assert err.max() <= tolerance(cfg), (label, err.max())
+    finally:
+        wl.packed.fmt_mask = full
+    d = rel_l2_rows(outs["int8"][ok], outs["fp16"][ok])
+    _say(f"    int8 against fp16 kernels: max row rel-L2 {d.max():.3e}")
+    assert d.max() <= tolerance(cfg)
+    # the grouped FFN entry point honours the bit too: same kernels, same Y
+    counts, offsets, perm, inv, _ = moeq.permute(torch.from_numpy(ref["ids"]).to("cuda").int(), cfg.E)
+    try:
+        Ys = {}
+        for label, mask in (("int8", full | moeq.MASK_INT8_GEMM), ("fp16", full)):
+            wl.packed.fmt_mask = mask
+            Ys[label] = moeq.grouped_ffn(wl.x, wl.packed, offsets, perm, cfg.k, act=act).cpu().numpy()
+        torch.cuda.synchronize()
+    finally:
+        wl.packed.fmt_mask = full
+    dy = rel_l2_rows(Ys["int8"], Ys["fp16"])
+    _say(f"    grouped FFN, int8 against fp16 kernels: max row rel-L2 {dy.max():.3e}")
+    assert dy.max() <= tolerance(cfg)
