@@ -34,10 +34,23 @@ __device__ inline float row_absmax(const void* x, int dt, size_t base, int cols)
   return r;
 }
 
+// Block-wide maximum of a per-thread value (256 threads).
+__device__ inline float block_max(float m) {
+  __shared__ float s_red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
 // one block per sorted row r: a16[r] = x[perm[r]] (fp16), or its int8 codes
 // held as fp16 (a16) and/or as bytes with their 64-column sums (a8, asum:
 // the int8 GEMM's operands; R rows); each thread moves 8 columns at a time
-// (H % 8 == 0, x 16-byte aligned)
+// (H % 8 == 0, x 16-byte aligned). With int8 codes and NC > 0 a thread keeps
+// its NC chunks of 8 columns in registers between the absmax and the
+// quantisation (H <= 2048 NC), so the row is read once.
+template <int NC>
 __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restrict__ x, int dt,
                                                           const int32_t* __restrict__ perm, int T,
                                                           int H,
@@ -61,7 +74,31 @@ __global__ __launch_bounds__(kThreads) void gather_a_kernel(const void* __restri
     return;
   }
   const size_t base = (size_t)t * H;
-  if (quant) {
+  if (quant && NC > 0) {
+    float v[NC > 0 ? NC : 1][8];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = 8 * (threadIdx.x + kThreads * j);
+      if (c < H) {
+        load8(x, dt, base + c, v[j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[j][q]));
+      }
+    }
+    const float s = __fdiv_rn(block_max(m), 127.f);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = 8 * (threadIdx.x + kThreads * j);
+      if (c < H) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[j][q] = quant_i8(v[j][q], s);
+        if (dst) store8_f16(dst + c, v[j]);
+        if (a8) store_sum64(asum, R, r, c, store8_i8p(a8 + (size_t)r * H + c, v[j]));
+      }
+    }
+    if (threadIdx.x == 0) ascale[r] = s;
+  } else if (quant) {
     float m = 0.f;
     for (int c = 8 * threadIdx.x; c < H; c += 8 * kThreads) {
       float v[8];
@@ -113,7 +150,11 @@ __device__ inline float row_absmax8(const void* x, int dt, size_t base, int cols
 }
 
 // h (fp32 [R, I], I % 8 == 0) -> int8 codes held as fp16 (h16) and/or as
-// bytes with their 64-column sums (h8, hsum), per-row scales
+// bytes with their 64-column sums (h8, hsum), per-row scales. NC > 0: each
+// thread keeps its NC chunks of 8 columns in registers between the absmax
+// and the quantisation (I <= 2048 NC), so the row is read once; NC == 0:
+// two passes over memory.
+template <int NC>
 __global__ __launch_bounds__(kThreads) void quant_rows_f32_kernel(const float* __restrict__ h,
                                                                 int I, f16* __restrict__ h16,
                                                                 float* __restrict__ hscale,
@@ -121,16 +162,42 @@ __global__ __launch_bounds__(kThreads) void quant_rows_f32_kernel(const float* _
                                                                 float* __restrict__ hsum, int R) {
   const int r = blockIdx.x;
   const size_t base = (size_t)r * I;
-  const float s = __fdiv_rn(row_absmax8(h, MOE_F32, base, I), 127.f);
-  for (int c = 8 * threadIdx.x; c < I; c += 8 * kThreads) {
-    float v[8];
-    load8(h, MOE_F32, base + c, v);
+  if constexpr (NC > 0) {
+    float v[NC][8];
+    float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
-    if (h16) store8_f16(h16 + base + c, v);
-    if (h8) store_sum64(hsum, R, r, c, store8_i8p(h8 + base + c, v));
+    for (int j = 0; j < NC; ++j) {
+      const int c = 8 * (threadIdx.x + kThreads * j);
+      if (c < I) {
+        load8(h, MOE_F32, base + c, v[j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[j][q]));
+      }
+    }
+    const float s = __fdiv_rn(block_max(m), 127.f);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = 8 * (threadIdx.x + kThreads * j);
+      if (c < I) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[j][q] = quant_i8(v[j][q], s);
+        if (h16) store8_f16(h16 + base + c, v[j]);
+        if (h8) store_sum64(hsum, R, r, c, store8_i8p(h8 + base + c, v[j]));
+      }
+    }
+    if (threadIdx.x == 0) hscale[r] = s;
+  } else {
+    const float s = __fdiv_rn(row_absmax8(h, MOE_F32, base, I), 127.f);
+    for (int c = 8 * threadIdx.x; c < I; c += 8 * kThreads) {
+      float v[8];
+      load8(h, MOE_F32, base + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = quant_i8(v[q], s);
+      if (h16) store8_f16(h16 + base + c, v);
+      if (h8) store_sum64(hsum, R, r, c, store8_i8p(h8 + base + c, v));
+    }
+    if (threadIdx.x == 0) hscale[r] = s;
   }
-  if (threadIdx.x == 0) hscale[r] = s;
 }
 
 // standalone per-row int8 quantisation; vec (cols % 8 == 0, v 16-byte and q
@@ -361,16 +428,28 @@ hipError_t launch_gather_a(const void* x, int xdt, const int32_t* perm, int T, i
                            uint32_t* flags, hipStream_t s) {
   const int R = T * k;
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_a_kernel, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, T, H, quant,
-                     a16, ascale, quant ? a8 : nullptr, asum, R, flags);
+  // int8 codes of rows up to 4096 / 16384 columns: the row is read once
+  auto kern = !quant || H > 8 * kThreads * 8 ? gather_a_kernel<0>
+              : H <= 8 * kThreads * 2        ? gather_a_kernel<2>
+                                             : gather_a_kernel<8>;
+  hipLaunchKernelGGL(kern, dim3(R), dim3(kThreads), 0, s, x, xdt, perm, T, H, quant, a16, ascale,
+                     quant ? a8 : nullptr, asum, R, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_f32(const float* h, int R, int I, f16* h16, float* hscale,
                                  int8_t* h8, float* hsum, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_f32_kernel, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale, h8,
-                     hsum, R);
+  // rows of up to 4096 / 16384 columns are read once (kept in registers)
+  if (I <= 8 * kThreads * 2)
+    hipLaunchKernelGGL(quant_rows_f32_kernel<2>, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale,
+                       h8, hsum, R);
+  else if (I <= 8 * kThreads * 8)
+    hipLaunchKernelGGL(quant_rows_f32_kernel<8>, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale,
+                       h8, hsum, R);
+  else
+    hipLaunchKernelGGL(quant_rows_f32_kernel<0>, dim3(R), dim3(kThreads), 0, s, h, I, h16, hscale,
+                       h8, hsum, R);
   return hipGetLastError();
 }
 
