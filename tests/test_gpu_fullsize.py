@@ -126,8 +126,9 @@ def test_fullsize_every_token(moeq, name, Ts):
 def test_fullsize_w4a8(moeq):
     """W4A8 at 16 and 8192 tokens: routing and permutation on every token;
     expert outputs Y on 8 experts (all rows of each one's partial last
-    m-tile plus 48 others); combined outputs of every token routed only to
-    those experts."""
+    m-tile plus 48 others), from the default kernels and from the opt-in
+    int8 MFMA GEMMs; combined outputs of every token routed only to those
+    experts."""
     name = "w4a8"
     wl = _workload(name)
     cfg = wl.cfg
@@ -146,12 +147,19 @@ def test_fullsize_w4a8(moeq):
         ok = _check_routing(moeq, wl, T, ids, w, rids[:T], rw[:T], flagged[:T])
         counts, offsets, perm, inv, _ = moeq.permute(ids, cfg.E)
         Y = moeq.grouped_ffn(x, wl.packed, offsets, perm, cfg.k, act=cfg.act)
+        # the opt-in int8 MFMA GEMMs on the same permutation (prefill sizes)
+        full = wl.packed.fmt_mask
+        try:
+            wl.packed.fmt_mask = full | moeq.MASK_INT8_GEMM
+            Y8 = moeq.grouped_ffn(x, wl.packed, offsets, perm, cfg.k, act=cfg.act)
+        finally:
+            wl.packed.fmt_mask = full
         torch.cuda.synchronize()
-        gpu[T] = dict(out=out.cpu().numpy(), Y=Y.cpu().numpy(), ok=ok,
+        gpu[T] = dict(out=out.cpu().numpy(), Y=Y.cpu().numpy(), Y8=Y8.cpu().numpy(), ok=ok,
                       ids=ids.cpu().numpy(), counts=counts.cpu().numpy(),
                       offsets=offsets.cpu().numpy(), perm=perm.cpu().numpy(),
                       inv=inv.cpu().numpy())
-        del out, Y, ws
+        del out, Y, Y8, ws
     # the 8 experts: those of the first decode tokens, then evenly spread ones
     S = []
     for e in list(gpu[16]["ids"][:4].reshape(-1)) + list(range(0, cfg.E, cfg.E // 8)):
@@ -186,9 +194,12 @@ def test_fullsize_w4a8(moeq):
             for r, y in zip(rows, ya):
                 Yref[T][int(r)] = y
             err = rel_l2_rows(g["Y"][rows], ya)
+            err8 = rel_l2_rows(g["Y8"][rows], ya)
             _say(f"    T={T} expert {e}: {c} rows, {last.size} in the partial m-tile, "
-                 f"{rows.size} checked, max row rel-L2 {err.max():.3e}")
+                 f"{rows.size} checked, max row rel-L2 {err.max():.3e} "
+                 f"(int8 GEMMs {err8.max():.3e})")
             assert err.max() <= tolerance(cfg), (T, e, err.max())
+            assert err8.max() <= tolerance(cfg), (T, e, err8.max())
         del Wg, Wu, Wd
     # combined outputs of the tokens whose experts are all in S
     for T, g in gpu.items():
