@@ -211,8 +211,9 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
  * experts on the int8 matrix cores when the activations are int8 (integer
  * group sums scaled into fp32 per group: the same result up to fp32
  * rounding), unless some expert needs the split roles or outlier lists.
- * Measured slower than the default fp16 kernels on this GPU; kept for
- * comparison. The phase entry points (moe_ffn_*) ignore it. */
+ * Measured slightly slower than the default fp16 kernels on this GPU, and
+ * closer to the exact result (no fp16 rounding of the decoded weights). The
+ * phase entry points (moe_ffn_*) ignore it. */
 #define MOE_MASK_INT8_GEMM (1u << 28)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 

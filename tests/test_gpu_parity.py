@@ -678,6 +678,9 @@ NEXT_CASES = [
     ("w4a8", 300, 512, 512, 8, 2, "split", 0.005),         # int8 x and h, split, outliers
     ("w4a8", 16, 512, 512, 8, 2, "split", 0.005),
     ("fine_e2m1", 70, 256, 256, 64, 6, "split", 0.005),
+    # Zipf-skewed routing at prefill size: experts with few or no rows in the
+    # padded transposed inputs of the outlier corrections
+    ("hotcold", 600, 512, 256, 32, 4, "mixed", 0.005),
 ]
 
 
@@ -779,6 +782,7 @@ I8_CASES = [
     ("w4a8", 1100, 512, 1024, 8, 2, 2, None),    # ~275 rows: full and partial m-tiles
     ("w4a8", 600, 1024, 512, 8, 2, 1, None),     # int8 x only: int8 gate/up, fp16 down
     ("w4a8", 600, 512, 512, 8, 2, 2, "mixed"),   # beside 2-bit and e2m1 experts: both kernels
+    ("w4a8", 900, 512, 512, 32, 2, 2, None),     # 32 experts of about 56 rows
 ]
 
 
