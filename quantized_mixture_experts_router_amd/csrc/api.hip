@@ -236,16 +236,21 @@ moe_status layer_forward_ws(const void* x, moe_dtype xdt, const float* Wr, const
   int32_t* inv = (int32_t*)ws_at(ws, L.inv);
   float* yp = (float*)ws_at(ws, L.yp);
   double* rpart = (double*)ws_at(ws, L.rpart);
-  MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
   const int kb = route_plan(T, H, E).kb;
   moe_status st;
   if (L.decode && front_fits(T, H, E, k)) {
     // small batch: top-k, permutation and gather in one block
+    MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
     MOE_TRY(launch_front(rpart, kb, x, xdt, b, T, H, E, k, ids, w, counts, offsets, perm, inv,
                          flags, aq != MOE_ACT_NONE, (f16*)ws_at(ws, L.a16),
                          (float*)ws_at(ws, L.ascale), s));
   } else {
-    MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
+    if (cert_plan(T, H, E, xdt).use) {
+      MOE_TRY(launch_route_cert(x, xdt, Wr, b, T, H, E, k, ids, w, rpart, s));
+    } else {
+      MOE_TRY(launch_route_logits(x, xdt, Wr, T, H, E, rpart, s));
+      MOE_TRY(launch_route_topk(rpart, kb, b, T, E, k, ids, w, nullptr, s));
+    }
     MOE_TRY(launch_permute(ids, T, k, E, counts, offsets, perm, inv, flags,
                            ws_at(ws, L.pscratch), s));
     const uint32_t m = effective_mask(fmt_mask);
@@ -397,7 +402,7 @@ size_t moe_workspace_size(int T, int H, int I, int E, int k, moe_actq aq) {
 
 size_t moe_route_workspace_size(int T, int H, int E) {
   if (T <= 0 || H <= 0 || E <= 0) return 0;
-  return align256(route_plan(T, H, E).part_bytes);
+  return align256(route_ws_bytes(T, H, E));
 }
 
 moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float* b, int T, int H,
@@ -411,6 +416,9 @@ moe_status moe_route(const void* x, moe_dtype xdt, const float* Wr, const float*
   if (!x || !Wr || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   if (ws_bytes < moe_route_workspace_size(T, H, E)) return MOE_ERR_WORKSPACE;
+  if (!logits && cert_plan(T, H, E, xdt).use)
+    return hip_status(launch_route_cert(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, ws,
+                                        (hipStream_t)stream));
   return hip_status(launch_route(x, xdt, Wr, b, T, H, E, k, topk_ids, topk_w, logits,
                                  (double*)ws, (hipStream_t)stream));
 }

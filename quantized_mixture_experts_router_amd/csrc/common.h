@@ -268,6 +268,60 @@ inline RoutePlan route_plan(int T, int H, int E) {
   return p;
 }
 
+// Certified router for prefill batches (route_cert.hip): approximate logits
+// on the bf16 matrix cores with a proven error bound, then exact fp64 logits
+// of the experts that bound cannot rule out of the top-k. The router weights
+// are first split into two bf16 planes [2][E][hp] (hp = H rounded up to 64)
+// with their rows' fp64 norms [E]; then one block per (128-token
+// tile, bn-expert tile, K split), bn = 128 for bf16 tokens and E > 64, else
+// 64; ks K splits leave ks fp32 partial logits [ks][T][E] and fp64 partial
+// squared norms of the token rows [ks][T]. Used for T >= 256 and E >= 32
+// (below, the fp64 logits kernel is as fast) when no fp32 logits are asked
+// for, and while every byte offset of x and Wr (as fp32) fits 31 bits.
+#ifndef MOEQ_CERT_BLOCKS
+#define MOEQ_CERT_BLOCKS 256
+#endif
+constexpr int kCertTileM = 128;  // tokens per block tile
+constexpr int kCertChunk = 64;   // hidden columns per pipeline stage
+struct CertPlan {
+  bool use;
+  int tt, et, bn, ks, cpb, hp;   // tiles, expert tile rows, K splits, chunks per block, padded H
+  size_t ap, nx, nw, wp, bytes;  // workspace offsets and size
+};
+inline CertPlan cert_plan(int T, int H, int E, int xdt) {
+  CertPlan p{};
+  p.use = T >= 256 && E >= 32 && E <= kMaxE && (size_t)T * H * 4 < (1ull << 31) &&
+          (size_t)E * H * 4 < (1ull << 31);
+  if (!p.use) return p;
+  const int nc = (H + kCertChunk - 1) / kCertChunk;
+  p.hp = nc * kCertChunk;
+  p.bn = xdt == MOE_BF16 && E > 64 ? 128 : 64;
+  p.tt = (T + kCertTileM - 1) / kCertTileM;
+  p.et = (E + p.bn - 1) / p.bn;
+  p.ks = 1;
+  while ((long)p.tt * p.et * p.ks < MOEQ_CERT_BLOCKS && nc / (2 * p.ks) >= 4) p.ks *= 2;
+  p.cpb = (nc + p.ks - 1) / p.ks;
+  size_t o = 0;
+  p.ap = o;
+  o = align256(o + (size_t)p.ks * T * E * 4);
+  p.nx = o;
+  o = align256(o + (size_t)p.ks * T * 8);
+  p.nw = o;
+  o = align256(o + (size_t)E * 8);
+  p.wp = o;
+  o = align256(o + (size_t)2 * E * p.hp * 2);
+  p.bytes = o;
+  return p;
+}
+inline size_t route_ws_bytes(int T, int H, int E) {
+  size_t a = route_plan(T, H, E).part_bytes;
+  for (int xdt : {MOE_F32, MOE_BF16}) {
+    const CertPlan c = cert_plan(T, H, E, xdt);
+    if (c.use && c.bytes > a) a = c.bytes;
+  }
+  return a;
+}
+
 // permutation: one block up to kPermuteSingleMax assignments, else
 // histogram / scan / scatter kernels over `blocks` blocks of `chunk`
 // assignments with scratch_bytes of device scratch (256-aligned)
@@ -316,7 +370,7 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k, int aq, bool outl =
   const FusedPlan fp = fused_plan(T, H, I, E, k, aq);
   const int planes = fp.use && fp.ns > L.splits ? fp.ns : L.splits;
   const size_t yp_bytes = (size_t)planes * R * H * 4;
-  const size_t rp_bytes = route_plan(T, H, E).part_bytes;
+  const size_t rp_bytes = route_ws_bytes(T, H, E);
   const size_t ps_bytes = permute_plan((int)R, E).scratch_bytes;
   size_t big = yp_bytes > rp_bytes ? yp_bytes : rp_bytes;
   big = big > ps_bytes ? big : ps_bytes;
@@ -353,6 +407,10 @@ hipError_t launch_route_topk(const double* P, int KB, const float* b, int T, int
 hipError_t launch_route(const void* x, int xdt, const float* Wr, const float* b, int T, int H,
                         int E, int k, int32_t* ids, float* w, float* logits, double* P,
                         hipStream_t s);
+// certified router (cert_plan(T, H, E, xdt).use; ws: route_ws_bytes(T, H, E))
+hipError_t launch_route_cert(const void* x, int xdt, const float* Wr, const float* b, int T,
+                             int H, int E, int k, int32_t* ids, float* w, void* ws,
+                             hipStream_t s);
 // fused small-batch front after the logits kernel: top-k, permutation,
 // gather (+ int8) in one block
 bool front_fits(int T, int H, int E, int k);
