@@ -159,9 +159,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fused_decode_kernel(FusedArgs
       load_b(i + 4, B1); load_a(i + 4, A1); if (i + 2 < nt) compute(i + 2, B2, A2);
     }
   }
-  __syncthreads();  // the h slice is complete
-
   // ---------------------------------------------------------------- phase 2
+  // (its first two weight tiles are requested before the barrier that
+  // completes the h slice: they do not depend on it)
   {
     const int P = H / 64;              // output row-tile pairs of down
     const int KS = S / F::KT;          // K tiles of the slice
@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fused_decode_kernel(FusedArgs
     BTile<F> B0, B1, B2;
     load_b(0, B0);
     load_b(1, B1);
+    __syncthreads();  // the h slice is complete
     for (int i = 0; i < nt; i += 3) {
       load_b(i + 2, B2); compute(i, B0);
       load_b(i + 3, B0); if (i + 1 < nt) compute(i + 1, B1);
