@@ -8,14 +8,18 @@
 // experts' logits can sit close together; here low precision only proposes,
 // and every decision that counts is taken on fp64 values.
 //
+// Step 0 (cert_prep_kernel): each fp32 router weight is split into two bf16
+// numbers, w = wh + wm + r with |r| <= 2^-16 |w| (round-to-nearest
+// conversions), stored as two planes, and each router row's fp64 norm is
+// taken.
+//
 // Step 1 (cert_logits_kernel): approximate logits A[t,e] on the bf16 matrix
-// cores. Each fp32 router weight is split into two bf16 numbers, w = wh + wm
-// + r with |r| <= 2^-16 |w| (round-to-nearest conversions), and fp32 token
-// rows the same way; bf16 token rows are exact. The products of bf16 numbers
-// are exact in fp32; the 32x32x16 bf16 instruction adds them into an fp32
-// tile, and every kFlush stages (kFlush * 64 columns) the tile is added into
-// fp64 and restarted from zero. The same blocks leave the fp64 sums of
-// squares of the token and expert rows they stream.
+// cores from those planes; fp32 token rows are split the same way in
+// registers, bf16 token rows are exact. The products of bf16 numbers are
+// exact in fp32; the 32x32x16 bf16 instruction adds them into an fp32 tile,
+// and every kFlush stages (kFlush * 64 columns) the tile is added into fp64
+// and restarted from zero. The blocks of the first expert tile also leave
+// the fp64 sums of squares of the token rows they stream.
 //
 // Step 2 (cert_select_kernel, one wavefront per token): an error bound
 //   |A[t,e] - L[t,e]| <= d[t,e] = cb * |x_t| |w_e| + 2^-40 |A[t,e]| + tiny,
@@ -24,15 +28,17 @@
 // magnitudes (any rounding mode that is faithful), the split residuals, the
 // fp32 partial stores and the fp64 sums; the magnitudes sum to at most
 // |x_t| |w_e| (Cauchy-Schwarz); cb doubles the total as a safety margin, and
-// the absolute term covers subnormals flushed to zero. An expert whose upper
-// end A + d lies below the k-th largest lower end A - d has k experts surely
-// above it and is out. The rest (the k winners and any expert the bound
-// cannot separate from them, about k + 0.2 per token on N(0,1) inputs) get
-// their logit recomputed exactly as the fp64 router does, a fixed-order fp64
-// dot product, and the top-k and the softmax run on those values with the
-// fp64 router's tie rule. A token whose approximate logits or bounds are not
-// finite (NaN or Inf in x, Wr or b, an fp32 overflow) has every expert
-// recomputed, so NaN routing is detected exactly as there.
+// the absolute term covers subnormals flushed to zero. The threshold is the
+// k-th largest of the 64 lanes' largest lower ends A - d, which is at most
+// the k-th largest lower end: an expert whose upper end A + d lies below it
+// has k experts surely above it and is out. The rest (the k winners and any
+// expert the bound cannot separate from them, k + 0.1 to 0.5 per token on
+// the workloads' inputs) get their logit recomputed exactly as the fp64
+// router does, a fixed-order fp64 dot product, and the top-k and the
+// softmax run on those values with the fp64 router's tie rule. A token whose
+// approximate logits or bounds are not finite (NaN or Inf in x, Wr or b, an
+// fp32 overflow) has every expert recomputed, so NaN routing is detected
+// exactly as there.
 #include "deq.h"
 #include "profile.h"
 #include "route_dev.h"
