@@ -567,6 +567,54 @@ def headline_oracle_sample(cfg, wl, outs):
     return cpu, par
 
 
+def hbm_sweep(torch, moeq, dev):
+    """Read rate of a 4 GiB buffer (16 x the last-level cache) over launch
+    shapes of the shaped streaming read: blocks per CU, block size, 16-byte
+    loads in flight per thread, the interleaved and the contiguous layout,
+    cached and non-temporal loads. Each shape: one untimed launch, then the
+    median of 5 launches timed by HIP events on the launch stream. Prints one
+    JSON line per shape and a final line with the fastest shape."""
+    import numpy as np
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    rows = []
+    for nt in (True, False):
+        for layout in (0, 1):
+            for waves in (4, 8, 16):
+                for inflight in (4, 8, 16):
+                    for per_cu in (1, 2, 4, 8, 16, 32):
+                        blocks = cus * per_cu
+                        if waves * per_cu > 64 or blocks > (1 << 16):
+                            continue
+                        moeq.stream_read_shaped(buf, blocks, waves, inflight, layout, nt, sink)
+                        st = []
+                        for _ in range(5):
+                            e0 = torch.cuda.Event(enable_timing=True)
+                            e1 = torch.cuda.Event(enable_timing=True)
+                            e0.record()
+                            moeq.stream_read_shaped(buf, blocks, waves, inflight, layout, nt, sink)
+                            e1.record()
+                            torch.cuda.synchronize()
+                            st.append(e0.elapsed_time(e1))
+                        ms = float(np.median(st))
+                        row = {"nontemporal": nt, "layout": ["interleaved", "contiguous"][layout],
+                               "waves": waves, "inflight": inflight, "blocks_per_cu": per_cu,
+                               "blocks": blocks, "ms": ms, "GBps": n / (ms * 1e-3) / 1e9}
+                        rows.append(row)
+                        print(json.dumps(row), flush=True)
+    best = max(rows, key=lambda r: r["GBps"])
+    print(json.dumps({"hbm_sweep_bytes": n, "cus": cus, "shapes": len(rows), "best": best,
+                      "default_shape_GBps": {
+                          "nontemporal": next(r["GBps"] for r in rows if r["nontemporal"] and
+                                              r["layout"] == "interleaved" and r["waves"] == 4 and
+                                              r["inflight"] == 8 and r["blocks_per_cu"] == 16),
+                          "cached": next(r["GBps"] for r in rows if not r["nontemporal"] and
+                                         r["layout"] == "interleaved" and r["waves"] == 4 and
+                                         r["inflight"] == 8 and r["blocks_per_cu"] == 16)}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -584,6 +632,8 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=10)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--hbm-sweep", action="store_true",
+                    help="only sweep the launch shapes of the streaming read over a 4 GiB buffer")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -610,6 +660,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": n, "launches": 5}))
+        return
+
+    if args.hbm_sweep:
+        hbm_sweep(torch, moeq, dev)
         return
 
     names = [n for n in args.workloads.split(",") if n]
@@ -697,8 +751,25 @@ def main():
                 st.append(e0.elapsed_time(e1))
             ctx["hbm_read_GBps_" + ("nontemporal" if nt else "cached")] = \
                 flush.numel() / (float(np.median(st)) * 1e-3) / 1e9
+        # the fastest shape of the launch-shape sweep (--hbm-sweep): one block of
+        # 4 wavefronts per CU, each block a contiguous run, 16 non-temporal
+        # 16-byte loads in flight per thread
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.empty(cus, dtype=torch.int32, device=dev)
+        moeq.stream_read_shaped(flush, cus, 4, 16, 1, True, sink)
+        st = []
+        for _ in range(5):
+            e0, e1 = bench.event(), bench.event()
+            e0.record()
+            moeq.stream_read_shaped(flush, cus, 4, 16, 1, True, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            st.append(e0.elapsed_time(e1))
+        ctx["hbm_read_GBps_best_shape"] = flush.numel() / (float(np.median(st)) * 1e-3) / 1e9
+        ctx["best_shape"] = "contiguous run per block, 1 block of 4 wavefronts per CU, 16 non-temporal 16-B loads in flight per thread"
         log(f"[bench] streaming read of 1 GiB: {ctx['hbm_read_GBps_cached']:.0f} GB/s cached, "
-            f"{ctx['hbm_read_GBps_nontemporal']:.0f} GB/s non-temporal")
+            f"{ctx['hbm_read_GBps_nontemporal']:.0f} GB/s non-temporal, "
+            f"{ctx['hbm_read_GBps_best_shape']:.0f} GB/s in the sweep's fastest shape")
         del flush
 
     head = HEADLINE if HEADLINE in entries and "prefill" in entries[HEADLINE] else \

@@ -432,6 +432,25 @@ moe_status moe_plan_tiers(const int64_t* counts, int E, const uint64_t* tier_byt
 moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                            void* stream);
 
+/* Measurement aid (not a step of the layer): the streaming read above with
+ * its launch shape as arguments, to find the read rate the device reaches
+ * and the shape that reaches it.
+ *   blocks   1..MOE_STREAM_MAX_BLOCKS blocks of 64*waves threads (waves
+ *            1..16);
+ *   inflight 1, 2, 4, 8 or 16 independent 16-byte loads per thread before
+ *            their words are folded;
+ *   layout   0: the grid sweeps the buffer as one front (thread t of block b
+ *            reads chunk b*nthr + t, then steps by nthr*blocks chunks);
+ *            1: block b reads its own contiguous run of ceil(chunks/blocks)
+ *            16-byte chunks, nthr chunks at a time.
+ * Other values give MOE_ERR_INVALID_ARG. sink (device, `blocks` uint32)
+ * receives one XOR word per block, so the XOR of the sink entries is the XOR
+ * of every 32-bit word of the buffer, as for moe_stream_read. */
+#define MOE_STREAM_MAX_BLOCKS 65536
+moe_status moe_stream_read_shaped(const void* src, size_t bytes, int nontemporal, int blocks,
+                                  int waves, int inflight, int layout, uint32_t* sink,
+                                  void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -11,7 +11,7 @@ from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_L
                    noalloc_scratch_bytes, pack_expert, pack_experts,
                    packed_expert_bytes, permute, plan_tiers, read_flags, route, route_i8,
                    route_workspace_size, router_i8_params, router_logit_range,
-                   stream_read, version,
+                   stream_read, stream_read_shaped, version,
                    workspace,
                    workspace_size)
 
@@ -25,5 +25,5 @@ __all__ = [
     "ffn_gate_up",
     "grouped_ffn", "layer_forward", "layer_forward_noalloc", "noalloc_scratch_bytes", "pack_expert", "pack_experts", "packed_expert_bytes",
     "permute", "plan_tiers", "read_flags", "route", "route_i8", "router_i8_params",
-    "router_logit_range", "route_workspace_size", "stream_read", "version", "workspace", "workspace_size",
+    "router_logit_range", "route_workspace_size", "stream_read", "stream_read_shaped", "version", "workspace", "workspace_size",
 ]

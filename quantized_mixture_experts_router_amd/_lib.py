@@ -83,6 +83,7 @@ _SIGS = {
     "moe_combine": ([_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
     "moe_layer_forward": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_stream_read": ([_vp, _sz, _i, _vp, _vp], _i),
+    "moe_stream_read_shaped": ([_vp, _sz, _i, _i, _i, _i, _i, _vp, _vp], _i),
     "moe_noalloc_scratch_bytes": ([], _sz),
     "moe_layer_forward_noalloc": ([_vp, _i, _vp, _vp, _vp, ctypes.c_uint32, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp], _i),
     "moe_act_quant_i8": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
@@ -391,6 +392,19 @@ def stream_read(buf, nontemporal=True, sink=None):
         sink = torch.empty(STREAM_BLOCKS, dtype=torch.int32, device=buf.device)
     _check(LIB.moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)),
                                _ptr(sink), _stream()), "moe_stream_read")
+    return sink
+
+
+def stream_read_shaped(buf, blocks, waves=4, inflight=8, layout=0, nontemporal=True, sink=None):
+    """Streaming read with an explicit launch shape (measurement aid); returns
+    the per-block XOR words (uint32 as int32 tensor of `blocks` entries)."""
+    buf = _dev(buf, "buf")
+    if sink is None:
+        sink = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    _check(LIB.moe_stream_read_shaped(_ptr(buf), buf.numel() * buf.element_size(),
+                                      int(bool(nontemporal)), int(blocks), int(waves),
+                                      int(inflight), int(layout), _ptr(sink), _stream()),
+           "moe_stream_read_shaped")
     return sink
 
 

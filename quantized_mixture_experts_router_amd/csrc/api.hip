@@ -646,4 +646,18 @@ moe_status moe_stream_read(const void* src, size_t bytes, int nontemporal, uint3
   return hip_status(launch_stream_read(src, bytes, nontemporal, sink, (hipStream_t)stream));
 }
 
+moe_status moe_stream_read_shaped(const void* src, size_t bytes, int nontemporal, int blocks,
+                                  int waves, int inflight, int layout, uint32_t* sink,
+                                  void* stream) {
+  if (blocks < 1 || blocks > MOE_STREAM_MAX_BLOCKS || waves < 1 || waves > 16 ||
+      (inflight != 1 && inflight != 2 && inflight != 4 && inflight != 8 && inflight != 16) ||
+      (layout != 0 && layout != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink || bytes % 16 != 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_stream_read_shaped(src, bytes, nontemporal, blocks, waves, inflight,
+                                              layout, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

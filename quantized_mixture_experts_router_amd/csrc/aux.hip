@@ -510,7 +510,80 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Shaped streaming read (measurement aid): the same XOR fold, with the
+// launch shape as a parameter, so the read rate can be measured over block
+// counts, block sizes, loads in flight per thread and two layouts:
+//  * interleaved (layout 0): thread t of block b reads chunks
+//    b*nthr + t + j*nthr*blocks, so the grid sweeps the buffer as one front;
+//  * contiguous (layout 1): block b owns one contiguous run of
+//    ceil(n16 / blocks) chunks and sweeps it nthr chunks at a time, the way a
+//    GEMV block streams its own weight rows.
+template <bool NT, int U>
+__global__ __launch_bounds__(1024) void stream_read_shaped_kernel(const u32x4* __restrict__ src,
+                                                                  size_t n16, int layout,
+                                                                  uint32_t* __restrict__ sink) {
+  __shared__ uint32_t part[16];
+  const size_t nthr = blockDim.x;
+  size_t i, stride, end;
+  if (layout == 0) {
+    i = (size_t)blockIdx.x * nthr + threadIdx.x;
+    stride = (size_t)gridDim.x * nthr;
+    end = n16;
+  } else {
+    const size_t chunk = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t b0 = min((size_t)blockIdx.x * chunk, n16);
+    i = b0 + threadIdx.x;
+    stride = nthr;
+    end = min(b0 + chunk, n16);
+  }
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < end; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < end; i += stride) {
+    const u32x4 v = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+  const int nw = blockDim.x / 64;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < nw; ++w) r ^= part[w];
+    sink[blockIdx.x] = r;
+  }
+}
+
+template <bool NT>
+hipError_t launch_shaped(const u32x4* src, size_t n16, int blocks, int waves, int inflight,
+                         int layout, uint32_t* sink, hipStream_t s) {
+  const dim3 grid(blocks), block(64 * waves);
+  switch (inflight) {
+    case 1: hipLaunchKernelGGL((stream_read_shaped_kernel<NT, 1>), grid, block, 0, s, src, n16, layout, sink); break;
+    case 2: hipLaunchKernelGGL((stream_read_shaped_kernel<NT, 2>), grid, block, 0, s, src, n16, layout, sink); break;
+    case 4: hipLaunchKernelGGL((stream_read_shaped_kernel<NT, 4>), grid, block, 0, s, src, n16, layout, sink); break;
+    case 8: hipLaunchKernelGGL((stream_read_shaped_kernel<NT, 8>), grid, block, 0, s, src, n16, layout, sink); break;
+    default: hipLaunchKernelGGL((stream_read_shaped_kernel<NT, 16>), grid, block, 0, s, src, n16, layout, sink); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_stream_read_shaped(const void* src, size_t bytes, int nontemporal, int blocks,
+                                     int waves, int inflight, int layout, uint32_t* sink,
+                                     hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  return nontemporal ? launch_shaped<true>((const u32x4*)src, n16, blocks, waves, inflight, layout, sink, s)
+                     : launch_shaped<false>((const u32x4*)src, n16, blocks, waves, inflight, layout, sink, s);
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                               hipStream_t s) {

@@ -477,6 +477,9 @@ hipError_t launch_ffn_fused(const moe_packed_expert* experts, const int32_t* off
                             uint32_t fmt_mask, uint32_t* flags, int T, int H, int I, int E, int k,
                             const f16* a16, const float* ascale, float* yp, int S_plan,
                             int ns_plan, int* ns_used, hipStream_t s);
+hipError_t launch_stream_read_shaped(const void* src, size_t bytes, int nontemporal, int blocks,
+                                     int waves, int inflight, int layout, uint32_t* sink,
+                                     hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, int nontemporal, uint32_t* sink,
                               hipStream_t s);
 hipError_t launch_pack_matrix(const moe_qmat* a, const moe_qmat* b_or_null, void* codes,

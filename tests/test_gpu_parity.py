@@ -421,6 +421,32 @@ def test_stream_read_xor(moeq, nbytes):
 
 
 
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000003, 3 << 20])
+def test_stream_read_shaped_xor(moeq, nbytes):
+    """Every launch shape of the shaped read covers every word once: the XOR
+    of its per-block words is the XOR of the buffer's words (both layouts,
+    blocks that own no chunk, loads in flight from 1 to 16, tails)."""
+    rng = np.random.default_rng(nbytes + 1)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    want = np.bitwise_xor.reduce(words)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    for blocks, waves, inflight, layout, nt in [(1, 1, 1, 0, False), (7, 3, 2, 1, True),
+                                                (256, 4, 8, 0, True), (1024, 16, 16, 1, False),
+                                                (4096, 4, 4, 1, True), (65536, 2, 16, 0, True)]:
+        sink = moeq.stream_read_shaped(buf, blocks, waves, inflight, layout, nt)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, (blocks, waves, inflight, layout, nt)
+
+
+def test_stream_read_shaped_rejects_bad_shapes(moeq):
+    buf = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for blocks, waves, inflight, layout in [(0, 4, 8, 0), (65537, 4, 8, 0), (8, 0, 8, 0),
+                                            (8, 17, 8, 0), (8, 4, 3, 0), (8, 4, 8, 2)]:
+        with pytest.raises(moeq.MoeError):
+            moeq.stream_read_shaped(buf, blocks, waves, inflight, layout,
+                                    sink=torch.empty(max(blocks, 1), dtype=torch.int32, device="cuda"))
+
 # ----------------------------------------------------- routing profile and tiers
 @pytest.mark.parametrize("T,k,E", [(1, 2, 8), (1000, 6, 256), (70000, 8, 64), (0, 2, 8)])
 def test_expert_histogram(moeq, T, k, E):
