@@ -215,6 +215,16 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
  * closer to the exact result (no fp16 rounding of the decoded weights). The
  * phase entry points (moe_ffn_*) ignore it. */
 #define MOE_MASK_INT8_GEMM (1u << 28)
+/* Bit 27 (MOE_MASK_SHARED_TILE), never set by moe_format_mask: at decode
+ * sizes, run every gate/up and down launch of the two-launch path on the
+ * shared-token-tile GEMV (four wavefronts on four row groups over the same K
+ * tile, the 32 token rows of that tile loaded into LDS once per block).
+ * Without the bit it runs the gate/up launches whose blocks fill at least two
+ * rounds of the device's block slots, and no down launch. The single-launch
+ * decode kernel, where moe_layer_forward takes it, is not affected. Same
+ * results as without the bit up to fp32 summation order. A kernel-selection
+ * control for tuning and tests. */
+#define MOE_MASK_SHARED_TILE (1u << 27)
 uint32_t moe_format_mask(const moe_packed_expert* descs, int E);
 
 /* Workspace bytes the layer entry points need for these sizes, with any

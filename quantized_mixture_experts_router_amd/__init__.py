@@ -5,7 +5,7 @@ include/moeq.h); this package is its thin Python binding.
 """
 from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_LOGIT, ID_NAN,
                    FLAG_FORMAT_NOT_LAUNCHED, FLAG_BAD_SEGMENT, FLAG_EXPERT_SHAPE, FLAG_FP16_RANGE,
-                   MASK_INT8_GEMM, MASK_NO_FUSE, MASK_OUTLIERS, MASK_SPLIT_GU, MOE_BF16, MOE_F32, MOE_W_ASYM, MOE_W_E2M1, EXPORTED, LIB, LIB_PATH,
+                   MASK_INT8_GEMM, MASK_NO_FUSE, MASK_SHARED_TILE, MASK_OUTLIERS, MASK_SPLIT_GU, MOE_BF16, MOE_F32, MOE_W_ASYM, MOE_W_E2M1, EXPORTED, LIB, LIB_PATH,
                    DeviceQMat, MoeError, PackedExperts, act_quant_i8, combine, expert_histogram, ffn_down,
                    ffn_gather, ffn_gate_up, grouped_ffn, layer_forward, layer_forward_noalloc,
                    noalloc_scratch_bytes, pack_expert, pack_experts,
@@ -18,7 +18,7 @@ from ._lib import (ACT_I8_X, ACT_I8_XH, ACT_NONE, FLAG_BAD_EXPERT_ID, FLAG_NAN_L
 __all__ = [
     "ACT_I8_X", "ACT_I8_XH", "ACT_NONE", "FLAG_BAD_EXPERT_ID", "FLAG_NAN_LOGIT", "ID_NAN",
     "FLAG_FORMAT_NOT_LAUNCHED", "FLAG_BAD_SEGMENT", "FLAG_EXPERT_SHAPE", "FLAG_FP16_RANGE",
-    "MASK_INT8_GEMM", "MASK_NO_FUSE", "MASK_OUTLIERS", "MASK_SPLIT_GU", "MOE_BF16",
+    "MASK_INT8_GEMM", "MASK_NO_FUSE", "MASK_SHARED_TILE", "MASK_OUTLIERS", "MASK_SPLIT_GU", "MOE_BF16",
     "MOE_F32", "MOE_W_ASYM", "MOE_W_E2M1", "EXPORTED", "LIB", "LIB_PATH", "DeviceQMat",
     "MoeError", "PackedExperts", "act_quant_i8", "combine", "expert_histogram", "ffn_down",
     "ffn_gather",

@@ -63,6 +63,7 @@ MASK_SPLIT_GU = 1 << 31
 MASK_NO_FUSE = 1 << 30
 MASK_OUTLIERS = 1 << 29
 MASK_INT8_GEMM = 1 << 28
+MASK_SHARED_TILE = 1 << 27
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {

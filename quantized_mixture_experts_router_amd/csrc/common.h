@@ -41,6 +41,7 @@ constexpr uint32_t kMaskSplitGU = MOE_MASK_SPLIT_GU;
 constexpr uint32_t kMaskNoFuse = MOE_MASK_NO_FUSE;
 constexpr uint32_t kMaskOutliers = MOE_MASK_OUTLIERS;
 constexpr uint32_t kMaskInt8 = MOE_MASK_INT8_GEMM;
+constexpr uint32_t kMaskSharedTile = MOE_MASK_SHARED_TILE;
 constexpr int kMaxE = 256;  // experts per layer
 static_assert(F_COUNT <= 28, "format mask bits");
 

@@ -576,6 +576,80 @@ __device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t sof
 #define MOEQ_DEC_OUTB 3
 #endif
 
+// End of a decode wavefront: outlier corrections and stores of its two
+// output tiles, for the accumulator registers r whose bit is set in `regs`
+// (v0, v1: the tiles' register values, K partial sums already added).
+template <class F, int ROLE>
+__device__ inline void decode_finish(const FfnArgs& a, const Task& t, const moe_packed_expert* ex,
+                                     rsrc_t rA, int rg, int split, int lane, uint32_t regs,
+                                     float (&v0)[16], float (&v1)[16]) {
+  const int n = lane & 31;
+  bool over = false;
+  // Outliers of the matrix, added once (by the K split that starts at 0):
+  // per output column, each listed weight's correction times the rows'
+  // inputs at its column. Entries go four at a time: their loads, then all
+  // the rows' input loads of the four, then the products, so a list costs
+  // a quarter as many memory round trips as its length.
+  const uint32_t* orp;
+  const OutEntry* oen;
+  if (role_outliers<ROLE>(ex, orp, oen) && split == 0) {
+    constexpr int B = MOEQ_DEC_OUTB;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int lr = outlier_row<ROLE>(a.N, rg, tt, n);
+      const int b0 = (int)orp[lr], c = (int)orp[lr + 1] - b0;
+      const OutEntry* en = oen + b0;
+      for (int j = 0; j < c; j += B) {
+        uint32_t kk[B];
+        float dd[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int e = min(j + u, c - 1);
+          kk[u] = en[e].k;
+          dd[u] = en[e].delta;
+        }
+        f16 x[B][16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!((regs >> r) & 1)) continue;
+          const uint32_t ro = (uint32_t)(t.row0 + min(acc_row(r, lane), t.mcount - 1)) * a.K;
+#pragma unroll
+          for (int u = 0; u < B; ++u)
+            x[u][r] = __builtin_bit_cast(f16, bload<uint16_t>(rA, (ro + kk[u]) * 2, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          if (j + u >= c) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (!((regs >> r) & 1)) continue;
+            if (tt) v1[r] = fmaf(dd[u], (float)x[u][r], v1[r]);
+            else v0[r] = fmaf(dd[u], (float)x[u][r], v0[r]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (!((regs >> r) & 1)) continue;
+    const int i = acc_row(r, lane);
+    if (i < t.mcount) {
+      const int row = t.row0 + i;
+      if constexpr (ROLE == R_GU) {
+        over |= store_gu(a, row, 32 * rg + n, v0[r], v1[r]);
+      } else if constexpr (ROLE == R_DN) {
+        store_dn(a, split, row, 64 * rg + n, v0[r]);
+        store_dn(a, split, row, 64 * rg + 32 + n, v1[r]);
+      } else {
+        over |= store_split<ROLE>(a, row, 64 * rg + n, v0[r]);
+        over |= store_split<ROLE>(a, row, 64 * rg + 32 + n, v1[r]);
+      }
+    }
+  }
+  if (over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
+}
+
 template <class F, int ROLE>
 __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw) {
   constexpr bool GU = ROLE == R_GU;
@@ -691,7 +765,6 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   if (!on) return;
   const int RPW = 16 / ksw;
   const int w0 = grp * ksw;
-  bool over = false;
   // this wavefront's rows: registers r of its K-split share that hold rows
   auto mine = [&](int r) { return r / RPW == ks && live(r); };
   float v0[16], v1[16];
@@ -707,75 +780,186 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
       v1[r] += red[(((w0 + w) * 2 + 1) * 16 + r) * 64 + lane];
     }
   }
-  // Outliers of the matrix, added once (by the K split that starts at 0):
-  // per output column, each listed weight's correction times the rows'
-  // inputs at its column. Entries go four at a time: their loads, then all
-  // the rows' input loads of the four, then the products, so a list costs
-  // a quarter as many memory round trips as its length.
-  const uint32_t* orp;
-  const OutEntry* oen;
-  if (role_outliers<ROLE>(ex, orp, oen) && split == 0) {
-    constexpr int B = MOEQ_DEC_OUTB;
+  uint32_t regs = 0;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int lr = outlier_row<ROLE>(a.N, rg, tt, n);
-      const int b0 = (int)orp[lr], c = (int)orp[lr + 1] - b0;
-      const OutEntry* en = oen + b0;
-      for (int j = 0; j < c; j += B) {
-        uint32_t kk[B];
-        float dd[B];
+  for (int r = 0; r < 16; ++r) regs |= mine(r) ? 1u << r : 0u;
+  decode_finish<F, ROLE>(a, t, ex, rA, rg, split, lane, regs, v0, v1);
+}
+
+// Decode GEMV with a shared token tile (launches with enough row groups to
+// fill the device): the 4 wavefronts of a block own 4
+// consecutive row groups and stream the same K tile of their weights at the
+// same time, so the block's 32 token rows of that K tile reach LDS once, by
+// DMA (buffer loads with an LDS destination), instead of once per wavefront
+// through the vector memory path. The token-row loads of the per-wavefront
+// kernel move twice the weight bytes through each CU's load path, from L2.
+// LDS holds a ring of three token tiles: at the start of tile i a wavefront
+// waits for its own DMA of tile i, the block meets at one barrier (every
+// DMA of tile i has landed, every wavefront is done with tile i-1), then the
+// DMA of tile i+2 goes into tile i-1's buffer and the weight codes of tile
+// i+2 into tile i-1's register slot, and tile i is computed. Token rows are
+// stored with their 16-byte chunks swizzled as in the prefill kernel, so the
+// A-fragment reads of 16 lanes fall on 16 different 4-bank groups. The
+// down projection's blocks take the K range of their split (blockIdx.y).
+template <class F, int ROLE>
+__global__ __launch_bounds__(kThreads) void ffn_decode_sa_kernel(FfnArgs a) {
+  constexpr bool GU = ROLE == R_GU;
+  constexpr int ROWB = F::KT * 2;              // bytes of a token row's K tile
+  constexpr int TILEB = 32 * ROWB;             // 4 KiB (KT 64) or 8 KiB (KT 128)
+  constexpr int CPR = F::KT / 8;               // 16-byte chunks per row
+  constexpr int NI = TILEB / (kThreads * 16);  // DMA instructions per wavefront and tile
+  constexpr int RPI = 64 / CPR;                // token rows one DMA instruction fills
+  // three arrays, not one: the compiler can then tell that the DMA into one
+  // buffer does not feed the reads of another and waits only where needed
+  __shared__ __attribute__((aligned(1024))) uint8_t tk0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tk1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tk2[TILEB];
+  const int NRG = GU ? a.N / 32 : a.N / 64;
+  const int NB = (NRG + 3) / 4;
+  Task t;
+  if (!find_task<ROLE>(a, F::ID, 32, NB, blockIdx.x, t)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, kh = lane >> 5;
+  const int rg = t.nt * 4 + wave;
+  const bool on = rg < NRG;
+  const int KTn = a.K / F::KT;
+  const int NE = a.K / F::GE;
+  const moe_packed_expert* ex = a.experts + t.e;
+  const uint8_t *codes, *params;
+  role_matrix<ROLE>(ex, codes, params);
+  const int rt0 = 2 * min(rg, NRG - 1);  // a group past the end streams a valid pair
+  const int NRT = GU ? 2 * a.N / 32 : a.N / 32;
+  const rsrc_t rC = make_rsrc(uniform_ptr(codes), (uint32_t)((size_t)NRT * KTn * F::TB));
+  const rsrc_t rP = make_rsrc(uniform_ptr(params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
+  const uint32_t vc0 = (uint32_t)rt0 * KTn * F::TB + lane * F::CB;
+  const uint32_t vc1 = vc0 + (uint32_t)KTn * F::TB;
+  const uint32_t vh0 = (uint32_t)rt0 * KTn * F::TB + F::HOFF + lane * 8;
+  const uint32_t vh1 = vh0 + (uint32_t)KTn * F::TB;
+  const uint32_t vp0 =
+      ((uint32_t)rt0 * NE * 32 + n + (F::GE <= F::KT ? kh * (F::SPAN / F::GE) : 0) * 32) * F::EB;
+  const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
+  const DeqConsts dk = make_deq_consts<F>();
+  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
+
+  // DMA slots: instruction j of wavefront w fills slots [(w NI + j) 64, +64)
+  // of a buffer, one 16-byte slot per lane; slot -> (row, stored chunk) ->
+  // logical chunk. Rows past the segment repeat its last row. A wavefront
+  // whose slots hold only such rows issues no DMA at all (block-uniform per
+  // wavefront, so its wait counts stay exact): at a handful of rows most
+  // of the tile is never loaded, and those rows' outputs are never stored.
+  auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
+  const bool dma_on = wave * NI * RPI < t.mcount;
+  uint32_t doff[NI];
 #pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int e = min(j + u, c - 1);
-          kk[u] = en[e].k;
-          dd[u] = en[e].delta;
-        }
-        f16 x[B][16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (!mine(r)) continue;
-          const uint32_t ro = (uint32_t)(t.row0 + min(acc_row(r, lane), t.mcount - 1)) * a.K;
-#pragma unroll
-          for (int u = 0; u < B; ++u)
-            x[u][r] = __builtin_bit_cast(f16, bload<uint16_t>(rA, (ro + kk[u]) * 2, 0));
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          if (j + u >= c) continue;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (!mine(r)) continue;
-            if (tt) v1[r] = fmaf(dd[u], (float)x[u][r], v1[r]);
-            else v0[r] = fmaf(dd[u], (float)x[u][r], v0[r]);
-          }
-        }
-      }
-    }
+  for (int j = 0; j < NI; ++j) {
+    const int slot = (wave * NI + j) * 64 + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    const int c = pc ^ swz(r);
+    doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
   }
+  const int split = blockIdx.y;
+  const int per = (KTn + a.splits - 1) / a.splits;
+  const int kb = split * per, nt = max(min(KTn, kb + per) - kb, 0);
+  auto tile_of = [&](int i) { return min(kb + i, KTn - 1); };
+  auto load_b = [&](int i, BTile<F>& b) {
+    const int kt = tile_of(i);
+    b.w0 = load_codes<F, kNT>(rC, vc0, vh0, (uint32_t)kt * F::TB);
+    b.w1 = load_codes<F, kNT>(rC, vc1, vh1, (uint32_t)kt * F::TB);
+    const uint32_t sp = (uint32_t)(kt * F::KT / F::GE) * 32 * F::EB;
+    b.q0.template load<kNT>(rP, vp0, sp);
+    b.q1.template load<kNT>(rP, vp1, sp);
+  };
+  f32x16 acc0 = {}, acc1 = {};
+  auto compute = [&](const uint8_t* buf, const BTile<F>& b) {
+    f16x8 av[F::STEPS];
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s) {
+      const int c = (kh * (F::SPAN / 8) + s) ^ swz(n);
+      av[s] = *reinterpret_cast<const f16x8*>(buf + n * ROWB + c * 16);
+    }
+#pragma unroll
+    for (int s = 0; s < F::STEPS; ++s) {
+      const f16x8 b0 = dequant_step<F>(b.w0, b.q0, s, dk);
+      const f16x8 b1 = dequant_step<F>(b.w1, b.q1, s, dk);
+      acc0 = mfma32(av[s], b0, acc0);
+      acc1 = mfma32(av[s], b1, acc1);
+    }
+  };
+  // memory operations per tile: this wavefront's DMA instructions (if it
+  // has any), then the weight loads (codes and parameters of two row tiles)
+  constexpr int LPT = 2 * code_loads<F>() + 2;
+  // The loop is instantiated with and without the DMA, so that the compiler's
+  // own wait counts (for the weight registers) are exact on each path: with
+  // one loop whose DMA is conditional, it waits on both paths as if the DMA
+  // were missing, i.e. for the last DMA and more weight loads than needed.
+  auto run = [&](auto dma_c) {
+    constexpr bool D = decltype(dma_c)::value;
+    auto dma = [&](int i, uint8_t* buf) {
+      if constexpr (D) {
+        const uint32_t so = (uint32_t)tile_of(i) * ROWB;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) dma16(rA, buf + (wave * NI + j) * 1024, doff[j], so);
+      }
+    };
+    // in flight at the start of tile i: weights i, DMA i+1, weights i+1
+    constexpr int VM = 2 * LPT + (D ? NI : 0);
+    auto step = [&](int i, const uint8_t* cur, uint8_t* nxt2, const BTile<F>& cb, BTile<F>& nb2) {
+      if constexpr (D) __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      dma(i + 2, nxt2);
+      load_b(i + 2, nb2);
+      compute(cur, cb);
+    };
+    // the nt tiles of the split's K range; prefetches past its end re-read
+    // a valid tile (unused)
+    BTile<F> B0, B1, B2;
+    dma(0, tk0);
+    load_b(0, B0);
+    dma(1, tk1);
+    load_b(1, B1);
+    // whole rounds of three tiles, then the last one or two: no branch
+    // inside the loop body, so its wait counts are the steady state's
+    int i = 0;
+    for (; i + 3 <= nt; i += 3) {
+      step(i, tk0, tk2, B0, B2);
+      step(i + 1, tk1, tk0, B1, B0);
+      step(i + 2, tk2, tk1, B2, B1);
+    }
+    if (i < nt) step(i, tk0, tk2, B0, B2);
+    if (i + 1 < nt) step(i + 1, tk1, tk0, B1, B0);
+    // no DMA may still be in flight when the block's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  if (dma_on)
+    run(IntC<1>{});
+  else
+    run(IntC<0>{});
+  if (!on) return;
+  const int mrows = __builtin_amdgcn_readfirstlane(t.mcount);
+  uint32_t regs = 0;
+  float v0[16], v1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (!mine(r)) continue;
-    const int i = acc_row(r, lane);
-    if (i < t.mcount) {
-      const int row = t.row0 + i;
-      if constexpr (ROLE == R_GU) {
-        over |= store_gu(a, row, 32 * rg + n, v0[r], v1[r]);
-      } else if constexpr (ROLE == R_DN) {
-        store_dn(a, split, row, 64 * rg + n, v0[r]);
-        store_dn(a, split, row, 64 * rg + 32 + n, v1[r]);
-      } else {
-        over |= store_split<ROLE>(a, row, 64 * rg + n, v0[r]);
-        over |= store_split<ROLE>(a, row, 64 * rg + 32 + n, v1[r]);
-      }
-    }
+    v0[r] = acc0[r];
+    v1[r] = acc1[r];
+    regs |= 8 * (r >> 2) + (r & 3) < mrows ? 1u << r : 0u;
   }
-  if (over && a.flags) atomicOr(a.flags, (uint32_t)MOE_FLAG_FP16_RANGE);
+  decode_finish<F, ROLE>(a, t, ex, rA, rg, split, lane, regs, v0, v1);
 }
 
 // decode: fewest K tiles a wavefront of a K-split group streams
 #ifndef MOEQ_DEC_MINT
 #define MOEQ_DEC_MINT 16
 #endif
+// decode: rounds of block slots the shared-token-tile kernel's gate/up
+// blocks must fill (fewer: Mixtral-shaped gate/up at 8 tokens, 1.02 rounds,
+// measured 5% slower on it, at 32 tokens, 1.17 rounds, 5% faster)
+#ifndef MOEQ_DEC_SA_ROUNDS
+#define MOEQ_DEC_SA_ROUNDS 2
+#endif
+
 
 // ===========================================================================
 // Prefill family
@@ -1221,6 +1405,27 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   constexpr bool GU = ROLE == R_GU;
   constexpr bool DN = ROLE == R_DN;
   if (decode) {
+    // the shared-token-tile kernel for the gate/up roles when its blocks (one
+    // per touched expert and set of 4 row groups, counting each touched
+    // expert as one 32-row tile) fill at least MOEQ_DEC_SA_ROUNDS rounds of
+    // the device's block slots; for any role when the caller's mask asks for
+    // it. (The down projection measured no faster on it: W4A8 at 16 tokens in
+    // two K splits the same, Mixtral at 8 and 32 tokens in the twelve splits
+    // two rounds need 16-25% slower.)
+    {
+      const int NRG = GU ? a.N / 32 : a.N / 64;
+      const long sa_blocks = (long)(a.R < a.E ? a.R : a.E) * ((NRG + 3) / 4);
+      int bpc = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void*)ffn_decode_sa_kernel<F, ROLE>,
+                                                       kThreads, 0) != hipSuccess || bpc <= 0)
+        bpc = 1;
+      if ((a.fmt_mask & kMaskSharedTile) ||
+          (!DN && sa_blocks >= (long)(MOEQ_DEC_SA_ROUNDS * device_cus() * bpc))) {
+        dim3 grid(max_tiles(a.R, a.E, 32) * ((NRG + 3) / 4), DN ? a.splits : 1);
+        hipLaunchKernelGGL((ffn_decode_sa_kernel<F, ROLE>), grid, dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     // wavefronts splitting K inside a block: as many as keep >= 16 K tiles
     // (per split) on each; when few weight rows are in flight (a handful of
     // tokens on small experts) streams of >= 8 tiles on more wavefronts

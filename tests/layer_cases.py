@@ -60,12 +60,15 @@ def prefill_order(T, H, I, E, k, bm=128, blocks_per_cu=2):
     longest first below that (lpt 1; the down projection uses four size
     classes below 2 blocks per slot, lpt 2)."""
     R = T * k
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
     if R < 48 * E:
         te = min(R, E)
         if T <= 32 and R <= te and te * (I // 64) >= 256:
             return "fused decode kernel (one row per expert)"
-        return "decode GEMV"
-    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+        # gate/up on the shared-token-tile kernel from two rounds of its block
+        # slots (three blocks per CU)
+        sa = te * ((I // 32 + 3) // 4) >= 2 * 3 * cus
+        return "decode GEMV" + (", gate/up with a shared token tile" if sa else "")
     slots = cus * blocks_per_cu
     tiles = (R + bm - 1) // bm + min(R, E)
     out = []

@@ -242,6 +242,10 @@ LAYER_CASES = [
     # expert-major prefill order: 2304 gate/up blocks, at least 4 per block slot
     # of a 256-CU device (the down launch, 72 blocks, takes the four-class order)
     ("mixtral", 4096, 256, 4096, 8, 2),
+    # decode gate/up on the shared-token-tile kernel without the mask bit
+    # (64 experts x 16 blocks of 4 row groups: two rounds of a 256-CU
+    # device's block slots)
+    ("mixtral", 64, 256, 4096, 64, 2),
 ]
 
 
@@ -745,6 +749,52 @@ def test_layer_parity_matrix_formats_and_outliers(moeq, name, T, H, I, E, k, kin
         err0 = rel_l2_rows(out0.cpu().numpy()[ok], ref["out"][ok])
         _say(f"    without the side lists: max row rel-L2 {err0.max():.3e}")
         assert err0.max() > 4 * err.max()
+
+
+SHARED_TILE_CASES = [
+    # name, T, H, I, E, k, kind (None: the workload's formats), outlier share
+    ("mixtral", 40, 640, 1024, 8, 2, None, 0.0),    # 4-bit: 10 K tiles (ring of three, ragged)
+    ("fine_e2m1", 70, 640, 512, 32, 6, None, 0.0),  # e2m1
+    ("hotcold", 150, 640, 256, 32, 8, None, 0.0),   # 2-bit (two DMAs per wavefront and tile),
+                                                    # skewed: several 32-row tiles per hot expert
+    ("w4a8", 16, 1024, 512, 8, 2, None, 0.0),       # int8 expert inputs and h
+    ("mixtral", 8, 256, 4096, 8, 2, None, 0.0),     # down projection in two K splits
+    ("mixtral", 1, 512, 4096, 8, 2, None, 0.0),     # one row: one wavefront loads the tile
+    ("mixtral", 40, 640, 512, 8, 2, "mixed", 0.005),  # 3-bit (two code loads), outlier lists
+    ("mixtral", 40, 640, 512, 8, 2, "split", 0.005),  # split gate and up roles, 1-bit
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,kind,frac", SHARED_TILE_CASES)
+def test_shared_tile_decode(moeq, name, T, H, I, E, k, kind, frac):
+    """The shared-token-tile decode GEMV, forced on every gate/up and down
+    launch by MOE_MASK_SHARED_TILE, against the oracle."""
+    from dataclasses import replace
+    cfg = synth.scaled_config(name, T=T, H=H, I=I, E=E, k=k, weight_mode="quantize",
+                              n_hot=min(64, E // 4) if name == "hotcold" else None)
+    if kind is not None:
+        cfg = replace(cfg, matrix_fmts=_fmt_plan(kind, E), weight_outlier_frac=frac)
+    order = prefill_order(T, H, I, E, k)
+    _say(f"[shared tile] {name} T={T} H={H} I={I} E={E} k={k} {kind} outliers={frac} "
+         f"act={cfg.act} ({order})")
+    assert "GEMV" in order
+    wl = Workload(cfg)
+    full = wl.packed.fmt_mask
+    ws = moeq.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.act)
+    try:
+        wl.packed.fmt_mask = full | moeq.MASK_SHARED_TILE
+        out, ids, w = moeq.layer_forward(wl.x, wl.Wr, wl.b, wl.packed, cfg.k, act=cfg.act, ws=ws)
+    finally:
+        wl.packed.fmt_mask = full
+    torch.cuda.synchronize()
+    assert moeq.read_flags(ws) == 0
+    ref = oracle.moe_layer(wl.x_np, cfg.x_dtype, wl.Wr_np, wl.b_np if cfg.zipf_alpha > 0 else None,
+                           wl.expert, cfg.E, cfg.k, act=cfg.act)
+    ok = ~ref["flagged"]
+    np.testing.assert_array_equal(ids.cpu().numpy()[ok], ref["ids"][ok])
+    err = rel_l2_rows(out.cpu().numpy()[ok], ref["out"][ok])
+    _say(f"    max row rel-L2 {err.max():.3e}")
+    assert err.max() <= tolerance(cfg), err.max()
 
 
 @pytest.mark.parametrize("T", [40, 600])
