@@ -219,8 +219,9 @@ moe_status moe_pack_expert(const moe_expert_canon* src, void* dst_dev, size_t ds
  * sizes, run every gate/up and down launch of the two-launch path on the
  * shared-token-tile GEMV (four wavefronts on four row groups over the same K
  * tile, the 32 token rows of that tile loaded into LDS once per block).
- * Without the bit it runs the gate/up launches whose blocks fill at least two
- * rounds of the device's block slots, and no down launch. The single-launch
+ * Without the bit it runs the launches whose wavefront streams are short (at
+ * most 32 K tiles) and whose blocks fill a round of the device's block slots,
+ * and the gate/up launches whose blocks fill two rounds. The single-launch
  * decode kernel, where moe_layer_forward takes it, is not affected. Same
  * results as without the bit up to fp32 summation order. A kernel-selection
  * control for tuning and tests. */

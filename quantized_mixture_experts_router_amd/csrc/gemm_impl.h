@@ -959,6 +959,11 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_sa_kernel(FfnArgs a) {
 #ifndef MOEQ_DEC_SA_ROUNDS
 #define MOEQ_DEC_SA_ROUNDS 2
 #endif
+// decode: longest per-wavefront stream (K tiles) for which the
+// shared-token-tile kernel runs from one round of block slots
+#ifndef MOEQ_DEC_SA_SHORT
+#define MOEQ_DEC_SA_SHORT 32
+#endif
 
 
 // ===========================================================================
@@ -1052,26 +1057,34 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
   const uint32_t vp1 = vp0 + (uint32_t)NE * 32 * F::EB;
 
   const DeqConsts dk = make_deq_consts<F>();
-  // Token tile DMA: instruction j of wavefront w fills LDS slots
-  // [(w NI + j) 64, +64) of the buffer, one 16-byte slot per lane. Slot ->
-  // (row, stored chunk) -> logical chunk; rows past the segment repeat its
-  // last row (their outputs are never stored). Offsets are in bytes from
-  // the start of K tile kt of the token matrix.
+  // Token tile DMA: the block's instruction g fills LDS slots [64 g, +64) of
+  // the buffer, one 16-byte slot per lane. Slot -> (row, stored chunk) ->
+  // logical chunk; rows past the segment repeat its last row (their outputs
+  // are never stored). Offsets are in bytes from the start of K tile kt of
+  // the token matrix. The NQ instructions of each 32-row sub-tile per
+  // wavefront are shared out over the wavefronts (instruction j of
+  // wavefront w: sub-tile j / NQ, g = (j / NQ) NQ kPW + (j % NQ) kPW + w),
+  // so a partial m-tile with AMT filled sub-tiles loads only those, with
+  // the same AMT NQ instructions on every wavefront (exact wait counts).
   // 128-byte rows: two rows per 64 banks, so rows 2i and 2i+1 share a chunk
   // pattern and differ in bank half; 256-byte rows fill all banks each.
+  static_assert(NI % kMT == 0 && (NI / kMT) * kPW * 64 == 32 * CPR, "DMA instructions per sub-tile");
+  constexpr int NQ = NI / kMT;
   auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
+  auto dslot = [&](int j) { return (j / NQ) * NQ * kPW + (j % NQ) * kPW + wave; };
   uint32_t doff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int slot = (wave * NI + j) * 64 + lane;
+    const int slot = dslot(j) * 64 + lane;
     const int r = slot / CPR, pc = slot % CPR;
     const int c = pc ^ swz(r);
     doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
   }
-  auto dma_a = [&](int kt, uint8_t* buf) {
+  // the DMA of K tile kt's first AMT sub-tiles
+  auto dma_a = [&](int kt, uint8_t* buf, auto amt_c) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16(rA, buf + (wave * NI + j) * 1024, doff[j], (uint32_t)kt * ROWB);
+    for (int j = 0; j < decltype(amt_c)::value * NQ; ++j)
+      dma16(rA, buf + dslot(j) * 1024, doff[j], (uint32_t)kt * ROWB);
   };
   auto load_b = [&](int kt, BTile<F>& b) {
     b.w0 = load_codes<F>(rC, vc0, vh0, (uint32_t)kt * F::TB);
@@ -1213,26 +1226,27 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
       // Three token buffers, three weight slots: the DMA of token tile kt+2
       // goes out at the start of tile kt (into the buffer tile kt-1 used) and
       // the weight codes of tile kt+3 at its end, so both are fetched two full
-      // tiles ahead. At the start of tile kt everything but the last 8 + NI
-      // memory operations (weights kt+1, DMA kt+1, weights kt+2) has landed.
+      // tiles ahead. At the start of tile kt everything but the last
+      // 2 LPT + AMT NQ memory operations (weights kt+1, DMA kt+1, weights
+      // kt+2) has landed.
       BTile<F> R2;
       // memory operations of one tile's weights (codes of two row tiles and
       // their parameters); weights kt+1, DMA kt+1 and weights kt+2 may stay
       // in flight
       constexpr int LPT = 2 * code_loads<F>() + 2;
-      constexpr int VM = 2 * LPT + NI;
+      constexpr int VM = 2 * LPT + AMT * NQ;
       auto tile = [&](int kt, uint8_t* cur, uint8_t* next2, BTile<F>& slot) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        dma_a(min(kt + 2, KTn - 1), next2);
+        dma_a(min(kt + 2, KTn - 1), next2, amt_c);
         mma_jit(cur, slot);
         load_b(min(kt + 3, KTn - 1), slot);
       };
       load_b(0, R0);
-      dma_a(0, lds0);
+      dma_a(0, lds0, amt_c);
       load_b(min(1, KTn - 1), R1);
-      dma_a(min(1, KTn - 1), lds1);
+      dma_a(min(1, KTn - 1), lds1, amt_c);
       load_b(min(2, KTn - 1), R2);
       int kt = 0;
       for (; kt + 2 < KTn; kt += 3) {
@@ -1252,9 +1266,9 @@ __global__ __launch_bounds__(64 * kPW, kBPC) void ffn_prefill_kernel(FfnArgs a) 
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // past the last tile this re-fills the idle buffer (no branch in the loop)
-        dma_a(min(kt + 1, KTn - 1), next);
+        dma_a(min(kt + 1, KTn - 1), next, amt_c);
       };
-      dma_a(0, lds0);
+      dma_a(0, lds0, amt_c);
       load_b(0, R0);
       load_b(min(1, KTn - 1), R1);
       int kt = 0;
@@ -1405,22 +1419,31 @@ hipError_t launch_one(const FfnArgs& a, bool decode, hipStream_t s) {
   constexpr bool GU = ROLE == R_GU;
   constexpr bool DN = ROLE == R_DN;
   if (decode) {
-    // the shared-token-tile kernel for the gate/up roles when its blocks (one
-    // per touched expert and set of 4 row groups, counting each touched
-    // expert as one 32-row tile) fill at least MOEQ_DEC_SA_ROUNDS rounds of
-    // the device's block slots; for any role when the caller's mask asks for
-    // it. (The down projection measured no faster on it: W4A8 at 16 tokens in
-    // two K splits the same, Mixtral at 8 and 32 tokens in the twelve splits
-    // two rounds need 16-25% slower.)
+    // The shared-token-tile kernel, whose blocks (one per touched expert,
+    // set of 4 row groups and K split, counting each touched expert as one
+    // 32-row tile) stream every K tile of their split on each wavefront:
+    //  * when those streams are short (at most MOEQ_DEC_SA_SHORT K tiles)
+    //    and the blocks fill at least one round of the device's block slots:
+    //    the 256-expert layers at 64 tokens (down 15-21%, gate/up 6-16%
+    //    faster), where the per-wavefront kernel splits K little or not at
+    //    all and so has about as many blocks;
+    //  * for gate/up, when the blocks fill at least MOEQ_DEC_SA_ROUNDS
+    //    rounds (W4A8 at 16 tokens: 4% faster). With fewer rounds the long
+    //    blocks leave a slow tail (Mixtral gate/up at 8 tokens, 1.02 rounds:
+    //    7% slower); its down launches, long streams over few blocks, were
+    //    slower on it at every size measured;
+    //  * for any launch when the caller's mask asks for it.
     {
       const int NRG = GU ? a.N / 32 : a.N / 64;
-      const long sa_blocks = (long)(a.R < a.E ? a.R : a.E) * ((NRG + 3) / 4);
+      const int KTw = (a.K / F::KT + a.splits - 1) / a.splits;
+      const long sa_blocks = (long)(a.R < a.E ? a.R : a.E) * ((NRG + 3) / 4) * a.splits;
       int bpc = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, (const void*)ffn_decode_sa_kernel<F, ROLE>,
                                                        kThreads, 0) != hipSuccess || bpc <= 0)
         bpc = 1;
-      if ((a.fmt_mask & kMaskSharedTile) ||
-          (!DN && sa_blocks >= (long)(MOEQ_DEC_SA_ROUNDS * device_cus() * bpc))) {
+      const long slots = (long)device_cus() * bpc;
+      if ((a.fmt_mask & kMaskSharedTile) || (KTw <= MOEQ_DEC_SA_SHORT && sa_blocks >= slots) ||
+          (!DN && sa_blocks >= MOEQ_DEC_SA_ROUNDS * slots)) {
         dim3 grid(max_tiles(a.R, a.E, 32) * ((NRG + 3) / 4), DN ? a.splits : 1);
         hipLaunchKernelGGL((ffn_decode_sa_kernel<F, ROLE>), grid, dim3(kThreads), 0, s, a);
         return hipGetLastError();

@@ -66,8 +66,10 @@ def prefill_order(T, H, I, E, k, bm=128, blocks_per_cu=2):
         if T <= 32 and R <= te and te * (I // 64) >= 256:
             return "fused decode kernel (one row per expert)"
         # gate/up on the shared-token-tile kernel from two rounds of its block
-        # slots (three blocks per CU)
-        sa = te * ((I // 32 + 3) // 4) >= 2 * 3 * cus
+        # slots (three blocks per CU), or from one with short K streams
+        # (4-bit tiles of 64 columns)
+        gu_blocks = te * ((I // 32 + 3) // 4)
+        sa = gu_blocks >= 2 * 3 * cus or (H // 64 <= 32 and gu_blocks >= 3 * cus)
         return "decode GEMV" + (", gate/up with a shared token tile" if sa else "")
     slots = cus * blocks_per_cu
     tiles = (R + bm - 1) // bm + min(R, E)
