@@ -39,6 +39,9 @@ __device__ inline T* uniform_ptr(T* p) {
 }
 // descriptor of `bytes` bytes at p (raw buffer: no stride, no format);
 // loads past the end return zero
+// A buffer offset past every range this library builds (ranges stay below
+// 2 GiB): loads at it return zeros without a memory access.
+constexpr uint32_t kPastRange = 0x80000000u;
 __device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }

@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fused_decode_kernel(FusedArgs
     const rsrc_t rC = make_rsrc(uniform_ptr(ex->gu_codes), (uint32_t)((size_t)NRT * KTn * F::TB));
     const rsrc_t rP =
         make_rsrc(uniform_ptr(ex->gu_params), (uint32_t)((size_t)NRT * NE * 32 * F::EB));
-    const uint32_t va = ((uint32_t)(t.row0 + (n < t.mcount ? n : 0)) * H + kh * F::SPAN) * 2;
+    // rows past the segment: an offset past the buffer's range (zeros, no
+    // memory access; their MFMA rows are never stored)
+    const uint32_t va = n < t.mcount ? ((uint32_t)(t.row0 + n) * H + kh * F::SPAN) * 2 : kPastRange;
     // tiles of this wavefront: unit u0 + i / per, K tile ks + ksw (i % per)
     const int per = (KTn - ks + ksw - 1) / ksw;
     const int nt = upw * per;

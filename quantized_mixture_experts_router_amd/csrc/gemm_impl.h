@@ -695,9 +695,14 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   const int per = (KTn + a.splits - 1) / a.splits;
   const int kb = split * per, ke = min(KTn, kb + per);
 
+  // Lanes of rows past the segment take an offset past the buffer's range:
+  // their loads return zeros without a memory access (buffer range check),
+  // and their MFMA rows are never stored. Those loads used to re-read the
+  // tile's first row: at a few rows per expert most of the token-row loads,
+  // which moved twice the weight bytes through each CU's load path.
   const bool arow = n < t.mcount;
   const rsrc_t rA = make_rsrc(a.a, (uint32_t)((size_t)a.R * a.K * 2));
-  const uint32_t va = ((uint32_t)(t.row0 + (arow ? n : 0)) * a.K + kh * F::SPAN) * 2;
+  const uint32_t va = arow ? ((uint32_t)(t.row0 + n) * a.K + kh * F::SPAN) * 2 : kPastRange;
 
   struct AFrag {
     f16x8 v[F::STEPS];
@@ -717,8 +722,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   };
   auto load_a = [&](int i, AFrag& af) {
     const int kt = tile_of(i);
-    // every lane loads: rows past the tile read the tile's first row, and
-    // their outputs (MFMA rows of their own) are never stored
+    // every lane loads: rows past the segment read zeros (offset past the
+    // range), and their outputs (MFMA rows of their own) are never stored
 #pragma unroll
     for (int s = 0; s < F::STEPS; ++s)
       af.v[s] = bload<f16x8>(rA, va, (uint32_t)(kt * F::KT + 8 * s) * 2);
@@ -844,10 +849,10 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_sa_kernel(FfnArgs a) {
 
   // DMA slots: instruction j of wavefront w fills slots [(w NI + j) 64, +64)
   // of a buffer, one 16-byte slot per lane; slot -> (row, stored chunk) ->
-  // logical chunk. Rows past the segment repeat its last row. A wavefront
-  // whose slots hold only such rows issues no DMA at all (block-uniform per
-  // wavefront, so its wait counts stay exact): at a handful of rows most
-  // of the tile is never loaded, and those rows' outputs are never stored.
+  // logical chunk. Rows past the segment take an offset past the buffer's
+  // range (no memory access; their LDS rows feed MFMA rows that are never
+  // stored). A wavefront whose slots hold only such rows issues no DMA at
+  // all (block-uniform per wavefront, so its wait counts stay exact).
   auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
   const bool dma_on = wave * NI * RPI < t.mcount;
   uint32_t doff[NI];
@@ -856,7 +861,7 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_sa_kernel(FfnArgs a) {
     const int slot = (wave * NI + j) * 64 + lane;
     const int r = slot / CPR, pc = slot % CPR;
     const int c = pc ^ swz(r);
-    doff[j] = (uint32_t)(((size_t)(t.row0 + min(r, t.mcount - 1)) * a.K + 8 * c) * 2);
+    doff[j] = r < t.mcount ? (uint32_t)(((size_t)(t.row0 + r) * a.K + 8 * c) * 2) : kPastRange;
   }
   const int split = blockIdx.y;
   const int per = (KTn + a.splits - 1) / a.splits;
