@@ -791,8 +791,8 @@ __global__ __launch_bounds__(kThreads) void ffn_decode_kernel(FfnArgs a, int ksw
   decode_finish<F, ROLE>(a, t, ex, rA, rg, split, lane, regs, v0, v1);
 }
 
-// Decode GEMV with a shared token tile (launches with enough row groups to
-// fill the device): the 4 wavefronts of a block own 4
+// Decode GEMV with a shared token tile (launches with short K streams or
+// enough row groups to fill the device): the 4 wavefronts of a block own 4
 // consecutive row groups and stream the same K tile of their weights at the
 // same time, so the block's 32 token rows of that K tile reach LDS once, by
 // DMA (buffer loads with an LDS destination), instead of once per wavefront
