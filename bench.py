@@ -800,6 +800,14 @@ def main():
     result["workloads"] = entries
     if ctx:
         result["context"] = ctx
+        # decode weight streams against the read rate the same run measured in
+        # the sweep's fastest shape (a plain read of the 1 GiB buffer)
+        best = ctx.get("hbm_read_GBps_best_shape")
+        if best:
+            for ent in entries.values():
+                for d in ent.get("decode", []):
+                    d["ffn_frac_of_best_read"] = d["ffn_weight_GBps"] / best
+                    d["layer_frac_of_best_read"] = d["layer_weight_GBps"] / best
     print(json.dumps(result))
 
 
