@@ -327,3 +327,19 @@ def test_package_fails_loudly_without_the_library():
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert out.returncode != 0
     assert "ImportError" in out.stderr and "no-such-libmoeq.so" in out.stderr
+
+
+def test_stream_read_shaped_rejects_shapes_on_host():
+    """Launch shapes outside the documented ranges are refused before any
+    device call (null buffers stand in for device memory); an empty read
+    with a valid shape is a no-op; a valid shape with a null buffer is refused."""
+    f = _lib.LIB.moe_stream_read_shaped
+    vp = ctypes.c_void_p
+    bad = [(0, 4, 8, 0), (65537, 4, 8, 0), (8, 0, 8, 0), (8, 17, 8, 0), (8, 4, 3, 0),
+           (8, 4, 0, 0), (8, 4, 32, 0), (8, 4, 8, 2), (8, 4, 8, -1)]
+    for blocks, waves, inflight, layout in bad:
+        assert f(vp(None), 16, 1, blocks, waves, inflight, layout, vp(None), vp(None)) == -1
+    assert f(vp(None), 0, 1, 256, 4, 16, 1, vp(None), vp(None)) == 0
+    assert f(vp(None), 16, 0, 256, 4, 16, 1, vp(None), vp(None)) == -1
+    assert f(vp(16), 24, 0, 256, 4, 16, 1, vp(64), vp(None)) == -1   # bytes % 16
+    assert f(vp(8), 16, 0, 256, 4, 16, 1, vp(64), vp(None)) == -3    # src alignment
